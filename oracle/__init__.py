@@ -1,0 +1,22 @@
+"""CPU oracle for the FP8 rowwise-scaled grouped GEMM (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The GPU library never does, and shares no code with it.
+"""
+from .grouped_gemm import (  # noqa: F401
+    ROW_UNTOUCHED,
+    ROW_WRITTEN,
+    ROW_ZEROED,
+    OracleResult,
+    bf16_bits_to_f64,
+    bf16_rne_from_f64,
+    bf16_ulp,
+    decode_e4m3fn,
+    dynamic_entries,
+    dynamic_row_classes,
+    e4m3fn_table,
+    grouped_dynamic,
+    grouped_stacked,
+    stacked_entries,
+    stacked_row_groups,
+)

@@ -1,0 +1,79 @@
+"""Exact rational brute force for tiny grouped GEMMs (a pin for the oracle).
+
+Independent of ``oracle/``: fp8 codes are decoded by torch's own float8_e4m3fn
+type, every product and sum is an exact ``Fraction``, and bf16 rounding is done
+on the exact rational with round-half-to-even.  Pure Python loops: tiny shapes only.
+"""
+from __future__ import annotations
+
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+
+def torch_decode_all() -> list:
+    """Exact value of every e4m3fn code as decoded by torch (None for NaN)."""
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    vals = codes.view(torch.float8_e4m3fn).to(torch.float32).tolist()
+    return [None if v != v else Fraction(v) for v in vals]
+
+
+_DEC = torch_decode_all()
+
+
+def bf16_bits_exact(v) -> int:
+    """Round an exact rational (or None = NaN) to bf16 with ties-to-even."""
+    if v is None:
+        return 0x7FC0
+    if v == 0:
+        return 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    # e = floor(log2(a))
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if Fraction(2) ** e > a:
+        e -= 1
+    elif Fraction(2) ** (e + 1) <= a:
+        e += 1
+    quantum = Fraction(2) ** (-133) if e < -126 else Fraction(2) ** (e - 7)
+    q = a / quantum
+    n = q.numerator // q.denominator
+    r = q - n
+    if r > Fraction(1, 2) or (r == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    y = n * quantum
+    if y >= Fraction(2) ** 128:
+        return sign | 0x7F80
+    f = np.float32(float(y))  # exact: y has <= 8 significant bits in range
+    assert Fraction(float(f)) == y
+    return sign | int(f.view(np.uint32) >> np.uint32(16))
+
+
+def dot_exact(a_codes, b_codes):
+    acc = Fraction(0)
+    for x, w in zip(a_codes.tolist(), b_codes.tolist()):
+        dx, dw = _DEC[x], _DEC[w]
+        if dx is None or dw is None:
+            return None
+        acc += dx * dw
+    return acc
+
+
+def stacked_exact(XQ, WQ, x_scale, w_scale, M_sizes):
+    """Exact bf16 bits [total_M, N]; rows of no group are None."""
+    total_M = XQ.shape[0]
+    G, N, _ = WQ.shape
+    out = [None] * total_M
+    start = 0
+    for g in range(G):
+        s = max(int(M_sizes[g]), 0)
+        for r in range(start, min(start + s, total_M)):
+            row = []
+            for n in range(N):
+                acc = dot_exact(XQ[r], WQ[g, n])
+                v = None if acc is None else acc * Fraction(float(x_scale[r])) * Fraction(float(w_scale[g, n]))
+                row.append(bf16_bits_exact(v))
+            out[r] = row
+        start += s
+    return out

@@ -1,0 +1,425 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+* the e4m3fn decode against torch's float8 type and the format definition;
+* the fp64 -> bf16 rounding against torch's fp32 -> bf16 and hand-derived ties;
+* the whole grouped GEMM against an exact rational brute force on tiny shapes and
+  against a hand-derived worked example;
+* invariants: summation-order independence, zero-padded K, the rowwise-scale
+  factorisation, dynamic == stacked on the compacted rows, closed forms (B = I,
+  one-hot rows, power-of-two scales), row classification;
+* planted mistakes: each one is injected into the oracle and must trip a pin.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import grouped_gemm as og
+from tests import exact_ref
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+FINITE_CODES = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+
+
+def _rand_problem(seed, sizes, N, K, total_M=None, finite=True):
+    rng = np.random.default_rng(seed)
+    sizes = np.asarray(sizes, np.int64)
+    if total_M is None:
+        total_M = int(np.clip(sizes, 0, None).sum())
+    G = sizes.size
+    XQ = rng.choice(FINITE_CODES, size=(total_M, K)).astype(np.uint8)
+    WQ = rng.choice(FINITE_CODES, size=(G, N, K)).astype(np.uint8)
+    xs = (2.0 ** rng.uniform(-12, 4, total_M)).astype(np.float32)
+    ws = (2.0 ** rng.uniform(-12, 4, (G, N))).astype(np.float32)
+    return XQ, WQ, xs, ws, sizes
+
+
+# ---------------------------------------------------------------------------
+# decode
+# ---------------------------------------------------------------------------
+
+def test_decode_matches_torch_all_codes():
+    t = oracle.e4m3fn_table()
+    ref = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(t), nan)
+    assert np.array_equal(t[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(t[~nan]), np.signbit(ref[~nan]))
+
+
+def test_decode_golden_codes():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "e4m3fn_codes.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        code_s, val_s = line.split()[:2]
+        code = int(code_s, 16)
+        got = oracle.decode_e4m3fn(np.array([code], np.uint8))[0]
+        if val_s == "nan":
+            assert np.isnan(got), hex(code)
+        else:
+            want = float.fromhex(val_s) if "0x" in val_s else float(val_s)
+            assert got == want and np.signbit(got) == np.signbit(want), (hex(code), got, want)
+        n += 1
+    assert n >= 15
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding
+# ---------------------------------------------------------------------------
+
+def test_bf16_golden_cases():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "bf16_rne_cases.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        x_s, bits_s = line.split()[:2]
+        x = float.fromhex(x_s)
+        got = int(oracle.bf16_rne_from_f64(np.array([x]))[0])
+        assert got == int(bits_s, 16), (x_s, hex(got), bits_s)
+        n += 1
+    assert n >= 15
+
+
+def test_bf16_matches_torch_on_fp32_inputs():
+    rng = np.random.default_rng(7)
+    u = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
+    x = u.view(np.float32)
+    x = x[~np.isnan(x)]
+    # plus values near bf16 rounding boundaries and in the subnormal range
+    base = rng.standard_normal(50_000).astype(np.float32)
+    b16 = torch.from_numpy(base).to(torch.bfloat16).float().numpy()
+    ties = (b16.view(np.uint32) + np.uint32(0x8000)).view(np.float32)
+    sub = (rng.standard_normal(20_000) * 2.0 ** -130).astype(np.float32)
+    x = np.concatenate([x, ties, sub, np.float32([0.0, -0.0, np.inf, -np.inf])])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = oracle.bf16_rne_from_f64(x.astype(np.float64))
+    assert np.array_equal(got, want)
+
+
+def test_bf16_exact_rational_agrees_on_random_fp64():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal(3000) * 2.0 ** rng.integers(-140, 130, 3000)
+    got = oracle.bf16_rne_from_f64(x)
+    from fractions import Fraction
+    want = np.array([exact_ref.bf16_bits_exact(Fraction(float(v))) for v in x], np.uint16)
+    assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------------------
+# the grouped GEMM, end to end
+# ---------------------------------------------------------------------------
+
+def _check_bruteforce(seed, sizes, N, K, total_M=None):
+    XQ, WQ, xs, ws, sizes = _rand_problem(seed, sizes, N, K, total_M)
+    res = oracle.grouped_stacked(XQ, WQ, xs, ws, sizes)
+    exact = exact_ref.stacked_exact(XQ, WQ, xs, ws, sizes)
+    for r, row in enumerate(exact):
+        if row is None:
+            if res.row_class[r] != oracle.ROW_UNTOUCHED:
+                return False
+            continue
+        if res.row_class[r] != oracle.ROW_WRITTEN:
+            return False
+        got = res.bits[r].astype(np.int64)
+        want = np.array(row, np.int64)
+        zero = (want & 0x7FFF) == 0
+        if not np.array_equal(got[~zero], want[~zero]):
+            return False
+        if not np.all((got[zero] & 0x7FFF) == 0):
+            return False
+    return True
+
+
+BRUTE_CASES = [
+    (11, [2, 0, 3], 5, 48, None),
+    (12, [1, 4], 3, 32, 7),
+    (13, [0, 0, 2, 1], 6, 16, None),
+    (14, [3], 4, 80, None),
+]
+
+
+@pytest.mark.parametrize("seed,sizes,N,K,total_M", BRUTE_CASES)
+def test_stacked_equals_exact_bruteforce(seed, sizes, N, K, total_M):
+    assert _check_bruteforce(seed, sizes, N, K, total_M)
+
+
+def _load_worked():
+    with open(os.path.join(GOLDEN, "worked_example.json")) as f:
+        ex = json.load(f)
+    K = ex["K"]
+
+    def vec(spec):
+        v = np.zeros(K, np.uint8)
+        if "all" in spec:
+            v[:] = int(spec["all"], 16)
+        else:
+            for k, c in spec.items():
+                v[int(k)] = int(c, 16)
+        return v
+
+    rows = {name: vec(spec) for name, spec in ex["rows"].items()}
+    W = np.stack([np.stack([vec(ex["weights"]["g0n0"]), vec(ex["weights"]["g0n1"])]),
+                  np.stack([vec(ex["weights"]["g1n0"]), vec(ex["weights"]["g1n1"])])])
+    xsd = dict(ex["x_scale"])
+    xsd["nan"] = float("nan")
+    ws = np.array(ex["w_scale"], np.float32)
+    return ex, rows, W, xsd, ws
+
+
+def test_worked_example_stacked():
+    ex, rows, W, xsd, ws = _load_worked()
+    order = ex["stacked"]["row_order"]
+    XQ = np.stack([rows[r] for r in order])
+    xs = np.array([xsd[r] for r in order], np.float32)
+    res = oracle.grouped_stacked(XQ, W, xs, ws, np.array(ex["stacked"]["M_sizes"]))
+    for i, want in enumerate(ex["stacked"]["expected_bits"]):
+        if want is None:
+            assert res.row_class[i] == oracle.ROW_UNTOUCHED
+        else:
+            assert res.row_class[i] == oracle.ROW_WRITTEN
+            assert [int(b, 16) for b in want] == res.bits[i].tolist()
+
+
+def test_worked_example_padded():
+    ex, rows, W, xsd, ws = _load_worked()
+    slabs = ex["padded"]["slabs"]
+    XQ = np.stack([np.stack([rows[r] for r in s]) for s in slabs])
+    xs = np.array([[xsd[r] for r in s] for s in slabs], np.float32)
+    res = oracle.grouped_dynamic(XQ, W, xs, ws, np.array(ex["padded"]["zero_start_index_M"]))
+    want = np.array([[[int(b, 16) for b in r] for r in s] for s in ex["padded"]["expected_bits"]])
+    assert np.array_equal(res.bits, want)
+    assert res.row_class.tolist() == [oracle.ROW_WRITTEN, oracle.ROW_ZEROED,
+                                      oracle.ROW_WRITTEN, oracle.ROW_WRITTEN]
+
+
+# ---------------------------------------------------------------------------
+# invariants and closed forms
+# ---------------------------------------------------------------------------
+
+def test_summation_order_independent():
+    XQ, WQ, xs, ws, sizes = _rand_problem(21, [5, 0, 7], 9, 160)
+    base = oracle.grouped_stacked(XQ, WQ, xs, ws, sizes)
+    perm = np.random.default_rng(3).permutation(160)
+    res = oracle.grouped_stacked(XQ[:, perm], WQ[:, :, perm], xs, ws, sizes)
+    assert np.array_equal(base.bits, res.bits)
+
+
+def test_zero_padded_k_is_bit_identical():
+    XQ, WQ, xs, ws, sizes = _rand_problem(22, [4, 6], 8, 144)
+    base = oracle.grouped_stacked(XQ, WQ, xs, ws, sizes)
+    pad = 256 - 144
+    XQp = np.concatenate([XQ, np.zeros((XQ.shape[0], pad), np.uint8)], 1)
+    WQp = np.concatenate([WQ, np.zeros(WQ.shape[:2] + (pad,), np.uint8)], 2)
+    res = oracle.grouped_stacked(XQp, WQp, xs, ws, sizes)
+    assert np.array_equal(base.bits, res.bits)
+
+
+def test_rowwise_factorisation_equals_dequantised_gemm():
+    """Scales factor out of the reduction: the result equals a GEMM on the
+    dequantised operands (dec(X) * x_scale) @ (dec(W) * w_scale)^T, to 1 ulp."""
+    rng = np.random.default_rng(23)
+    x = rng.standard_normal((40, 272)).astype(np.float32)
+    w = rng.standard_normal((24, 272)).astype(np.float32)
+    from workloads import quantize_rows
+    XQ, xs = quantize_rows(x)
+    WQ, ws = quantize_rows(w)
+    res = oracle.grouped_stacked(XQ, WQ[None], xs, ws[None], np.array([40]))
+    torch_dec = lambda q: torch.from_numpy(q).view(torch.float8_e4m3fn).double().numpy()
+    ref = (torch_dec(XQ) * xs[:, None].astype(np.float64)) @ (torch_dec(WQ) * ws[:, None].astype(np.float64)).T
+    got = oracle.bf16_bits_to_f64(res.bits)
+    assert np.all(np.abs(got - ref) <= oracle.bf16_ulp(ref))
+
+
+def test_dynamic_equals_stacked_on_compacted_rows():
+    rng = np.random.default_rng(24)
+    G, em, N, K = 4, 9, 7, 64
+    XQ = rng.choice(FINITE_CODES, size=(G, em, K)).astype(np.uint8)
+    WQ = rng.choice(FINITE_CODES, size=(G, N, K)).astype(np.uint8)
+    xs = (2.0 ** rng.uniform(-6, 2, (G, em))).astype(np.float32)
+    ws = (2.0 ** rng.uniform(-6, 2, (G, N))).astype(np.float32)
+    zsi = np.array([0, 9, 4, 1])
+    dyn = oracle.grouped_dynamic(XQ, WQ, xs, ws, zsi)
+    rows = np.concatenate([XQ[g, :zsi[g]] for g in range(G)])
+    xsc = np.concatenate([xs[g, :zsi[g]] for g in range(G)])
+    st = oracle.grouped_stacked(rows, WQ, xsc, ws, zsi)
+    dyn_rows = np.concatenate([dyn.bits[g, :zsi[g]] for g in range(G)])
+    assert np.array_equal(dyn_rows, st.bits)
+    for g in range(G):
+        assert np.all(dyn.bits[g, zsi[g]:] == 0)
+
+
+def test_identity_weights_reproduce_a():
+    """B = I (the diagnostic used for a lost accumulator slot): with W = 1.0 on the
+    diagonal, w_scale = 1 and a power-of-two x_scale, Y = dec(XQ) * x_scale exactly."""
+    rng = np.random.default_rng(25)
+    K = 64
+    XQ = rng.choice(FINITE_CODES, size=(12, K)).astype(np.uint8)
+    WQ = np.zeros((1, K, K), np.uint8)
+    WQ[0, np.arange(K), np.arange(K)] = 0x38
+    xs = (2.0 ** rng.integers(-4, 4, 12)).astype(np.float32)
+    res = oracle.grouped_stacked(XQ, WQ, xs, np.ones((1, K), np.float32), np.array([12]))
+    tdec = torch.from_numpy(XQ).view(torch.float8_e4m3fn).float() * torch.from_numpy(xs)[:, None]
+    want = tdec.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = res.bits.copy()
+    zero = (want & 0x7FFF) == 0
+    assert np.array_equal(got[~zero], want[~zero])
+    assert np.all((got[zero] & 0x7FFF) == 0)
+
+
+def test_one_hot_rows_closed_form():
+    rng = np.random.default_rng(26)
+    K, N = 48, 5
+    for trial in range(20):
+        a, b = rng.choice(FINITE_CODES, 2)
+        k0 = rng.integers(K)
+        XQ = np.zeros((1, K), np.uint8)
+        XQ[0, k0] = a
+        WQ = rng.choice(FINITE_CODES, size=(1, N, K)).astype(np.uint8)
+        WQ[0, 2, k0] = b
+        xs = np.float32([rng.uniform(0.1, 3)])
+        ws = rng.uniform(0.1, 3, (1, N)).astype(np.float32)
+        res = oracle.grouped_stacked(XQ, WQ, xs, ws, np.array([1]))
+        from fractions import Fraction
+        dec = exact_ref._DEC
+        v = dec[a] * dec[WQ[0, 2, k0]] * Fraction(float(xs[0])) * Fraction(float(ws[0, 2]))
+        want = exact_ref.bf16_bits_exact(v)
+        if (want & 0x7FFF) == 0:
+            assert (int(res.bits[0, 2]) & 0x7FFF) == 0
+        else:
+            assert int(res.bits[0, 2]) == want
+
+
+def test_power_of_two_scale_doubles_exactly():
+    XQ, WQ, xs, ws, sizes = _rand_problem(27, [3, 5], 6, 64)
+    xs = np.clip(xs, 2.0 ** -8, None).astype(np.float32)
+    a = oracle.grouped_stacked(XQ, WQ, xs, ws, sizes)
+    b = oracle.grouped_stacked(XQ, WQ, (xs * 2).astype(np.float32), ws, sizes)
+    assert np.array_equal(b.values, a.values * 2)
+
+
+def test_row_classes_stacked():
+    owner = oracle.stacked_row_groups(np.array([2, -1, 3]), 7)
+    assert owner.tolist() == [0, 0, 2, 2, 2, -1, -1]
+    owner = oracle.stacked_row_groups(np.array([2, 4, 3]), 5)
+    assert owner.tolist() == [0, 0, 1, 1, 1]
+    owner = oracle.stacked_row_groups(np.array([0, 0]), 3)
+    assert owner.tolist() == [-1, -1, -1]
+
+
+def test_row_classes_dynamic_and_zeroing_flag():
+    c = oracle.dynamic_row_classes(np.array([0, 3, 9, -2]), 3, True)
+    W, Z = oracle.ROW_WRITTEN, oracle.ROW_ZEROED
+    assert c.tolist() == [[Z, Z, Z], [W, W, W], [W, W, W], [Z, Z, Z]]
+    c = oracle.dynamic_row_classes(np.array([1]), 3, False)
+    assert c.tolist() == [[W, oracle.ROW_UNTOUCHED, oracle.ROW_UNTOUCHED]]
+
+
+def test_k_zero_returns_zeros_in_both_layouts():
+    st = oracle.grouped_stacked(np.zeros((5, 0), np.uint8), np.zeros((2, 4, 0), np.uint8),
+                                np.ones(5, np.float32), np.ones((2, 4), np.float32), np.array([2, 1]))
+    assert np.all(st.bits == 0) and np.all(st.row_class == oracle.ROW_ZEROED)
+    dy = oracle.grouped_dynamic(np.zeros((2, 3, 0), np.uint8), np.zeros((2, 4, 0), np.uint8),
+                                np.ones((2, 3), np.float32), np.ones((2, 4), np.float32), np.array([1, 3]),
+                                zeroing_output_tensor=False)
+    assert np.all(dy.bits == 0) and np.all(dy.row_class == oracle.ROW_ZEROED)
+
+
+def test_empty_and_full_groups():
+    """An empty group produces no rows; a full group equals G = 1 on its slice."""
+    XQ, WQ, xs, ws, sizes = _rand_problem(28, [0, 6, 0, 4], 7, 96)
+    res = oracle.grouped_stacked(XQ, WQ, xs, ws, sizes)
+    one = oracle.grouped_stacked(XQ[6:10], WQ[3:4], xs[6:10], ws[3:4], np.array([4]))
+    assert np.array_equal(res.bits[6:10], one.bits)
+
+
+def test_entries_match_full_result():
+    XQ, WQ, xs, ws, sizes = _rand_problem(29, [3, 0, 5, 2], 11, 64, total_M=12)
+    full = oracle.grouped_stacked(XQ, WQ, xs, ws, sizes)
+    rows = np.array([0, 2, 3, 7, 9, 10, 11])
+    cols = np.array([0, 5, 10])
+    vals, bits, owner = oracle.stacked_entries(XQ, WQ, xs, ws, sizes, rows, cols)
+    assert np.array_equal(bits, full.bits[np.ix_(rows, cols)])
+    G, em = 3, 4
+    rng = np.random.default_rng(30)
+    XQd = rng.choice(FINITE_CODES, size=(G, em, 32)).astype(np.uint8)
+    WQd = rng.choice(FINITE_CODES, size=(G, 6, 32)).astype(np.uint8)
+    xsd = rng.uniform(0.5, 2, (G, em)).astype(np.float32)
+    wsd = rng.uniform(0.5, 2, (G, 6)).astype(np.float32)
+    zsi = np.array([2, 0, 4])
+    fulld = oracle.grouped_dynamic(XQd, WQd, xsd, wsd, zsi)
+    g = np.array([0, 0, 1, 2, 2])
+    r = np.array([1, 3, 0, 2, 3])
+    vals, bits, cls = oracle.dynamic_entries(XQd, WQd, xsd, wsd, zsi, g, r, np.arange(6))
+    assert np.array_equal(bits, fulld.bits[g, r])
+
+
+# ---------------------------------------------------------------------------
+# planted mistakes: each must trip at least one pin
+# ---------------------------------------------------------------------------
+
+def _pins_pass():
+    ok = all(_check_bruteforce(*c) for c in BRUTE_CASES)
+    try:
+        test_worked_example_stacked()
+        test_worked_example_padded()
+    except AssertionError:
+        ok = False
+    return ok
+
+
+def _mut_transposed_index(a_codes, b_codes):
+    return og.decode_e4m3fn(a_codes) @ og.decode_e4m3fn(b_codes[::-1]).T
+
+
+def _mut_dropped_term(a_codes, b_codes):
+    return og.decode_e4m3fn(a_codes[:, 1:]) @ og.decode_e4m3fn(b_codes[:, 1:]).T
+
+
+def _mut_no_xscale(acc, xs, ws):
+    return acc * np.asarray(ws, np.float64)[None, :]
+
+
+def _mut_group_shift(M_sizes, total_M):
+    return og.__dict__["_orig_rows"](np.roll(np.asarray(M_sizes), 1), total_M)
+
+
+def _mut_sign(codes):
+    return np.abs(og._E4M3FN_TABLE[np.asarray(codes, np.uint8)])
+
+
+def _mut_fp32_detour(v):
+    x = torch.from_numpy(np.asarray(v, np.float64).astype(np.float32))
+    return x.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def _mut_truncate(v):
+    f = np.asarray(v, np.float64).astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+@pytest.mark.parametrize("name,attr,fn", [
+    ("transposed/reversed W index", "_accumulate", _mut_transposed_index),
+    ("dropped K term", "_accumulate", _mut_dropped_term),
+    ("x_scale dropped", "_apply_scales", _mut_no_xscale),
+    ("wrong group", "stacked_row_groups", _mut_group_shift),
+    ("sign lost in decode", "decode_e4m3fn", _mut_sign),
+    ("bf16 rounding truncates", "bf16_rne_from_f64", _mut_truncate),
+])
+def test_planted_mistake_is_caught(monkeypatch, name, attr, fn):
+    assert _pins_pass()
+    monkeypatch.setitem(og.__dict__, "_orig_rows", og.stacked_row_groups)
+    monkeypatch.setattr(og, attr, fn)
+    assert not _pins_pass(), f"planted mistake not caught: {name}"
+
+
+def test_planted_double_rounding_is_caught(monkeypatch):
+    monkeypatch.setattr(og, "bf16_rne_from_f64", _mut_fp32_detour)
+    monkeypatch.setattr(oracle, "bf16_rne_from_f64", _mut_fp32_detour)
+    with pytest.raises(AssertionError):
+        test_bf16_golden_cases()
