@@ -1,0 +1,267 @@
+// Host side of the fp8 rowwise-scaled grouped GEMM C ABI: argument checks,
+// launch planning (tile configuration, tails, grid) and dispatch.
+//
+// Contracts follow MSLK pull request 471 ("Back the FP8 rowwise grouped GEMM ops
+// with FlyDSL on ROCm"): the op refuses what it cannot compute instead of
+// silently ignoring it (commits on strided outputs and on preshuffle refusals),
+// a zero-length contraction returns a zeroed output (commit on zero-length
+// reductions), and no benchmarking ever happens inside a call -- a fixed
+// selector picks the tile (commit on the autotune policy).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "fp8gg.h"
+#include "fp8gg_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+fp8gg_status fail(fp8gg_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+fp8gg_status ok() {
+  g_last_error.clear();
+  return FP8GG_OK;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+struct Range {
+  const void* p;
+  int64_t bytes;
+  const char* name;
+};
+
+bool overlap(const Range& a, const Range& b) {
+  if (a.bytes <= 0 || b.bytes <= 0 || !a.p || !b.p) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a.p), b0 = reinterpret_cast<uintptr_t>(b.p);
+  return a0 < b0 + static_cast<uintptr_t>(b.bytes) && b0 < a0 + static_cast<uintptr_t>(a.bytes);
+}
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  return std::atoi(v);
+}
+
+// Shape checks shared by plan() and the entry points.
+fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
+  if (layout != FP8GG_LAYOUT_STACKED && layout != FP8GG_LAYOUT_PADDED)
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "unknown layout %d", layout);
+  if (G < 0 || M < 0 || N < 0 || K < 0)
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "negative size (G=%lld M=%lld N=%lld K=%lld)", (long long)G,
+                (long long)M, (long long)N, (long long)K);
+  if (K % 16 != 0)
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "K=%lld must be a multiple of 16", (long long)K);
+  if (N % 8 != 0)
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "N=%lld must be a multiple of 8", (long long)N);
+  if (preshuffled && (N % FP8GG_SHUFFLE_N != 0 || K % FP8GG_SHUFFLE_K != 0))
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE,
+                "pre-shuffled weights need N %% %d == 0 and K %% %d == 0 (N=%lld K=%lld)", FP8GG_SHUFFLE_N,
+                FP8GG_SHUFFLE_K, (long long)N, (long long)K);
+  const int64_t lim = (int64_t(1) << 31) - 256;
+  if (K > lim || N > lim || M > lim || G > lim)
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "a dimension exceeds 2^31-256");
+  if (layout == FP8GG_LAYOUT_PADDED && G * M > lim)
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "G*expected_m exceeds 2^31-256");
+  return FP8GG_OK;
+}
+
+// Fixed selector.  The key is the rows one group contributes on average (total_M
+// is normalised by G for the stacked layout), as a tile only ever sees one group.
+int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
+  (void)K;
+  (void)N;
+  if (preshuffled) return -1;
+  const int64_t per_group = layout == FP8GG_LAYOUT_STACKED ? (G > 0 ? (M + G - 1) / G : M) : M;
+  if (per_group >= 256) return 0;
+  if (per_group >= 128) return 1;
+  if (per_group >= 48) return 2;
+  return 3;
+}
+
+fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K,
+                       fp8gg_plan* p) {
+  std::memset(p, 0, sizeof *p);
+  p->config_id = -1;
+  fp8gg_status st = check_shape(layout, preshuffled, G, M, N, K);
+  if (st != FP8GG_OK) return st;
+  const int64_t rows = layout == FP8GG_LAYOUT_STACKED ? M : G * M;
+  if (rows == 0 || N == 0) return FP8GG_OK;  // empty output: nothing to launch
+  if (K == 0) {
+    p->zero_fill = 1;
+    return FP8GG_OK;
+  }
+  if (G == 0) return FP8GG_OK;  // stacked rows that belong to no group are left untouched
+
+  int cfg = select_config(layout, preshuffled, G, M, N, K);
+  if (cfg < 0)
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "no kernel configuration for this call (preshuffled=%d)", preshuffled);
+  const int forced = env_int("FP8GG_CONFIG", -1);
+  if (forced >= 0) {
+    if (forced >= fp8gg::kNumConfigs || fp8gg::kConfigs[forced].preshuffled != (preshuffled ? 1 : 0))
+      return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_CONFIG=%d does not name a usable configuration", forced);
+    cfg = forced;
+  }
+  const fp8gg::KernelConfig& c = fp8gg::kConfigs[cfg];
+  p->config_id = cfg;
+  p->BM = c.BM;
+  p->BN = c.BN;
+  p->BK = fp8gg::kBK;
+  p->threads = c.WM * c.WN * 64;
+  p->stages = c.stages;
+  p->k_tail = (K % fp8gg::kBK) != 0;
+  p->n_tail = (N % c.BN) != 0;
+  p->n_tiles = (N + c.BN - 1) / c.BN;
+  if (layout == FP8GG_LAYOUT_STACKED) {
+    // Sum over groups of ceil(M_g / BM) <= ceil(total_M / BM) + G - 1, and each
+    // tile holds at least one row.
+    int64_t ub = (M + c.BM - 1) / c.BM + G - 1;
+    p->m_tiles = ub < M ? ub : M;
+    p->grid = p->m_tiles * p->n_tiles;
+  } else {
+    p->m_tiles = (M + c.BM - 1) / c.BM;
+    p->grid = p->m_tiles * p->n_tiles * G;
+  }
+  p->lds_bytes = fp8gg::lds_bytes(c);
+  if (p->grid > 0x7FFFFFFFLL)
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "grid of %lld workgroups exceeds the launch limit",
+                (long long)p->grid);
+  return FP8GG_OK;
+}
+
+fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* WQ, const float* xs,
+                 const float* ws, const int64_t* meta, uint16_t* Y, int64_t G, int64_t M, int64_t N, int64_t K,
+                 int zeroing, void* stream) {
+  fp8gg_plan p;
+  fp8gg_status st = make_plan(layout, preshuffled, G, M, N, K, &p);
+  if (st != FP8GG_OK) return st;
+  const int64_t rows = layout == FP8GG_LAYOUT_STACKED ? M : G * M;
+  if (rows == 0 || N == 0) return ok();
+  if (!Y) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y is null");
+  if (!aligned(Y, 16)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.zero_fill) {
+    hipError_t e = fp8gg::launch_zero_fill(Y, rows * N, s);
+    if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "zero fill launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
+  if (p.config_id < 0) return ok();
+  if (!XQ || !WQ || !xs || !ws || !meta)
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "null input pointer (XQ=%p WQ=%p x_scale=%p w_scale=%p meta=%p)",
+                (const void*)XQ, (const void*)WQ, (const void*)xs, (const void*)ws, (const void*)meta);
+  if (!aligned(XQ, 16) || !aligned(WQ, 16) || !aligned(ws, 16))
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "XQ, WQ and w_scale must be 16-byte aligned");
+  if (!aligned(xs, 4) || !aligned(meta, 8))
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "x_scale must be 4-byte and the metadata 8-byte aligned");
+  const Range out{Y, rows * N * 2, "Y"};
+  const Range ins[] = {{XQ, rows * K, "XQ"},
+                       {WQ, G * N * K, "WQ"},
+                       {xs, rows * 4, "x_scale"},
+                       {ws, G * N * 4, "w_scale"},
+                       {meta, G * 8, "metadata"}};
+  for (const Range& r : ins)
+    if (overlap(out, r)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y overlaps %s", r.name);
+
+  fp8gg::GemmArgs a;
+  a.X = XQ;
+  a.W = WQ;
+  a.xs = xs;
+  a.ws = ws;
+  a.meta = meta;
+  a.Y = Y;
+  a.G = G;
+  a.M = M;
+  a.N = N;
+  a.K = K;
+  a.m_tiles = p.m_tiles;
+  a.n_tiles = p.n_tiles;
+  a.zeroing = zeroing ? 1 : 0;
+  if (env_int("FP8GG_LOG", 0))
+    std::fprintf(stderr,
+                 "[fp8gg] layout=%d pre=%d G=%lld M=%lld N=%lld K=%lld -> cfg=%d tile=%dx%dx%d thr=%d st=%d "
+                 "ktail=%d ntail=%d grid=%lld (m_tiles=%lld n_tiles=%lld)\n",
+                 layout, preshuffled, (long long)G, (long long)M, (long long)N, (long long)K, p.config_id, p.BM,
+                 p.BN, p.BK, p.threads, p.stages, p.k_tail, p.n_tail, (long long)p.grid, (long long)p.m_tiles,
+                 (long long)p.n_tiles);
+  hipError_t e = fp8gg::launch_gemm(layout, p.config_id, p.k_tail != 0, a, p.grid, s);
+  if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+fp8gg_status f8f8bf16_rowwise_grouped_stacked(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                              const float* w_scale, const int64_t* M_sizes, uint16_t* Y,
+                                              int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream) {
+  return run(FP8GG_LAYOUT_STACKED, 0, XQ, WQ, x_scale, w_scale, M_sizes, Y, G, total_M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_rowwise_grouped_dynamic(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                              const float* w_scale, const int64_t* zero_start_index_M,
+                                              uint16_t* Y, int64_t G, int64_t expected_m, int64_t N, int64_t K,
+                                              int zeroing_output_tensor, void* stream) {
+  return run(FP8GG_LAYOUT_PADDED, 0, XQ, WQ, x_scale, w_scale, zero_start_index_M, Y, G, expected_m, N, K,
+             zeroing_output_tensor, stream);
+}
+
+fp8gg_status f8f8bf16_rowwise_grouped_stacked_preshuffle(const uint8_t* XQ, const uint8_t* WQs,
+                                                         const float* x_scale, const float* w_scale,
+                                                         const int64_t* M_sizes, uint16_t* Y, int64_t G,
+                                                         int64_t total_M, int64_t N, int64_t K, void* stream) {
+  return run(FP8GG_LAYOUT_STACKED, 1, XQ, WQs, x_scale, w_scale, M_sizes, Y, G, total_M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_rowwise_grouped_dynamic_preshuffle(const uint8_t* XQ, const uint8_t* WQs,
+                                                         const float* x_scale, const float* w_scale,
+                                                         const int64_t* zero_start_index_M, uint16_t* Y,
+                                                         int64_t G, int64_t expected_m, int64_t N, int64_t K,
+                                                         int zeroing_output_tensor, void* stream) {
+  return run(FP8GG_LAYOUT_PADDED, 1, XQ, WQs, x_scale, w_scale, zero_start_index_M, Y, G, expected_m, N, K,
+             zeroing_output_tensor, stream);
+}
+
+fp8gg_status f8f8bf16_shuffle_b(const uint8_t* WQ, uint8_t* WQs, int64_t G, int64_t N, int64_t K,
+                                void* stream) {
+  fp8gg_status st = check_shape(FP8GG_LAYOUT_STACKED, 1, G, 0, N, K);
+  if (st != FP8GG_OK) return st;
+  const int64_t bytes = G * N * K;
+  if (bytes == 0) return ok();
+  if (!WQ || !WQs) return fail(FP8GG_ERR_INVALID_ARGUMENT, "null pointer");
+  if (!aligned(WQ, 16) || !aligned(WQs, 16))
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "WQ and WQs must be 16-byte aligned");
+  if (overlap(Range{WQ, bytes, "WQ"}, Range{WQs, bytes, "WQs"}))
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "WQs overlaps WQ");
+  hipError_t e = fp8gg::launch_shuffle_b(WQ, WQs, G, N, K, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "shuffle launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+const char* f8f8bf16_last_error(void) { return g_last_error.c_str(); }
+
+fp8gg_status f8f8bf16_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K,
+                           fp8gg_plan* out) {
+  if (!out) return fail(FP8GG_ERR_INVALID_ARGUMENT, "out is null");
+  fp8gg_status st = make_plan(layout, preshuffled, G, M, N, K, out);
+  if (st == FP8GG_OK) ok();
+  return st;
+}
+
+int32_t f8f8bf16_num_configs(void) { return fp8gg::kNumConfigs; }
+
+}  // extern "C"

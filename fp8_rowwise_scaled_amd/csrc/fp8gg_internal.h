@@ -1,0 +1,53 @@
+// Internal interface between the host API (validation, planning) and the
+// device kernels of the fp8 rowwise-scaled grouped GEMM library.
+#ifndef FP8GG_INTERNAL_H_
+#define FP8GG_INTERNAL_H_
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp8gg {
+
+enum Layout : int { kStacked = 0, kPadded = 1 };
+
+// Operands of one grouped GEMM call, as the kernels see them.  Row-major, dense.
+struct GemmArgs {
+  const uint8_t* X;      // stacked: [M, K]; padded: [G * M, K] (M = expected_m)
+  const uint8_t* W;      // [G, N, K] (plain) or the pre-shuffled blocks
+  const float* xs;       // one scale per row of X
+  const float* ws;       // [G, N]
+  const int64_t* meta;   // stacked: M_sizes [G]; padded: zero_start_index_M [G]
+  uint16_t* Y;           // bf16 bits, one row per row of X, N columns
+  int64_t G, M, N, K;
+  int64_t m_tiles;       // stacked: upper bound of M tiles over all groups; padded: per slab
+  int64_t n_tiles;
+  int32_t zeroing;       // padded: write zeros into padding rows
+};
+
+// A compiled kernel configuration (workgroup tile and pipeline).
+struct KernelConfig {
+  int BM;       // rows of X per workgroup
+  int BN;       // columns of Y (rows of W) per workgroup
+  int WM, WN;   // waves along M and N (threads = 64 * WM * WN)
+  int stages;   // LDS pipeline depth
+  int preshuffled;  // 1: W is read from the pre-shuffled layout straight into registers
+};
+
+constexpr int kBK = 64;          // K bytes per pipeline stage (one 32x32x64 fp8 MFMA)
+
+extern const KernelConfig kConfigs[];
+extern const int kNumConfigs;
+
+inline int lds_bytes(const KernelConfig& c) {
+  return c.preshuffled ? c.stages * c.BM * kBK : c.stages * (c.BM + c.BN) * kBK;
+}
+
+hipError_t launch_gemm(int layout, int config_id, bool k_tail, const GemmArgs& args,
+                       int64_t grid, hipStream_t stream);
+hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t stream);
+hipError_t launch_shuffle_b(const uint8_t* W, uint8_t* Ws, int64_t G, int64_t N, int64_t K,
+                            hipStream_t stream);
+
+}  // namespace fp8gg
+
+#endif  // FP8GG_INTERNAL_H_

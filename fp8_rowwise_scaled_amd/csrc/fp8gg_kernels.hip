@@ -1,0 +1,438 @@
+// Device kernels of the fp8 (e4m3fn) rowwise-scaled grouped GEMM for gfx950.
+//
+// Method (MSLK pull request 471, "Back the FP8 rowwise grouped GEMM ops with
+// FlyDSL on ROCm"):
+//   * rowwise scales are constant along K, so the K loop accumulates the raw fp8
+//     products and one epilogue applies x_scale[m] * w_scale[g, n] (Design notes,
+//     scaling-scheme paragraph);
+//   * only the step that finds a tile's group differs between layouts; loads,
+//     K loop and epilogue are shared (Design notes, "one kernel, not six");
+//   * stacked layout: the host launches an upper bound of M tiles and each tile
+//     finds its group from the device-side row counts or retires (commit on
+//     self-retiring tiles); padded layout: the group is a grid coordinate and the
+//     row base a multiple of expected_m (commit adding the padded layout);
+//   * K-tail: K need only be a multiple of 16 bytes; chunks past K read as zero
+//     (commit on the K-tail variant); N-tail: W rows past N are not used and stores
+//     past N are dropped, predicated on the last column of each store (commits on
+//     the N-tail variant and on store predicates).
+//
+// gfx950 mapping (this file's own design):
+//   * fp8 MFMA v_mfma_f32_32x32x64_f8f6f4 (fp32 accumulate).  W is the MFMA "A"
+//     operand (MFMA rows = output columns n) and X the "B" operand (MFMA columns =
+//     output rows m), so each lane's accumulators cover consecutive output columns
+//     of one row and the epilogue stores 16-byte vectors.
+//   * A and B tiles of 64 K-bytes are copied global -> LDS with
+//     global_load_lds_dwordx4 (no staging registers), several stages deep.
+//   * LDS rows are 64 bytes (four 16-byte chunks); chunk c of row p is stored at
+//     c ^ ((p >> 1) & 3), which makes the MFMA operand reads (32 lanes reading 32
+//     consecutive rows at one logical chunk) bank-conflict free.
+//   * W rows are placed in LDS in "MFMA order": LDS row 32*fn + rho of a wave's
+//     slice holds the output column that MFMA row rho of block fn produces in the
+//     chosen lane -> column map, so the loads do the permutation for free.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "fp8gg_internal.h"
+
+namespace fp8gg {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+typedef __attribute__((address_space(1))) void* gbl_ptr_t;
+
+// Sixteen zero bytes.  K-tail chunks at or past K are fetched from here, so the
+// last K tile is zero-padded without a masked load.
+__device__ __attribute__((aligned(64))) const uint8_t g_zero16[64] = {0};
+
+// ---------------------------------------------------------------------------
+// Small device helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ v16f mfma_32x32x64_fp8(const v8i& a, const v8i& b, const v16f& c) {
+  // cbsz = blgp = 0 selects fp8 e4m3 for both operands; zero scale operands give the
+  // plain (unscaled) product.
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  // v_cvt_pk_bf16_f32: round to nearest even.
+  const __bf16 l = (__bf16)lo;
+  const __bf16 h = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+  // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+  // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt bits 6:4, lgkmcnt 11:8).
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
+    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
+    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
+    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
+// Group resolution: the only layout-dependent step.
+// ---------------------------------------------------------------------------
+
+struct Tile {
+  int64_t g;
+  int64_t row_base;   // first row of the tile (row index into X / xs / Y)
+  int64_t row_end;    // rows [row_base, row_end) are computed
+  int64_t zero_end;   // rows [row_end, zero_end) are written as zero
+};
+
+// Stacked: walk the groups with a running row prefix and tile prefix.  Counts are
+// clamped (negative -> 0, cumulative end -> M), so any metadata stays in bounds.
+template <int BM>
+__device__ __forceinline__ bool resolve_stacked(const GemmArgs& a, int64_t m_tile, Tile& t) {
+  int64_t start = 0, tiles_before = 0;
+  for (int64_t g = 0; g < a.G; ++g) {
+    int64_t s = a.meta[g];
+    s = s < 0 ? 0 : s;
+    int64_t end = start + s;
+    end = end > a.M ? a.M : end;
+    const int64_t tiles = (end - start + BM - 1) / BM;
+    if (m_tile < tiles_before + tiles) {
+      t.g = g;
+      t.row_base = start + (m_tile - tiles_before) * BM;
+      t.row_end = end;
+      t.zero_end = end;
+      return true;
+    }
+    tiles_before += tiles;
+    start = end;
+  }
+  return false;
+}
+
+// Padded: the group is a grid coordinate; slab g spans rows [g*M, (g+1)*M).
+template <int BM>
+__device__ __forceinline__ bool resolve_padded(const GemmArgs& a, int64_t g, int64_t m_tile, Tile& t) {
+  int64_t valid = a.meta[g];
+  valid = valid < 0 ? 0 : (valid > a.M ? a.M : valid);
+  const int64_t slab = g * a.M;
+  t.g = g;
+  t.row_base = slab + m_tile * BM;
+  t.row_end = slab + valid;
+  t.zero_end = a.zeroing ? slab + a.M : slab + valid;
+  return t.row_base < t.zero_end;
+}
+
+// Writes zeros into rows [r0, r1) x columns [c0, c1) of Y (16-byte vectors).
+template <int NT>
+__device__ __forceinline__ void zero_rect(uint16_t* Y, int64_t N, int64_t r0, int64_t r1,
+                                          int64_t c0, int64_t c1) {
+  const int64_t vec_per_row = (c1 - c0) / 8;  // c0, c1 are multiples of 8
+  const int64_t total = (r1 - r0) * vec_per_row;
+  const v4i z = {0, 0, 0, 0};
+  for (int64_t i = threadIdx.x; i < total; i += NT) {
+    const int64_t r = r0 + i / vec_per_row;
+    const int64_t c = c0 + (i % vec_per_row) * 8;
+    *(v4i*)(Y + r * N + c) = z;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The grouped GEMM kernel (plain W, both operands staged through LDS)
+// ---------------------------------------------------------------------------
+
+template <int LAYOUT, int BM, int BN, int WM, int WN, int STAGES, bool KTAIL>
+__global__ void __launch_bounds__(WM * WN * 64)
+gg_lds_kernel(GemmArgs a) {
+  constexpr int NT = WM * WN * 64;
+  constexpr int BK = kBK;
+  constexpr int TM = BM / WM;           // wave tile along M (rows of X)
+  constexpr int TN = BN / WN;           // wave tile along N (columns of Y)
+  constexpr int FM = TM / 32;           // 32x32 MFMA blocks per wave along M
+  constexpr int FN = TN / 32;           // ... along N
+  constexpr int A_CHUNKS = BM * BK / 16;
+  constexpr int B_CHUNKS = BN * BK / 16;
+  constexpr int A_LOADS = (A_CHUNKS + NT - 1) / NT;
+  constexpr int B_LOADS = (B_CHUNKS + NT - 1) / NT;
+  constexpr int A_BYTES = BM * BK;
+  constexpr int STAGE_BYTES = (BM + BN) * BK;
+  static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
+  static_assert(A_CHUNKS % 64 == 0 && B_CHUNKS % 64 == 0, "tile rows must be a multiple of 16");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN;
+  const int wn = wave % WN;
+
+  // ---- which tile ----
+  const int64_t bid = blockIdx.x;
+  const int64_t n_tile = bid % a.n_tiles;
+  const int64_t rest = bid / a.n_tiles;
+  Tile t;
+  if (LAYOUT == kStacked) {
+    if (!resolve_stacked<BM>(a, rest, t)) return;
+  } else {
+    if (!resolve_padded<BM>(a, rest / a.m_tiles, rest % a.m_tiles, t)) return;
+  }
+  const int64_t N = a.N;
+  const int64_t K = a.K;
+  const int64_t n0 = n_tile * BN;
+  const int64_t tile_row_end = t.row_base + BM;
+
+  if (t.row_base >= t.row_end) {
+    // Entirely padding (padded layout with zeroing): no K loop.
+    const int64_t r1 = tile_row_end < t.zero_end ? tile_row_end : t.zero_end;
+    const int64_t c1 = n0 + BN < N ? n0 + BN : N;
+    zero_rect<NT>(a.Y, N, t.row_base, r1, n0, c1);
+    return;
+  }
+
+  // ---- per-thread copy descriptors (global source at k = 0) ----
+  // Chunk q of a stage (16 bytes) lands at LDS byte 16*q: row p = q / 4, physical
+  // chunk q % 4, which holds logical chunk (q % 4) ^ ((p >> 1) & 3).
+  const uint8_t* a_src[A_LOADS];
+  int a_kc[A_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int q = i * NT + tid;
+    const int p = (q >> 2) % BM;
+    const int c = (q & 3) ^ ((p >> 1) & 3);
+    int64_t row = t.row_base + p;
+    row = row < t.row_end ? row : t.row_end - 1;   // rows past the group: any valid row, result dropped
+    a_src[i] = a.X + row * K + c * 16;
+    a_kc[i] = c * 16;
+  }
+  const uint8_t* b_src[B_LOADS];
+  int b_kc[B_LOADS];
+  const uint8_t* Wg = a.W + t.g * N * K;
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) {
+    const int q = i * NT + tid;
+    const int p = (q >> 2) % BN;
+    const int c = (q & 3) ^ ((p >> 1) & 3);
+    // MFMA order: LDS row p = wn_*TN + 32*fn + rho holds output column
+    // wn_*TN + h*16*FN + 16*fn + 4*j + tt, rho = 8*j + 4*h + tt.
+    const int wn_ = p / TN;
+    const int pp = p % TN;
+    const int fn = pp >> 5;
+    const int rho = pp & 31;
+    const int nl = wn_ * TN + ((rho >> 2) & 1) * 16 * FN + 16 * fn + 4 * (rho >> 3) + (rho & 3);
+    int64_t n = n0 + nl;
+    n = n < N ? n : N - 1;                            // columns past N: result dropped
+    b_src[i] = Wg + n * K + c * 16;
+    b_kc[i] = c * 16;
+  }
+
+  const int nk = (int)((K + BK - 1) / BK);
+
+  auto issue = [&](int kt) {
+    uint8_t* sbase = smem + (kt % STAGES) * STAGE_BYTES;
+    const int64_t koff = (int64_t)kt * BK;
+    const bool last = KTAIL && (kt == nk - 1);
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      if (A_CHUNKS % NT == 0 || i * NT + wave * 64 < A_CHUNKS) {
+        const uint8_t* src = a_src[i] + koff;
+        if (last && koff + a_kc[i] >= K) src = g_zero16;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(sbase + (i * NT + wave * 64) * 16), 16, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      if (B_CHUNKS % NT == 0 || i * NT + wave * 64 < B_CHUNKS) {
+        const uint8_t* src = b_src[i] + koff;
+        if (last && koff + b_kc[i] >= K) src = g_zero16;
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src,
+                                         (lds_ptr_t)(sbase + A_BYTES + (i * NT + wave * 64) * 16), 16, 0, 0);
+      }
+    }
+  };
+  // Loads this thread issues per stage (the vmcnt unit of one stage); waves whose
+  // chunk range ends inside a partial round issue fewer.
+  int loads_per_stage = 0;
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) loads_per_stage += (A_CHUNKS % NT == 0 || i * NT + wave * 64 < A_CHUNKS);
+#pragma unroll
+  for (int i = 0; i < B_LOADS; ++i) loads_per_stage += (B_CHUNKS % NT == 0 || i * NT + wave * 64 < B_CHUNKS);
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{0};
+
+  // Prologue: stages 0 .. STAGES-2 in flight.
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nk) issue(s);
+
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  for (int kt = 0; kt < nk; ++kt) {
+    // Tile kt has landed once at most (tiles issued after it) loads of this thread
+    // are outstanding; then the barrier makes every thread's copies visible and
+    // frees the stage that the next issue overwrites.
+    const int ahead = nk - 1 - kt;
+    if (ahead >= STAGES - 2) wait_vmcnt_le((STAGES - 2) * loads_per_stage);
+    else wait_vmcnt_le(0);
+    block_barrier();
+    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+
+    const uint8_t* sA = smem + (kt % STAGES) * STAGE_BYTES;
+    const uint8_t* sB = sA + A_BYTES;
+    v8i xf[FM], wf[FN];
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int p = wm * TM + 32 * fm + r32;
+      const int sw = (p >> 1) & 3;
+      const v4i lo = *(const v4i*)(sA + p * 64 + (((2 * h) ^ sw) * 16));
+      const v4i hi = *(const v4i*)(sA + p * 64 + (((2 * h + 1) ^ sw) * 16));
+      xf[fm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int p = wn * TN + 32 * fn + r32;
+      const int sw = (p >> 1) & 3;
+      const v4i lo = *(const v4i*)(sB + p * 64 + (((2 * h) ^ sw) * 16));
+      const v4i hi = *(const v4i*)(sB + p * 64 + (((2 * h + 1) ^ sw) * 16));
+      wf[fn] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wf[fn], xf[fm], acc[fm][fn]);
+  }
+
+  // ---- epilogue: y = bf16((acc * x_scale[m]) * w_scale[g, n]) ----
+  // Lane (h, r32) holds, for block (fm, fn), slot i = 4*j + tt, output row
+  // wm*TM + 32*fm + r32 and column col0 + 16*fn + i.
+  const int64_t col0 = n0 + wn * TN + h * 16 * FN;
+  const float* wsg = a.ws + t.g * N;
+  float wsv[16 * FN];
+#pragma unroll
+  for (int v = 0; v < 4 * FN; ++v) {
+    const int64_t c = col0 + 4 * v;
+    v4f w4 = {0.f, 0.f, 0.f, 0.f};
+    if (c < N) w4 = *(const v4f*)(wsg + c);
+    wsv[4 * v + 0] = w4.x;
+    wsv[4 * v + 1] = w4.y;
+    wsv[4 * v + 2] = w4.z;
+    wsv[4 * v + 3] = w4.w;
+  }
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int64_t m = t.row_base + wm * TM + 32 * fm + r32;
+    if (m < t.row_end) {
+      const float xsv = a.xs[m];
+      uint16_t* yrow = a.Y + m * N;
+#pragma unroll
+      for (int s = 0; s < 2 * FN; ++s) {           // 8 columns per 16-byte store
+        const int64_t c = col0 + 8 * s;
+        if (c < N) {
+          const int fn = s >> 1;
+          const int base = (s & 1) * 8;
+          uint32_t pk[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float v0 = (acc[fm][fn][base + 2 * e] * xsv) * wsv[16 * fn + base + 2 * e];
+            const float v1 = (acc[fm][fn][base + 2 * e + 1] * xsv) * wsv[16 * fn + base + 2 * e + 1];
+            pk[e] = pack_bf16x2(v0, v1);
+          }
+          *(v4i*)(yrow + c) = v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+        }
+      }
+    } else if (m < t.zero_end) {
+      uint16_t* yrow = a.Y + m * N;
+#pragma unroll
+      for (int s = 0; s < 2 * FN; ++s) {
+        const int64_t c = col0 + 8 * s;
+        if (c < N) *(v4i*)(yrow + c) = v4i{0, 0, 0, 0};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Zero fill (K == 0): a plain kernel rather than a memset, so the call can be
+// captured into a graph without a memset node.
+// ---------------------------------------------------------------------------
+
+__global__ void __launch_bounds__(256) zero_fill_kernel(v4i* __restrict__ y, int64_t n_vec) {
+  const v4i z = {0, 0, 0, 0};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n_vec; i += (int64_t)gridDim.x * 256) y[i] = z;
+}
+
+// ---------------------------------------------------------------------------
+// Configuration table and launch dispatch
+// ---------------------------------------------------------------------------
+
+//                               BM   BN  WM WN stages preshuffled
+const KernelConfig kConfigs[] = {
+    /* 0 */ {256, 256, 2, 4, 2, 0},
+    /* 1 */ {128, 256, 2, 4, 2, 0},
+    /* 2 */ {64, 256, 1, 4, 2, 0},
+    /* 3 */ {32, 128, 1, 4, 2, 0},
+};
+const int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
+
+template <int LAYOUT, int BM, int BN, int WM, int WN, int STAGES>
+static hipError_t launch_lds(bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
+  const dim3 block(WM * WN * 64);
+  if (k_tail)
+    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, WM, WN, STAGES, true>), dim3((uint32_t)grid), block, 0, s, a);
+  else
+    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, WM, WN, STAGES, false>), dim3((uint32_t)grid), block, 0, s, a);
+  return hipGetLastError();
+}
+
+template <int LAYOUT>
+static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
+  switch (config_id) {
+    case 0: return launch_lds<LAYOUT, 256, 256, 2, 4, 2>(k_tail, a, grid, s);
+    case 1: return launch_lds<LAYOUT, 128, 256, 2, 4, 2>(k_tail, a, grid, s);
+    case 2: return launch_lds<LAYOUT, 64, 256, 1, 4, 2>(k_tail, a, grid, s);
+    case 3: return launch_lds<LAYOUT, 32, 128, 1, 4, 2>(k_tail, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm(int layout, int config_id, bool k_tail, const GemmArgs& a, int64_t grid,
+                       hipStream_t s) {
+  if (layout == kStacked) return launch_layout<kStacked>(config_id, k_tail, a, grid, s);
+  return launch_layout<kPadded>(config_id, k_tail, a, grid, s);
+}
+
+hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t s) {
+  const int64_t n_vec = n_elems / 8;  // N % 8 == 0, so the output is whole 16-byte vectors
+  if (n_vec == 0) return hipSuccess;
+  int64_t blocks = (n_vec + 255) / 256;
+  blocks = blocks > 4096 ? 4096 : blocks;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, (v4i*)Y, n_vec);
+  return hipGetLastError();
+}
+
+hipError_t launch_shuffle_b(const uint8_t*, uint8_t*, int64_t, int64_t, int64_t, hipStream_t) {
+  return hipErrorNotSupported;
+}
+
+}  // namespace fp8gg

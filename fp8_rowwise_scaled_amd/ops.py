@@ -1,0 +1,124 @@
+"""Python entry points over the C ABI: argument marshalling only.
+
+Every computation runs in the HIP kernels of libfp8gg.so; torch supplies device
+memory and the current stream.  There is no CPU fallback: without the built
+library these functions raise.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+
+_FP8 = getattr(torch, "float8_e4m3fn", None)
+
+
+def _bytes(t: torch.Tensor, name: str) -> torch.Tensor:
+    if _FP8 is not None and t.dtype == _FP8:
+        t = t.view(torch.uint8)
+    if t.dtype != torch.uint8:
+        raise ValueError(f"{name} must be float8_e4m3fn or uint8 (raw e4m3fn bytes), got {t.dtype}")
+    return t
+
+
+def _check(t: torch.Tensor, name: str, dtype, shape) -> None:
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _stacked(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out):
+    XQ = _bytes(XQ, "XQ")
+    WQ = _bytes(WQ, "WQ")
+    if XQ.dim() != 2 or WQ.dim() != 3:
+        raise ValueError("XQ must be [total_M, K] and WQ [G, N, K]")
+    total_M, K = XQ.shape
+    G, N, K2 = WQ.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: XQ has {K}, WQ has {K2}")
+    _check(XQ, "XQ", torch.uint8, (total_M, K))
+    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _check(x_scale, "x_scale", torch.float32, (total_M,))
+    _check(w_scale, "w_scale", torch.float32, (G, N))
+    _check(M_sizes, "M_sizes", torch.int64, (G,))
+    if out is None:
+        out = torch.empty((total_M, N), dtype=torch.bfloat16, device=XQ.device)
+    _check(out, "out", torch.bfloat16, (total_M, N))
+    lib = _lib.load()
+    st = getattr(lib, fn_name)(XQ.data_ptr(), WQ.data_ptr(), x_scale.data_ptr(), w_scale.data_ptr(),
+                               M_sizes.data_ptr(), out.data_ptr(), G, total_M, N, K, _stream(XQ.device))
+    _lib.check(st, fn_name)
+    return out
+
+
+def _dynamic(fn_name, XQ, WQ, x_scale, w_scale, zero_start_index_M, zeroing_output_tensor, out):
+    XQ = _bytes(XQ, "XQ")
+    WQ = _bytes(WQ, "WQ")
+    if XQ.dim() != 3 or WQ.dim() != 3:
+        raise ValueError("XQ must be [G, expected_m, K] and WQ [G, N, K]")
+    G, em, K = XQ.shape
+    G2, N, K2 = WQ.shape
+    if G2 != G or K2 != K:
+        raise ValueError(f"shape mismatch: XQ {tuple(XQ.shape)} vs WQ {tuple(WQ.shape)}")
+    _check(XQ, "XQ", torch.uint8, (G, em, K))
+    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _check(x_scale, "x_scale", torch.float32, (G, em))
+    _check(w_scale, "w_scale", torch.float32, (G, N))
+    _check(zero_start_index_M, "zero_start_index_M", torch.int64, (G,))
+    if out is None:
+        out = torch.empty((G, em, N), dtype=torch.bfloat16, device=XQ.device)
+    _check(out, "out", torch.bfloat16, (G, em, N))
+    lib = _lib.load()
+    st = getattr(lib, fn_name)(XQ.data_ptr(), WQ.data_ptr(), x_scale.data_ptr(), w_scale.data_ptr(),
+                               zero_start_index_M.data_ptr(), out.data_ptr(), G, em, N, K,
+                               int(bool(zeroing_output_tensor)), _stream(XQ.device))
+    _lib.check(st, fn_name)
+    return out
+
+
+def f8f8bf16_rowwise_grouped_stacked(XQ, WQ, x_scale, w_scale, M_sizes, out=None):
+    """Y [total_M, N] bf16 for the stacked layout (see include/fp8gg.h)."""
+    return _stacked("f8f8bf16_rowwise_grouped_stacked", XQ, WQ, x_scale, w_scale, M_sizes, out)
+
+
+def f8f8bf16_rowwise_grouped_stacked_preshuffle(XQ, WQs, x_scale, w_scale, M_sizes, out=None):
+    """As the stacked op, with WQs produced by f8f8bf16_shuffle_b."""
+    return _stacked("f8f8bf16_rowwise_grouped_stacked_preshuffle", XQ, WQs, x_scale, w_scale, M_sizes, out)
+
+
+def f8f8bf16_rowwise_grouped_dynamic(XQ, WQ, x_scale, w_scale, zero_start_index_M,
+                                     zeroing_output_tensor=True, out=None):
+    """Y [G, expected_m, N] bf16 for the padded layout (see include/fp8gg.h)."""
+    return _dynamic("f8f8bf16_rowwise_grouped_dynamic", XQ, WQ, x_scale, w_scale, zero_start_index_M,
+                    zeroing_output_tensor, out)
+
+
+def f8f8bf16_rowwise_grouped_dynamic_preshuffle(XQ, WQs, x_scale, w_scale, zero_start_index_M,
+                                                zeroing_output_tensor=True, out=None):
+    """As the dynamic op, with WQs produced by f8f8bf16_shuffle_b."""
+    return _dynamic("f8f8bf16_rowwise_grouped_dynamic_preshuffle", XQ, WQs, x_scale, w_scale,
+                    zero_start_index_M, zeroing_output_tensor, out)
+
+
+def f8f8bf16_shuffle_b(WQ, out=None):
+    """Rearranges WQ [G, N, K] into the pre-shuffled layout (same shape and bytes)."""
+    WQ = _bytes(WQ, "WQ")
+    if WQ.dim() != 3:
+        raise ValueError("WQ must be [G, N, K]")
+    G, N, K = WQ.shape
+    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    if out is None:
+        out = torch.empty_like(WQ)
+    _check(out, "out", torch.uint8, (G, N, K))
+    st = _lib.load().f8f8bf16_shuffle_b(WQ.data_ptr(), out.data_ptr(), G, N, K, _stream(WQ.device))
+    _lib.check(st, "f8f8bf16_shuffle_b")
+    return out

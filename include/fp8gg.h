@@ -1,0 +1,168 @@
+/*
+ * fp8gg.h -- C ABI of the FP8 (e4m3fn) rowwise-scaled grouped GEMM for MI355X (gfx950).
+ *
+ * Per expert group g the library computes
+ *
+ *     Y_g[m, n] = bf16_rne( (sum_k XQ_g[m, k] * WQ[g, n, k]) * x_scale[m] * w_scale[g, n] )
+ *
+ * with fp8 e4m3fn operands, fp32 accumulation of the unscaled products, the two
+ * scales applied once after the reduction, and round-to-nearest-even to bf16.
+ * Source of the operation: MSLK pull request 471, "Back the FP8 rowwise grouped
+ * GEMM ops with FlyDSL on ROCm" -- Summary (op table: the stacked op with [G]
+ * int64 row counts, the dynamic op with [G, M, K] slabs and a runtime valid-row
+ * count, and the preshuffle siblings) and Design notes (rowwise scales factor out
+ * of the K loop and are applied once in the epilogue).
+ *
+ * Conventions shared by every entry point
+ *   - All tensor pointers are DEVICE pointers.  All tensors are dense and row-major
+ *     (contiguous); there are no stride arguments.  The caller owns every buffer.
+ *   - fp8 operands are raw e4m3fn bytes (uint8_t); Y is raw bf16 bits (uint16_t).
+ *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is only
+ *     enqueued: no entry point allocates device memory, copies between host and
+ *     device, or synchronises, so every call may be captured into a HIP graph.
+ *   - Device-side metadata (M_sizes, zero_start_index_M) is never read by the host.
+ *     The kernels clamp it (negative counts -> 0, cumulative row ends -> total_M,
+ *     valid rows -> [0, expected_m]), so inconsistent metadata can never cause an
+ *     out-of-bounds access; the values computed for it are then unspecified.
+ *   - Shape rules: K % 16 == 0 and N % 8 == 0 (a 16-byte load granule along K and
+ *     an 8-column store granule along N; MSLK #471 commits on the K-tail and N-tail
+ *     variants).  K need not be a multiple of the K tile, N not of the N tile.
+ *   - Alignment: XQ, WQ, w_scale and Y must be 16-byte aligned; x_scale 4-byte.
+ *   - Y must not overlap any input.
+ *   - K == 0: the whole output is zero-filled (a contraction over nothing sums to
+ *     zero; MSLK #471 commit on zero-length reductions).  An output with no
+ *     elements launches nothing.
+ *   - Errors: every check runs on the host before anything is enqueued.  A failed
+ *     check returns a non-zero status, enqueues nothing and leaves a message for
+ *     f8f8bf16_last_error().  A launch failure returns FP8GG_ERR_HIP.
+ *   - The library is re-entrant; calls on different streams may run concurrently.
+ */
+#ifndef FP8GG_H_
+#define FP8GG_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FP8GG_OK = 0,
+  FP8GG_ERR_INVALID_ARGUMENT = 1,  /* null pointer, negative size, misalignment, aliasing */
+  FP8GG_ERR_UNSUPPORTED_SHAPE = 2, /* K % 16 != 0, N % 8 != 0, preshuffle granules, limits */
+  FP8GG_ERR_HIP = 3                /* the HIP runtime reported an error at launch */
+} fp8gg_status;
+
+/*
+ * Stacked layout (MSLK #471: Summary op table, stacked row; commit adding the
+ * layout enum, layout "sizes").  Groups are concatenated along M: group g owns
+ * the next M_sizes[g] rows of XQ / x_scale / Y, starting after groups 0..g-1.
+ *
+ *   XQ        [total_M, K]   fp8 e4m3fn activations
+ *   WQ        [G, N, K]      fp8 e4m3fn weights (one [N, K] matrix per group)
+ *   x_scale   [total_M]      fp32, one scale per row of XQ
+ *   w_scale   [G, N]         fp32, one scale per output column of each group
+ *   M_sizes   [G]            int64 row counts, on the device
+ *   Y         [total_M, N]   bf16 output
+ *
+ * Rows at or beyond sum(M_sizes) (clamped to total_M) are not written.
+ */
+fp8gg_status f8f8bf16_rowwise_grouped_stacked(
+    const uint8_t* XQ, const uint8_t* WQ, const float* x_scale, const float* w_scale,
+    const int64_t* M_sizes, uint16_t* Y,
+    int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Padded ("dynamic") layout (MSLK #471: Summary op table, dynamic row; commits
+ * adding the padded layout and its test).  Each group owns a slab of expected_m
+ * rows; only the first zero_start_index_M[g] rows of slab g are valid.
+ *
+ *   XQ                  [G, expected_m, K]  fp8 e4m3fn
+ *   WQ                  [G, N, K]           fp8 e4m3fn
+ *   x_scale             [G, expected_m]     fp32
+ *   w_scale             [G, N]              fp32
+ *   zero_start_index_M  [G]                 int64 valid-row counts, on the device
+ *   Y                   [G, expected_m, N]  bf16
+ *   zeroing_output_tensor  non-zero: padding rows of Y are written as +0.0;
+ *                          zero: padding rows are left untouched.
+ *
+ * Padding rows of XQ and x_scale may hold anything (NaN included): they never
+ * reach a written output.
+ */
+fp8gg_status f8f8bf16_rowwise_grouped_dynamic(
+    const uint8_t* XQ, const uint8_t* WQ, const float* x_scale, const float* w_scale,
+    const int64_t* zero_start_index_M, uint16_t* Y,
+    int64_t G, int64_t expected_m, int64_t N, int64_t K,
+    int zeroing_output_tensor, void* stream);
+
+/*
+ * Pre-shuffled weights (MSLK #471: commit registering the stacked op and its
+ * preshuffle sibling; Design notes on preshuffled B: offered only where each
+ * group owns a whole [N, K]).  WQs is WQ rearranged once by f8f8bf16_shuffle_b
+ * into the order in which the matrix cores consume it; it has the same byte
+ * count as WQ.  Additional shape rule: N % FP8GG_SHUFFLE_N == 0 and
+ * K % FP8GG_SHUFFLE_K == 0 (the shuffle interleaves N and K, so a partial block
+ * cannot be masked).  All other arguments are as in the plain entry points.
+ */
+#define FP8GG_SHUFFLE_N 32
+#define FP8GG_SHUFFLE_K 64
+
+fp8gg_status f8f8bf16_rowwise_grouped_stacked_preshuffle(
+    const uint8_t* XQ, const uint8_t* WQs, const float* x_scale, const float* w_scale,
+    const int64_t* M_sizes, uint16_t* Y,
+    int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
+
+fp8gg_status f8f8bf16_rowwise_grouped_dynamic_preshuffle(
+    const uint8_t* XQ, const uint8_t* WQs, const float* x_scale, const float* w_scale,
+    const int64_t* zero_start_index_M, uint16_t* Y,
+    int64_t G, int64_t expected_m, int64_t N, int64_t K,
+    int zeroing_output_tensor, void* stream);
+
+/*
+ * Rearranges WQ [G, N, K] into the pre-shuffled order WQs (same size, must not
+ * overlap WQ).  Byte layout: for group g, N-block nb (FP8GG_SHUFFLE_N rows) and
+ * K-block kb (FP8GG_SHUFFLE_K bytes), the 2048-byte block at
+ *     ((g * N/32 + nb) * K/64 + kb) * 2048
+ * holds, for lane l in [0, 64), the 32 bytes WQ[g, nb*32 + (l % 32),
+ * kb*64 + (l / 32)*32 .. +32) at offset l*32.  Same shape rules as the
+ * preshuffled GEMMs.
+ */
+fp8gg_status f8f8bf16_shuffle_b(const uint8_t* WQ, uint8_t* WQs,
+                                int64_t G, int64_t N, int64_t K, void* stream);
+
+/* Message describing the last failure on the calling thread ("" if none). */
+const char* f8f8bf16_last_error(void);
+
+/*
+ * Launch plan, computed on the host only (no HIP call).  Exposed so that tests
+ * and offline tuning can see what a call would launch.
+ */
+typedef struct {
+  int32_t config_id;  /* index of the kernel configuration; -1 = nothing to compute */
+  int32_t BM, BN, BK; /* workgroup tile: rows of XQ, columns of Y, bytes of K      */
+  int32_t threads;    /* threads per workgroup                                      */
+  int32_t stages;     /* LDS pipeline depth                                         */
+  int32_t k_tail;     /* 1 if K % BK != 0 (the last K tile is masked)               */
+  int32_t n_tail;     /* 1 if N % BN != 0 (the last N tile is masked)               */
+  int64_t m_tiles;    /* stacked: upper bound of M tiles; padded: tiles per slab    */
+  int64_t n_tiles;
+  int64_t grid;       /* workgroups launched by the GEMM kernel                     */
+  int32_t zero_fill;  /* 1 if the call zero-fills Y instead (K == 0)                */
+  int32_t lds_bytes;  /* LDS per workgroup                                          */
+} fp8gg_plan;
+
+enum { FP8GG_LAYOUT_STACKED = 0, FP8GG_LAYOUT_PADDED = 1 };
+
+/* M is total_M for the stacked layout and expected_m for the padded one.
+ * Performs the same shape checks as the GEMM entry points. */
+fp8gg_status f8f8bf16_plan(int layout, int preshuffled, int64_t G, int64_t M,
+                           int64_t N, int64_t K, fp8gg_plan* out);
+
+/* Number of kernel configurations compiled into the library (for tuning). */
+int32_t f8f8bf16_num_configs(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP8GG_H_ */

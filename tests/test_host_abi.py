@@ -1,0 +1,101 @@
+"""CPU-only checks of the C ABI: the library loads, exports every declared
+symbol, plans launches, and refuses bad arguments before touching the GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_rowwise_scaled_amd as F
+from fp8_rowwise_scaled_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fp8gg.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(f8f8bf16_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert len(names) == 8
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_lib.EXPORTS)
+
+
+def test_plan_gate_up():
+    p = F.plan(F.LAYOUT_STACKED, False, 8, 4096, 4096, 7168)
+    assert p["config_id"] >= 0 and p["k_tail"] == 0 and p["zero_fill"] == 0
+    # upper bound of M tiles: ceil(total_M / BM) + G - 1, at most total_M
+    assert p["m_tiles"] == min(-(-4096 // p["BM"]) + 7, 4096)
+    assert p["n_tiles"] == -(-4096 // p["BN"])
+    assert p["grid"] == p["m_tiles"] * p["n_tiles"]
+
+
+def test_plan_padded_tails():
+    p = F.plan(F.LAYOUT_PADDED, False, 16, 512, 1000, 7184)
+    assert p["k_tail"] == (7184 % p["BK"] != 0) == 1
+    assert p["n_tail"] == (1000 % p["BN"] != 0)
+    assert p["grid"] == p["m_tiles"] * p["n_tiles"] * 16
+
+
+def test_plan_small_m_bound():
+    p = F.plan(F.LAYOUT_STACKED, False, 8, 1, 7168, 2048)
+    assert p["m_tiles"] == 1      # one row can fill at most one tile
+
+
+def test_plan_empty_and_k_zero():
+    assert F.plan(F.LAYOUT_STACKED, False, 8, 0, 64, 64)["config_id"] == -1
+    assert F.plan(F.LAYOUT_STACKED, False, 8, 16, 0, 64)["config_id"] == -1
+    p = F.plan(F.LAYOUT_PADDED, False, 2, 16, 64, 0)
+    assert p["zero_fill"] == 1 and p["config_id"] == -1
+
+
+@pytest.mark.parametrize("G,M,N,K", [(1, 4, 8, 24), (1, 4, 12, 32), (-1, 4, 8, 16), (1, -4, 8, 16)])
+def test_plan_refuses_bad_shapes(G, M, N, K):
+    with pytest.raises(ValueError):
+        F.plan(F.LAYOUT_STACKED, False, G, M, N, K)
+
+
+def test_preshuffle_granule_rule():
+    with pytest.raises(ValueError):
+        F.plan(F.LAYOUT_STACKED, True, 2, 64, 40, 128)   # N % 32
+    with pytest.raises(ValueError):
+        F.plan(F.LAYOUT_STACKED, True, 2, 64, 64, 80)    # K % 64
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_entry_points_refuse_before_any_gpu_call():
+    lib = _lib.load()
+    a = 0x10000000  # never dereferenced: every call below fails host-side checks
+    # K % 16
+    st = lib.f8f8bf16_rowwise_grouped_stacked(a, a, a, a, a, a + 0x1000000, 2, 8, 16, 24, None)
+    assert st == _lib.ERR_UNSUPPORTED_SHAPE and "multiple of 16" in F.last_error()
+    # null input
+    st = lib.f8f8bf16_rowwise_grouped_stacked(None, a, a, a, a, a + 0x1000000, 2, 8, 16, 32, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT and "null" in F.last_error()
+    # misaligned Y
+    st = lib.f8f8bf16_rowwise_grouped_dynamic(a, a, a, a, a, a + 0x1000002, 2, 8, 16, 32, 1, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT and "aligned" in F.last_error()
+    # Y overlapping XQ
+    st = lib.f8f8bf16_rowwise_grouped_stacked(a, a + 0x100000, a + 0x200000, a + 0x300000, a + 0x400000,
+                                              a + 0x10, 2, 8, 16, 32, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT and "overlaps" in F.last_error()
+    # shuffle with overlap
+    st = lib.f8f8bf16_shuffle_b(a, a + 64, 1, 32, 64, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT
+    # empty output: nothing to do, even with null pointers
+    st = lib.f8f8bf16_rowwise_grouped_stacked(None, None, None, None, None, None, 4, 0, 16, 32, None)
+    assert st == _lib.OK and F.last_error() == ""
+
+
+def test_num_configs():
+    assert _lib.load().f8f8bf16_num_configs() >= 1
