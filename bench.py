@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Benchmark of the fp8 rowwise-scaled grouped GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+A step is one call of the grouped GEMM (group resolution, K loop, scaled
+epilogue) over one batch of the workload's inputs, which are resident in HBM
+before timing starts.  Prints ONE JSON line on stdout; diagnostics go to stderr.
+
+Timing: W untimed warm-up calls, then exactly K timed calls bracketed by device
+synchronisation.  Each call is also bracketed by HIP events recorded on the
+stream the kernel runs on, which gives the kernel's average duration for the
+roofline figure.  When a workload's bytes are small against the 256 MB
+Infinity Cache, calls rotate over several copies of the inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fp8 rowwise grouped GEMM TFLOPS (valid rows), % fp8 MFMA peak; µs/call at M<=32"
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+MALL_BYTES = 256 * 2 ** 20    # Infinity Cache
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+WORKLOADS = ["moe_gate_up", "tiny_stacked", "dense_expert", "dense_expert_preshuffle", "padded_tails"] + [
+    f"moe_down_M{m}" for m in (1, 8, 32, 256, 2048, 8192)]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def make_workload(name):
+    import workloads as wl
+    if name == "moe_gate_up":
+        return wl.moe_gate_up(), "stacked", False
+    if name == "tiny_stacked":
+        return wl.tiny_stacked(), "stacked", False
+    if name == "dense_expert":
+        return wl.dense_expert(), "stacked", False
+    if name == "dense_expert_preshuffle":
+        return wl.dense_expert(), "stacked", True
+    if name == "padded_tails":
+        return wl.padded_tails(), "padded", False
+    if name.startswith("moe_down_M"):
+        return wl.moe_down(int(name[len("moe_down_M"):])), "stacked", False
+    raise ValueError(name)
+
+
+def algorithmic_work(w, layout):
+    """flop = 2 N K R; bytes = R K + G_ne N K + 4 R + 4 G_ne N + 2 N R_out + 8 G.
+
+    R = valid rows, G_ne = groups with a valid row, R_out = rows written (valid
+    rows plus zeroed padding rows).  Unread weights of empty groups and unread
+    padding inputs are not counted."""
+    import numpy as np
+    G, N, K = w.G, w.N, w.K
+    if layout == "stacked":
+        sizes = np.clip(w.M_sizes, 0, None)
+        R = int(min(sizes.sum(), w.total_M))
+        G_ne = int(np.count_nonzero(sizes))
+        R_out = R
+    else:
+        z = np.clip(w.zero_start_index_M, 0, w.expected_m)
+        R = int(z.sum())
+        G_ne = int(np.count_nonzero(z))
+        R_out = G * w.expected_m
+    flop = 2 * N * K * R
+    nbytes = R * K + G_ne * N * K + 4 * R + 4 * G_ne * N + 2 * N * R_out + 8 * G
+    return flop, nbytes, R, G_ne
+
+
+def kernel_source_hash():
+    csrc = os.path.join(ROOT, "fp8_rowwise_scaled_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".hip", ".cpp", ".h")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, src_hash):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none for this workload or the kernels changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get("workloads", {}).get(workload)
+    if not e or e.get("kernel_hash") != src_hash:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=3):
+    """The oracle as it stands, on the full workload, on this host's cores."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < max_runs and (time.perf_counter() - t_all) < min_seconds:
+        t0 = time.perf_counter()
+        if layout == "stacked":
+            oracle.grouped_stacked(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
+        else:
+            oracle.grouped_dynamic(w.XQ, w.WQ, w.x_scale, w.w_scale, w.zero_start_index_M, True)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    return {"value": round(flop / med / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"the full workload, {len(times)} run(s), median {med:.3f} s per call "
+                      "(e4m3fn table decode, fp64 matmul per group, fp64 scales, bf16 RNE)"}
+
+
+def copy_calibration(nbytes):
+    """A plain device copy of known size, profiled beside the GEMM to scale the
+    HBM byte counters."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {nbytes} bytes read and written per copy, 5 copies")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=1000)
+    ap.add_argument("--workload", default="moe_gate_up", choices=WORKLOADS)
+    ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate over (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of this many bytes (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this build has no "
+              "multi-GPU path; the grouped GEMM shards by expert group, one process per GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import fp8_rowwise_scaled_amd as F
+
+    F.load()
+    w, layout, pre = make_workload(args.workload)
+    flop, nbytes, R, G_ne = algorithmic_work(w, layout)
+    log(f"workload {w.name}: layout={layout} preshuffled={pre} G={w.G} N={w.N} K={w.K} R={R} G_ne={G_ne} "
+        f"flop={flop:.4g} bytes={nbytes:.4g}")
+
+    dev = torch.device("cuda", 0)
+    touched = nbytes
+    rotate = args.rotate or max(1, min(64, math.ceil(2 * MALL_BYTES / max(touched, 1))))
+    X = torch.from_numpy(w.XQ).to(dev)
+    Wt = torch.from_numpy(w.WQ).to(dev)
+    xs = torch.from_numpy(w.x_scale).to(dev)
+    ws = torch.from_numpy(w.w_scale).to(dev)
+    meta = torch.from_numpy(w.M_sizes if layout == "stacked" else w.zero_start_index_M).to(dev)
+    if pre:
+        Wt = F.f8f8bf16_shuffle_b(Wt)
+    sets = [(X, Wt, xs, ws, meta)]
+    for _ in range(rotate - 1):
+        sets.append(tuple(t.clone() for t in sets[0]))
+    outs = [torch.empty((w.total_M, w.N) if layout == "stacked" else (w.G, w.expected_m, w.N),
+                        dtype=torch.bfloat16, device=dev) for _ in range(rotate)]
+    log(f"rotating over {rotate} input set(s)")
+
+    if layout == "stacked":
+        fn = F.f8f8bf16_rowwise_grouped_stacked_preshuffle if pre else F.f8f8bf16_rowwise_grouped_stacked
+
+        def call(i):
+            s = sets[i % rotate]
+            fn(s[0], s[1], s[2], s[3], s[4], out=outs[i % rotate])
+    else:
+        fn = F.f8f8bf16_rowwise_grouped_dynamic_preshuffle if pre else F.f8f8bf16_rowwise_grouped_dynamic
+
+        def call(i):
+            s = sets[i % rotate]
+            fn(s[0], s[1], s[2], s[3], s[4], zeroing_output_tensor=True, out=outs[i % rotate])
+
+    stream = torch.cuda.current_stream(dev)
+    for i in range(args.warmup):
+        call(i)
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        call(i)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
+    avg = sum(durs) / len(durs)
+    med = statistics.median(durs)
+    ms_per_step = wall / args.steps * 1e3
+    value = flop / (wall / args.steps) / 1e12
+    log(f"per call: wall {ms_per_step * 1e3:.2f} us, kernel avg {avg * 1e6:.2f} us, median {med * 1e6:.2f} us, "
+        f"min {min(durs) * 1e6:.2f} us")
+
+    mfma_bound = flop / (PEAK_FP8_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9)
+    src_hash = kernel_source_hash()
+    traffic = measured_traffic(args.workload, src_hash)
+    if mfma_bound:
+        achieved = flop / avg / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
+    else:
+        achieved = nbytes / avg / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+    log(f"kernel: {flop / avg / 1e12:.1f} TFLOP/s ({flop / avg / 1e12 / PEAK_FP8_TFLOPS:.1%} of fp8 peak), "
+        f"{nbytes / avg / 1e9:.0f} GB/s ({nbytes / avg / 1e9 / PEAK_HBM_GBS:.1%} of HBM); source hash {src_hash}")
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3fn",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name,
+            "layout": layout,
+            "preshuffled": pre,
+            "G": w.G,
+            "rows": int(w.total_M if layout == "stacked" else w.G * w.expected_m),
+            "valid_rows": R,
+            "N": w.N,
+            "K": w.K,
+            "group_rows": (w.M_sizes if layout == "stacked" else w.zero_start_index_M).tolist(),
+            "rotating_input_sets": rotate,
+            "us_per_call": round(avg * 1e6, 3),
+        },
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle ...")
+        result["cpu_baseline"] = cpu_baseline(w, layout, flop)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
