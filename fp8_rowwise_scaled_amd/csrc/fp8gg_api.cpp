@@ -85,8 +85,12 @@ fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int6
 int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
   (void)K;
   (void)N;
-  if (preshuffled) return -1;
   const int64_t per_group = layout == FP8GG_LAYOUT_STACKED ? (G > 0 ? (M + G - 1) / G : M) : M;
+  if (preshuffled) {
+    if (per_group >= 128) return 4;
+    if (per_group >= 48) return 5;
+    return 6;
+  }
   if (per_group >= 256) return 0;
   if (per_group >= 128) return 1;
   if (per_group >= 48) return 2;

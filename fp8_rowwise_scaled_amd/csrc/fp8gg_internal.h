@@ -29,8 +29,9 @@ struct KernelConfig {
   int BM;       // rows of X per workgroup
   int BN;       // columns of Y (rows of W) per workgroup
   int WM, WN;   // waves along M and N (threads = 64 * WM * WN)
-  int stages;   // LDS pipeline depth
+  int stages;   // LDS pipeline depth (X and W; X only when W is pre-shuffled)
   int preshuffled;  // 1: W is read from the pre-shuffled layout straight into registers
+  int wdepth;   // pre-shuffled: K steps of W fragments held in flight in registers
 };
 
 constexpr int kBK = 64;          // K bytes per pipeline stage (one 32x32x64 fp8 MFMA)

@@ -139,6 +139,9 @@ __device__ __forceinline__ bool resolve_padded(const GemmArgs& a, int64_t g, int
   return t.row_base < t.zero_end;
 }
 
+// First 32-column block of wave w's slice when each wave covers TN columns.
+__device__ __forceinline__ int64_t wn_block(int w, int TN) { return (int64_t)w * (TN / 32); }
+
 // Writes zeros into rows [r0, r1) x columns [c0, c1) of Y (16-byte vectors).
 template <int NT>
 __device__ __forceinline__ void zero_rect(uint16_t* Y, int64_t N, int64_t r0, int64_t r1,
@@ -373,6 +376,230 @@ gg_lds_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Pre-shuffled W: the grouped GEMM with W read straight into registers
+// ---------------------------------------------------------------------------
+//
+// Layout of the pre-shuffled weights (also declared with f8f8bf16_shuffle_b): for
+// group g, 32-row block nb and 64-byte K block kb, the 2048 bytes at
+// ((g * N/32 + nb) * K/64 + kb) * 2048 hold, at offset 32*l for lane l, the bytes
+// W[g, 32*nb + l % 32, 64*kb + 32*(l / 32) .. +32).  That is exactly the MFMA A
+// operand of one 32x32x64 step, so a wave fetches it with one contiguous 2 KB read
+// and W never passes through LDS.  X still goes global -> LDS (double-buffered) and
+// is shared by the waves of a workgroup, which all split N (one wave row).
+//
+// W fragments are prefetched WDEPTH K steps ahead into a register ring; the K loop
+// is unrolled by WDEPTH so that every ring slot is a compile-time register.
+
+__global__ void __launch_bounds__(256) shuffle_b_kernel(const v4i* __restrict__ W, v4i* __restrict__ Ws,
+                                                        int64_t G, int64_t N, int64_t K) {
+  // One 16-byte output chunk per iteration: chunk o of block b is lane (o % 128) / 2,
+  // half o % 2 of the block's 2048 bytes.
+  const int64_t nb_n = N / 32, nb_k = K / 64;
+  const int64_t total = G * N * K / 16;
+  for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
+    const int64_t blk = o / 128;
+    const int within = (int)(o % 128);
+    const int lane = within >> 1;
+    const int half = within & 1;
+    const int64_t kb = blk % nb_k;
+    const int64_t gnb = blk / nb_k;         // g * N/32 + nb
+    const int64_t g = gnb / nb_n;
+    const int64_t nb = gnb % nb_n;
+    const int64_t row = nb * 32 + (lane & 31);
+    const int64_t col = kb * 64 + (lane >> 5) * 32 + half * 16;
+    Ws[o] = W[((g * N + row) * K + col) / 16];
+  }
+}
+
+template <int LAYOUT, int BM, int BN, int WN, int WDEPTH>
+__global__ void __launch_bounds__(WN * 64)
+gg_pre_kernel(GemmArgs a) {
+  constexpr int NT = WN * 64;
+  constexpr int BK = kBK;
+  constexpr int TN = BN / WN;           // wave tile along N
+  constexpr int FM = BM / 32;
+  constexpr int FN = TN / 32;
+  constexpr int A_CHUNKS = BM * BK / 16;
+  constexpr int A_LOADS = (A_CHUNKS + NT - 1) / NT;
+  constexpr int STAGE_BYTES = BM * BK;
+  static_assert(BM % 32 == 0 && TN % 32 == 0, "tiles must be multiples of 32");
+  static_assert(A_CHUNKS % 64 == 0, "tile rows must be a multiple of 16");
+
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE_BYTES];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int64_t bid = blockIdx.x;
+  const int64_t n_tile = bid % a.n_tiles;
+  const int64_t rest = bid / a.n_tiles;
+  Tile t;
+  if (LAYOUT == kStacked) {
+    if (!resolve_stacked<BM>(a, rest, t)) return;
+  } else {
+    if (!resolve_padded<BM>(a, rest / a.m_tiles, rest % a.m_tiles, t)) return;
+  }
+  const int64_t N = a.N;
+  const int64_t K = a.K;
+  const int64_t n0 = n_tile * BN;
+  const int64_t tile_row_end = t.row_base + BM;
+
+  if (t.row_base >= t.row_end) {
+    const int64_t r1 = tile_row_end < t.zero_end ? tile_row_end : t.zero_end;
+    const int64_t c1 = n0 + BN < N ? n0 + BN : N;
+    zero_rect<NT>(a.Y, N, t.row_base, r1, n0, c1);
+    return;
+  }
+
+  const uint8_t* a_src[A_LOADS];
+#pragma unroll
+  for (int i = 0; i < A_LOADS; ++i) {
+    const int q = i * NT + tid;
+    const int p = (q >> 2) % BM;
+    const int c = (q & 3) ^ ((p >> 1) & 3);
+    int64_t row = t.row_base + p;
+    row = row < t.row_end ? row : t.row_end - 1;
+    a_src[i] = a.X + row * K + c * 16;
+  }
+  const int64_t nblk_n = N / 32;
+  const int64_t nblk_k = K / 64;
+  const uint8_t* w_src[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    int64_t nb = n0 / 32 + wn_block(wave, TN) + fn;
+    nb = nb < nblk_n ? nb : nblk_n - 1;            // blocks past N: result dropped
+    w_src[fn] = a.W + ((t.g * nblk_n + nb) * nblk_k) * 2048 + lane * 32;
+  }
+
+  const int nk = (int)(K / BK);
+  auto issue_x = [&](int kt) {
+    uint8_t* sbase = smem + (kt & 1) * STAGE_BYTES;
+    const int64_t koff = (int64_t)kt * BK;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i)
+      if (A_CHUNKS % NT == 0 || i * NT + wave * 64 < A_CHUNKS)
+        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(a_src[i] + koff),
+                                         (lds_ptr_t)(sbase + (i * NT + wave * 64) * 16), 16, 0, 0);
+  };
+  auto load_w = [&](int kt, v8i (&dst)[FN]) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const v4i* p = (const v4i*)(w_src[fn] + (int64_t)kt * 2048);
+      const v4i lo = p[0];
+      const v4i hi = p[1];
+      dst[fn] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    }
+  };
+
+  v16f acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{0};
+
+  v8i wr[WDEPTH][FN];
+#pragma unroll
+  for (int d = 0; d < WDEPTH; ++d)
+    if (d < nk) load_w(d, wr[d]);
+  asm volatile("" ::: "memory");
+  issue_x(0);
+
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  for (int kt0 = 0; kt0 < nk; kt0 += WDEPTH) {
+#pragma unroll
+    for (int d = 0; d < WDEPTH; ++d) {
+      const int kt = kt0 + d;
+      if (kt < nk) {
+        // X(kt) was the last copy issued before the W loads of step kt-1+WDEPTH.
+        if (kt == 0) wait_vmcnt_le(0);
+        else wait_vmcnt_le(kt - 1 + WDEPTH < nk ? 2 * FN : 0);
+        block_barrier();
+        if (kt + 1 < nk) issue_x(kt + 1);
+        asm volatile("" ::: "memory");
+        const uint8_t* sA = smem + (kt & 1) * STAGE_BYTES;
+        v8i xf[FM];
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          const int p = 32 * fm + r32;
+          const int sw = (p >> 1) & 3;
+          const v4i lo = *(const v4i*)(sA + p * 64 + (((2 * h) ^ sw) * 16));
+          const v4i hi = *(const v4i*)(sA + p * 64 + (((2 * h + 1) ^ sw) * 16));
+          xf[fm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+        }
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wr[d][fn], xf[fm], acc[fm][fn]);
+        if (kt + WDEPTH < nk) load_w(kt + WDEPTH, wr[d]);
+      }
+    }
+  }
+
+  // ---- epilogue ----
+  // MFMA row rho of block fn is column n0 + wave*TN + 32*fn + rho; lane (h, r32) slot
+  // i = 4*j + tt holds rho = 8*j + 4*h + tt.  After scaling and packing, lanes h and
+  // h+32 trade j-groups with permlane32_swap so that each lane owns 8 consecutive
+  // columns per (fn, pair of j) and stores 16 bytes.
+  const int64_t cw = n0 + (int64_t)wave * TN;
+  const float* wsg = a.ws + t.g * N;
+  float wsv[FN][4][4];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = cw + 32 * fn + 8 * j + 4 * h;
+      v4f w4 = {0.f, 0.f, 0.f, 0.f};
+      if (c < N) w4 = *(const v4f*)(wsg + c);
+      wsv[fn][j][0] = w4.x;
+      wsv[fn][j][1] = w4.y;
+      wsv[fn][j][2] = w4.z;
+      wsv[fn][j][3] = w4.w;
+    }
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int64_t m = t.row_base + 32 * fm + r32;
+    const bool write = m < t.row_end;
+    const bool zero = !write && m < t.zero_end;
+    const float xsv = write ? a.xs[m] : 0.f;
+    uint16_t* yrow = a.Y + m * N;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+      for (int jp = 0; jp < 2; ++jp) {          // j pairs (0,1) and (2,3)
+        uint32_t e[2][2];                         // [j parity][packed pair]
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+          const int j = 2 * jp + jj;
+#pragma unroll
+          for (int pr = 0; pr < 2; ++pr) {
+            const float v0 = (acc[fm][fn][4 * j + 2 * pr] * xsv) * wsv[fn][j][2 * pr];
+            const float v1 = (acc[fm][fn][4 * j + 2 * pr + 1] * xsv) * wsv[fn][j][2 * pr + 1];
+            e[jj][pr] = pack_bf16x2(v0, v1);
+          }
+        }
+        // lanes < 32 keep j even and take the partner's j even; lanes >= 32 keep j odd
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(e[0][pr], e[1][pr], false, false);
+          e[0][pr] = sw[0];
+          e[1][pr] = sw[1];
+        }
+        const int64_t c = cw + 32 * fn + 16 * jp + 8 * h;
+        if (c < N) {
+          if (write)
+            *(v4i*)(yrow + c) = v4i{(int)e[0][0], (int)e[0][1], (int)e[1][0], (int)e[1][1]};
+          else if (zero)
+            *(v4i*)(yrow + c) = v4i{0, 0, 0, 0};
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Zero fill (K == 0): a plain kernel rather than a memset, so the call can be
 // captured into a graph without a memset node.
 // ---------------------------------------------------------------------------
@@ -386,12 +613,15 @@ __global__ void __launch_bounds__(256) zero_fill_kernel(v4i* __restrict__ y, int
 // Configuration table and launch dispatch
 // ---------------------------------------------------------------------------
 
-//                               BM   BN  WM WN stages preshuffled
+//                               BM   BN  WM WN stages preshuffled wdepth
 const KernelConfig kConfigs[] = {
-    /* 0 */ {256, 256, 2, 4, 2, 0},
-    /* 1 */ {128, 256, 2, 4, 2, 0},
-    /* 2 */ {64, 256, 1, 4, 2, 0},
-    /* 3 */ {32, 128, 1, 4, 2, 0},
+    /* 0 */ {256, 256, 2, 4, 2, 0, 0},
+    /* 1 */ {128, 256, 2, 4, 2, 0, 0},
+    /* 2 */ {64, 256, 1, 4, 2, 0, 0},
+    /* 3 */ {32, 128, 1, 4, 2, 0, 0},
+    /* 4 */ {128, 256, 1, 4, 2, 1, 2},
+    /* 5 */ {64, 256, 1, 4, 2, 1, 4},
+    /* 6 */ {32, 128, 1, 4, 2, 1, 4},
 };
 const int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -405,6 +635,12 @@ static hipError_t launch_lds(bool k_tail, const GemmArgs& a, int64_t grid, hipSt
   return hipGetLastError();
 }
 
+template <int LAYOUT, int BM, int BN, int WN, int WDEPTH>
+static hipError_t launch_pre(const GemmArgs& a, int64_t grid, hipStream_t s) {
+  hipLaunchKernelGGL((gg_pre_kernel<LAYOUT, BM, BN, WN, WDEPTH>), dim3((uint32_t)grid), dim3(WN * 64), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int LAYOUT>
 static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
   switch (config_id) {
@@ -412,6 +648,9 @@ static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, i
     case 1: return launch_lds<LAYOUT, 128, 256, 2, 4, 2>(k_tail, a, grid, s);
     case 2: return launch_lds<LAYOUT, 64, 256, 1, 4, 2>(k_tail, a, grid, s);
     case 3: return launch_lds<LAYOUT, 32, 128, 1, 4, 2>(k_tail, a, grid, s);
+    case 4: return launch_pre<LAYOUT, 128, 256, 4, 2>(a, grid, s);
+    case 5: return launch_pre<LAYOUT, 64, 256, 4, 4>(a, grid, s);
+    case 6: return launch_pre<LAYOUT, 32, 128, 4, 4>(a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -431,8 +670,13 @@ hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_shuffle_b(const uint8_t*, uint8_t*, int64_t, int64_t, int64_t, hipStream_t) {
-  return hipErrorNotSupported;
+hipError_t launch_shuffle_b(const uint8_t* W, uint8_t* Ws, int64_t G, int64_t N, int64_t K, hipStream_t s) {
+  const int64_t chunks = G * N * K / 16;
+  if (chunks == 0) return hipSuccess;
+  int64_t blocks = (chunks + 255) / 256;
+  blocks = blocks > 8192 ? 8192 : blocks;
+  hipLaunchKernelGGL(shuffle_b_kernel, dim3((uint32_t)blocks), dim3(256), 0, s, (const v4i*)W, (v4i*)Ws, G, N, K);
+  return hipGetLastError();
 }
 
 }  // namespace fp8gg

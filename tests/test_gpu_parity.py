@@ -241,3 +241,64 @@ def test_refusals_raise(F):
         out = torch.empty((3, 48), dtype=torch.bfloat16, device="cuda")[:, :24]
         F.f8f8bf16_rowwise_grouped_stacked(P.dev(w.XQ), P.dev(w.WQ), P.dev(w.x_scale), P.dev(w.w_scale),
                                            P.dev(w.M_sizes), out=out)
+
+
+# ---------------------------------------------------------------------------
+# pre-shuffled weights
+# ---------------------------------------------------------------------------
+
+def shuffle_reference(WQ: np.ndarray) -> np.ndarray:
+    """The pre-shuffled byte order stated in include/fp8gg.h, written with numpy:
+    block (g, nb, kb) of 2048 bytes holds, at 32*l, W[g, 32nb + l%32, 64kb + 32(l/32) .. +32)."""
+    G, N, K = WQ.shape
+    v = WQ.reshape(G, N // 32, 32, K // 64, 2, 32)          # g, nb, r, kb, half, byte
+    v = v.transpose(0, 1, 3, 4, 2, 5)                        # g, nb, kb, half, r, byte  (lane = half*32 + r)
+    return np.ascontiguousarray(v).reshape(G, N, K)
+
+
+def test_shuffle_layout(F):
+    rng = np.random.default_rng(1000)
+    W = rng.integers(0, 256, (3, 96, 192)).astype(np.uint8)
+    got = F.f8f8bf16_shuffle_b(P.dev(W)).cpu().numpy()
+    assert np.array_equal(got, shuffle_reference(W))
+
+
+PRE_CASES = [
+    # (layout, sizes or zsi, expected_m, N, K)
+    ("stacked", [0, 1, 31, 32, 33], None, 128, 64),
+    ("stacked", [63, 64, 65, 0, 129], None, 288, 192),
+    ("stacked", [300, 0, 77], None, 544, 1024),
+    ("padded", [0, 5, 64, 100], 100, 256, 128),
+    ("padded", [300, 0, 299, 257], 300, 96, 320),
+]
+
+
+@pytest.mark.parametrize("cfg", [None, 4, 5, 6])
+@pytest.mark.parametrize("case", range(len(PRE_CASES)))
+def test_preshuffled_matches_oracle_and_plain(F, config_env, cfg, case):
+    layout, meta, em, N, K = PRE_CASES[case]
+    print(f"case preshuffle cfg={cfg} {layout} {meta} em={em} N={N} K={K}", flush=True)
+    if layout == "stacked":
+        w = wl.make_stacked(meta, N, K, seed=1100 + case)
+        config_env(None)
+        plain = run_stacked(F, w)
+        config_env(cfg)
+        got = run_stacked(F, w, pre=True)
+        P.assert_rows_match(got, oracle_stacked(w), label=f"pre cfg{cfg} case{case}")
+    else:
+        w = wl.make_dynamic(meta, em, N, K, seed=1100 + case)
+        config_env(None)
+        plain = run_dynamic(F, w)
+        config_env(cfg)
+        got = run_dynamic(F, w, pre=True)
+        P.assert_rows_match(got, oracle_dynamic(w), label=f"pre cfg{cfg} case{case}")
+    assert np.array_equal(got, plain), "pre-shuffled and plain paths differ bitwise"
+
+
+def test_preshuffled_refuses_partial_blocks(F):
+    w = wl.make_stacked([4], 40, 64, seed=1200)
+    with pytest.raises(ValueError):
+        F.f8f8bf16_shuffle_b(P.dev(w.WQ))
+    with pytest.raises(ValueError):
+        F.f8f8bf16_rowwise_grouped_stacked_preshuffle(P.dev(w.XQ), P.dev(w.WQ), P.dev(w.x_scale),
+                                                      P.dev(w.w_scale), P.dev(w.M_sizes))
