@@ -80,8 +80,9 @@ fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int6
   return FP8GG_OK;
 }
 
-// Fixed selector.  The key is the rows one group contributes on average (total_M
-// is normalised by G for the stacked layout), as a tile only ever sees one group.
+// Fixed selector (measured on MI355X; no benchmarking inside a call).  The key is
+// the rows one group contributes on average -- total_M normalised by G for the
+// stacked layout -- because a tile only ever sees one group.
 int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
   (void)K;
   (void)N;
@@ -91,8 +92,8 @@ int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, 
     if (per_group >= 48) return 5;
     return 6;
   }
-  if (per_group >= 256) return 0;
-  if (per_group >= 128) return 1;
+  if (per_group >= 512) return 7;   // 256x256, K stage 128
+  if (per_group >= 128) return 9;   // 128x256, K stage 128
   if (per_group >= 48) return 2;
   return 3;
 }
@@ -116,7 +117,7 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "no kernel configuration for this call (preshuffled=%d)", preshuffled);
   const int forced = env_int("FP8GG_CONFIG", -1);
   if (forced >= 0) {
-    if (forced >= fp8gg::kNumConfigs || fp8gg::kConfigs[forced].preshuffled != (preshuffled ? 1 : 0))
+    if (forced >= fp8gg::kNumConfigs || fp8gg::is_preshuffled(fp8gg::kConfigs[forced]) != (preshuffled != 0))
       return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_CONFIG=%d does not name a usable configuration", forced);
     cfg = forced;
   }
@@ -124,10 +125,10 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
   p->config_id = cfg;
   p->BM = c.BM;
   p->BN = c.BN;
-  p->BK = fp8gg::kBK;
+  p->BK = c.BK;
   p->threads = c.WM * c.WN * 64;
   p->stages = c.stages;
-  p->k_tail = (K % fp8gg::kBK) != 0;
+  p->k_tail = (K % c.BK) != 0;
   p->n_tail = (N % c.BN) != 0;
   p->n_tiles = (N + c.BN - 1) / c.BN;
   if (layout == FP8GG_LAYOUT_STACKED) {

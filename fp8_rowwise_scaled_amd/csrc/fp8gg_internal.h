@@ -28,19 +28,22 @@ struct GemmArgs {
 struct KernelConfig {
   int BM;       // rows of X per workgroup
   int BN;       // columns of Y (rows of W) per workgroup
+  int BK;       // K bytes per pipeline stage (64 or 128: one or two 32x32x64 MFMA steps)
   int WM, WN;   // waves along M and N (threads = 64 * WM * WN)
   int stages;   // LDS pipeline depth (X and W; X only when W is pre-shuffled)
-  int preshuffled;  // 1: W is read from the pre-shuffled layout straight into registers
+  int kind;     // 0: X and W through LDS; 1: same, software-pipelined; 2: pre-shuffled W
   int wdepth;   // pre-shuffled: K steps of W fragments held in flight in registers
 };
 
-constexpr int kBK = 64;          // K bytes per pipeline stage (one 32x32x64 fp8 MFMA)
+enum { kKindLds = 0, kKindLdsPipelined = 1, kKindPreshuffled = 2 };
 
 extern const KernelConfig kConfigs[];
 extern const int kNumConfigs;
 
+inline bool is_preshuffled(const KernelConfig& c) { return c.kind == kKindPreshuffled; }
+
 inline int lds_bytes(const KernelConfig& c) {
-  return c.preshuffled ? c.stages * c.BM * kBK : c.stages * (c.BM + c.BN) * kBK;
+  return is_preshuffled(c) ? 2 * c.BM * c.BK : c.stages * (c.BM + c.BN) * c.BK;
 }
 
 hipError_t launch_gemm(int layout, int config_id, bool k_tail, const GemmArgs& args,

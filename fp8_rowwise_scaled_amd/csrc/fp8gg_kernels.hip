@@ -23,9 +23,9 @@
 //     of one row and the epilogue stores 16-byte vectors.
 //   * A and B tiles of 64 K-bytes are copied global -> LDS with
 //     global_load_lds_dwordx4 (no staging registers), several stages deep.
-//   * LDS rows are 64 bytes (four 16-byte chunks); chunk c of row p is stored at
-//     c ^ ((p >> 1) & 3), which makes the MFMA operand reads (32 lanes reading 32
-//     consecutive rows at one logical chunk) bank-conflict free.
+//   * LDS rows are 64 bytes (four 16-byte chunks), XOR-swizzled per row (lds_swz)
+//     so that the MFMA operand reads (consecutive rows at one logical chunk) are
+//     bank-conflict free.
 //   * W rows are placed in LDS in "MFMA order": LDS row 32*fn + rho of a wave's
 //     slice holds the output column that MFMA row rho of block fn produces in the
 //     chosen lane -> column map, so the loads do the permutation for free.
@@ -81,9 +81,24 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
     case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
     case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
     case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
+    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
+    case 15: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
+    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
+    case 18: __builtin_amdgcn_s_waitcnt(0x4F72); break;
+    case 20: __builtin_amdgcn_s_waitcnt(0x4F74); break;
+    case 24: __builtin_amdgcn_s_waitcnt(0x4F78); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // anything else: wait for all
   }
 }
+
+// LDS rows are BK bytes (BK/16 chunks of 16 bytes); chunk c of row p is stored at
+// chunk c ^ lds_swz<BK>(p).  gfx950 serves a ds_read_b128 sixteen lanes (256 bytes,
+// 64 banks) at a time, and rows p and p + 256/BK share banks, so XOR-ing with
+// (p / (256/BK)) mod (BK/16) spreads the 16 consecutive rows that 16 lanes read at
+// one logical chunk over all 16 bank groups.
+template <int BK>
+__device__ __forceinline__ int lds_swz(int p) { return (p / (256 / BK)) & (BK / 16 - 1); }
 
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
@@ -160,11 +175,12 @@ __device__ __forceinline__ void zero_rect(uint16_t* Y, int64_t N, int64_t r0, in
 // The grouped GEMM kernel (plain W, both operands staged through LDS)
 // ---------------------------------------------------------------------------
 
-template <int LAYOUT, int BM, int BN, int WM, int WN, int STAGES, bool KTAIL>
+template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PIPE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gg_lds_kernel(GemmArgs a) {
   constexpr int NT = WM * WN * 64;
-  constexpr int BK = kBK;
+  constexpr int CPR = BK / 16;          // 16-byte chunks per LDS row
+  constexpr int KS = BK / 64;           // MFMA K steps per stage
   constexpr int TM = BM / WM;           // wave tile along M (rows of X)
   constexpr int TN = BN / WN;           // wave tile along N (columns of Y)
   constexpr int FM = TM / 32;           // 32x32 MFMA blocks per wave along M
@@ -177,6 +193,7 @@ gg_lds_kernel(GemmArgs a) {
   constexpr int STAGE_BYTES = (BM + BN) * BK;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(A_CHUNKS % 64 == 0 && B_CHUNKS % 64 == 0, "tile rows must be a multiple of 16");
+  static_assert(BK == 64 || BK == 128, "BK is 64 or 128");
 
   __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
 
@@ -210,15 +227,15 @@ gg_lds_kernel(GemmArgs a) {
   }
 
   // ---- per-thread copy descriptors (global source at k = 0) ----
-  // Chunk q of a stage (16 bytes) lands at LDS byte 16*q: row p = q / 4, physical
-  // chunk q % 4, which holds logical chunk (q % 4) ^ ((p >> 1) & 3).
+  // Chunk q of a stage (16 bytes) lands at LDS byte 16*q: row p = q / CPR, physical
+  // chunk q % CPR, which holds logical chunk (q % CPR) ^ lds_swz<BK>(p).
   const uint8_t* a_src[A_LOADS];
   int a_kc[A_LOADS];
 #pragma unroll
   for (int i = 0; i < A_LOADS; ++i) {
     const int q = i * NT + tid;
-    const int p = (q >> 2) % BM;
-    const int c = (q & 3) ^ ((p >> 1) & 3);
+    const int p = (q / CPR) % BM;
+    const int c = (q % CPR) ^ lds_swz<BK>(p);
     int64_t row = t.row_base + p;
     row = row < t.row_end ? row : t.row_end - 1;   // rows past the group: any valid row, result dropped
     a_src[i] = a.X + row * K + c * 16;
@@ -230,8 +247,8 @@ gg_lds_kernel(GemmArgs a) {
 #pragma unroll
   for (int i = 0; i < B_LOADS; ++i) {
     const int q = i * NT + tid;
-    const int p = (q >> 2) % BN;
-    const int c = (q & 3) ^ ((p >> 1) & 3);
+    const int p = (q / CPR) % BN;
+    const int c = (q % CPR) ^ lds_swz<BK>(p);
     // MFMA order: LDS row p = wn_*TN + 32*fn + rho holds output column
     // wn_*TN + h*16*FN + 16*fn + 4*j + tt, rho = 8*j + 4*h + tt.
     const int wn_ = p / TN;
@@ -283,47 +300,96 @@ gg_lds_kernel(GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = v16f{0};
 
-  // Prologue: stages 0 .. STAGES-2 in flight.
-#pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s)
-    if (s < nk) issue(s);
-
   const int h = lane >> 5;
   const int r32 = lane & 31;
 
-  for (int kt = 0; kt < nk; ++kt) {
-    // Tile kt has landed once at most (tiles issued after it) loads of this thread
-    // are outstanding; then the barrier makes every thread's copies visible and
-    // frees the stage that the next issue overwrites.
-    const int ahead = nk - 1 - kt;
-    if (ahead >= STAGES - 2) wait_vmcnt_le((STAGES - 2) * loads_per_stage);
-    else wait_vmcnt_le(0);
-    block_barrier();
-    if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-
+  // MFMA operands of stage kt from LDS: for MFMA step ks of the stage, lane (h, r32)
+  // takes row r32 of each 32-row block, bytes [64*ks + 32h, +32) (logical chunks
+  // 4ks + 2h and 4ks + 2h + 1).
+  auto read_frags = [&](int kt, v8i (&xf)[KS][FM], v8i (&wf)[KS][FN]) {
     const uint8_t* sA = smem + (kt % STAGES) * STAGE_BYTES;
     const uint8_t* sB = sA + A_BYTES;
-    v8i xf[FM], wf[FN];
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const int p = wm * TM + 32 * fm + r32;
-      const int sw = (p >> 1) & 3;
-      const v4i lo = *(const v4i*)(sA + p * 64 + (((2 * h) ^ sw) * 16));
-      const v4i hi = *(const v4i*)(sA + p * 64 + (((2 * h + 1) ^ sw) * 16));
-      xf[fm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) {
+        const int p = wm * TM + 32 * fm + r32;
+        const int sw = lds_swz<BK>(p);
+        const v4i lo = *(const v4i*)(sA + p * BK + (((4 * ks + 2 * h) ^ sw) * 16));
+        const v4i hi = *(const v4i*)(sA + p * BK + (((4 * ks + 2 * h + 1) ^ sw) * 16));
+        xf[ks][fm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int p = wn * TN + 32 * fn + r32;
+        const int sw = lds_swz<BK>(p);
+        const v4i lo = *(const v4i*)(sB + p * BK + (((4 * ks + 2 * h) ^ sw) * 16));
+        const v4i hi = *(const v4i*)(sB + p * BK + (((4 * ks + 2 * h + 1) ^ sw) * 16));
+        wf[ks][fn] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      }
     }
+  };
+  auto mfmas = [&](const v8i (&xf)[KS][FM], const v8i (&wf)[KS][FN]) {
 #pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const int p = wn * TN + 32 * fn + r32;
-      const int sw = (p >> 1) & 3;
-      const v4i lo = *(const v4i*)(sB + p * 64 + (((2 * h) ^ sw) * 16));
-      const v4i hi = *(const v4i*)(sB + p * 64 + (((2 * h + 1) ^ sw) * 16));
-      wf[fn] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wf[ks][fn], xf[ks][fm], acc[fm][fn]);
+  };
+
+  if constexpr (!PIPE) {
+    // Prologue: stages 0 .. STAGES-2 in flight.
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (s < nk) issue(s);
+    for (int kt = 0; kt < nk; ++kt) {
+      // Tile kt has landed once at most (tiles issued after it) loads of this thread
+      // are outstanding; then the barrier makes every thread's copies visible and
+      // frees the stage that the next issue overwrites.
+      const int ahead = nk - 1 - kt;
+      if (ahead >= STAGES - 2) wait_vmcnt_le((STAGES - 2) * loads_per_stage);
+      else wait_vmcnt_le(0);
+      block_barrier();
+      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
+      v8i xf[KS][FM], wf[KS][FN];
+      read_frags(kt, xf, wf);
+      mfmas(xf, wf);
     }
+  } else {
+    // Software-pipelined loop: while the MFMAs of step s run on registers read
+    // during step s-1, the operands of step s+1 are read from LDS into the other
+    // register set and the copies of steps s+2 .. s+STAGES-1 are in flight.
+    // Prologue: copies of steps 0 .. STAGES-1 (every stage starts free).
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wf[fn], xf[fm], acc[fm][fn]);
+    for (int s = 0; s < STAGES; ++s)
+      if (s < nk) issue(s);
+    {
+      const int issued = nk < STAGES ? nk : STAGES;
+      wait_vmcnt_le((issued - 1) * loads_per_stage);
+    }
+    block_barrier();
+    v8i xa[KS][FM], wa[KS][FN], xb[KS][FM], wb[KS][FN];
+    read_frags(0, xa, wa);
+
+    auto step = [&](int s, const v8i (&xc)[KS][FM], const v8i (&wc)[KS][FN], v8i (&xn)[KS][FM],
+                    v8i (&wn_)[KS][FN]) {
+      // This wave's reads of step s are complete (the stage may be refilled after
+      // the barrier), and step s+1's copies have landed.
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
+      if (s + 1 < nk) {
+        const int issued_last = (s + STAGES - 1 < nk - 1) ? s + STAGES - 1 : nk - 1;
+        wait_vmcnt_le((issued_last - (s + 1)) * loads_per_stage);
+      }
+      block_barrier();
+      if (s + STAGES < nk) issue(s + STAGES);
+      if (s + 1 < nk) read_frags(s + 1, xn, wn_);
+      mfmas(xc, wc);
+    };
+    for (int s = 0; s < nk; s += 2) {
+      step(s, xa, wa, xb, wb);
+      if (s + 1 < nk) step(s + 1, xb, wb, xa, wa);
+    }
   }
 
   // ---- epilogue: y = bf16((acc * x_scale[m]) * w_scale[g, n]) ----
@@ -415,7 +481,7 @@ template <int LAYOUT, int BM, int BN, int WN, int WDEPTH>
 __global__ void __launch_bounds__(WN * 64)
 gg_pre_kernel(GemmArgs a) {
   constexpr int NT = WN * 64;
-  constexpr int BK = kBK;
+  constexpr int BK = 64;                // one MFMA K step per stage (the shuffle's K block)
   constexpr int TN = BN / WN;           // wave tile along N
   constexpr int FM = BM / 32;
   constexpr int FN = TN / 32;
@@ -457,7 +523,7 @@ gg_pre_kernel(GemmArgs a) {
   for (int i = 0; i < A_LOADS; ++i) {
     const int q = i * NT + tid;
     const int p = (q >> 2) % BM;
-    const int c = (q & 3) ^ ((p >> 1) & 3);
+    const int c = (q & 3) ^ lds_swz<64>(p);
     int64_t row = t.row_base + p;
     row = row < t.row_end ? row : t.row_end - 1;
     a_src[i] = a.X + row * K + c * 16;
@@ -524,7 +590,7 @@ gg_pre_kernel(GemmArgs a) {
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
           const int p = 32 * fm + r32;
-          const int sw = (p >> 1) & 3;
+          const int sw = lds_swz<64>(p);
           const v4i lo = *(const v4i*)(sA + p * 64 + (((2 * h) ^ sw) * 16));
           const v4i hi = *(const v4i*)(sA + p * 64 + (((2 * h + 1) ^ sw) * 16));
           xf[fm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
@@ -613,25 +679,36 @@ __global__ void __launch_bounds__(256) zero_fill_kernel(v4i* __restrict__ y, int
 // Configuration table and launch dispatch
 // ---------------------------------------------------------------------------
 
-//                               BM   BN  WM WN stages preshuffled wdepth
+// kind: 0 = both operands through LDS, 1 = same with the software-pipelined loop,
+//       2 = pre-shuffled W straight to registers (X through LDS).
+//                      BM   BN   BK  WM WN stages kind wdepth
 const KernelConfig kConfigs[] = {
-    /* 0 */ {256, 256, 2, 4, 2, 0, 0},
-    /* 1 */ {128, 256, 2, 4, 2, 0, 0},
-    /* 2 */ {64, 256, 1, 4, 2, 0, 0},
-    /* 3 */ {32, 128, 1, 4, 2, 0, 0},
-    /* 4 */ {128, 256, 1, 4, 2, 1, 2},
-    /* 5 */ {64, 256, 1, 4, 2, 1, 4},
-    /* 6 */ {32, 128, 1, 4, 2, 1, 4},
+    /* 0 */ {256, 256, 64, 2, 4, 4, 0, 0},
+    /* 1 */ {128, 256, 64, 2, 4, 4, 0, 0},
+    /* 2 */ {64, 256, 64, 1, 4, 2, 0, 0},
+    /* 3 */ {32, 128, 64, 1, 4, 2, 0, 0},
+    /* 4 */ {128, 256, 64, 1, 4, 2, 2, 2},
+    /* 5 */ {64, 256, 64, 1, 4, 2, 2, 4},
+    /* 6 */ {32, 128, 64, 1, 4, 2, 2, 4},
+    /* 7 */ {256, 256, 128, 2, 4, 2, 0, 0},
+    /* 8 */ {256, 128, 128, 2, 4, 3, 0, 0},
+    /* 9 */ {128, 256, 128, 2, 4, 3, 0, 0},
+    /* 10 */ {128, 128, 128, 2, 2, 4, 0, 0},
+    /* 11 */ {256, 256, 64, 2, 4, 4, 1, 0},
+    /* 12 */ {256, 128, 128, 2, 2, 3, 0, 0},
+    /* 13 */ {128, 128, 64, 2, 2, 4, 0, 0},
 };
 const int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-template <int LAYOUT, int BM, int BN, int WM, int WN, int STAGES>
+template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool PIPE = false>
 static hipError_t launch_lds(bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
   const dim3 block(WM * WN * 64);
   if (k_tail)
-    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, WM, WN, STAGES, true>), dim3((uint32_t)grid), block, 0, s, a);
+    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, true, PIPE>), dim3((uint32_t)grid), block,
+                       0, s, a);
   else
-    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, WM, WN, STAGES, false>), dim3((uint32_t)grid), block, 0, s, a);
+    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, false, PIPE>), dim3((uint32_t)grid), block,
+                       0, s, a);
   return hipGetLastError();
 }
 
@@ -641,16 +718,24 @@ static hipError_t launch_pre(const GemmArgs& a, int64_t grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+// One case per row of kConfigs (same order).
 template <int LAYOUT>
 static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
   switch (config_id) {
-    case 0: return launch_lds<LAYOUT, 256, 256, 2, 4, 2>(k_tail, a, grid, s);
-    case 1: return launch_lds<LAYOUT, 128, 256, 2, 4, 2>(k_tail, a, grid, s);
-    case 2: return launch_lds<LAYOUT, 64, 256, 1, 4, 2>(k_tail, a, grid, s);
-    case 3: return launch_lds<LAYOUT, 32, 128, 1, 4, 2>(k_tail, a, grid, s);
+    case 0: return launch_lds<LAYOUT, 256, 256, 64, 2, 4, 4>(k_tail, a, grid, s);
+    case 1: return launch_lds<LAYOUT, 128, 256, 64, 2, 4, 4>(k_tail, a, grid, s);
+    case 2: return launch_lds<LAYOUT, 64, 256, 64, 1, 4, 2>(k_tail, a, grid, s);
+    case 3: return launch_lds<LAYOUT, 32, 128, 64, 1, 4, 2>(k_tail, a, grid, s);
     case 4: return launch_pre<LAYOUT, 128, 256, 4, 2>(a, grid, s);
     case 5: return launch_pre<LAYOUT, 64, 256, 4, 4>(a, grid, s);
     case 6: return launch_pre<LAYOUT, 32, 128, 4, 4>(a, grid, s);
+    case 7: return launch_lds<LAYOUT, 256, 256, 128, 2, 4, 2>(k_tail, a, grid, s);
+    case 8: return launch_lds<LAYOUT, 256, 128, 128, 2, 4, 3>(k_tail, a, grid, s);
+    case 9: return launch_lds<LAYOUT, 128, 256, 128, 2, 4, 3>(k_tail, a, grid, s);
+    case 10: return launch_lds<LAYOUT, 128, 128, 128, 2, 2, 4>(k_tail, a, grid, s);
+    case 11: return launch_lds<LAYOUT, 256, 256, 64, 2, 4, 4, true>(k_tail, a, grid, s);
+    case 12: return launch_lds<LAYOUT, 256, 128, 128, 2, 2, 3>(k_tail, a, grid, s);
+    case 13: return launch_lds<LAYOUT, 128, 128, 64, 2, 2, 4>(k_tail, a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -25,6 +25,33 @@ def F():
     return F
 
 
+def _configs(preshuffled: bool):
+    """Ids of the compiled kernel configurations of one kind (plain or pre-shuffled),
+    found by asking the host planner which ones it accepts."""
+    import fp8_rowwise_scaled_amd as F
+    from fp8_rowwise_scaled_amd import _lib
+    ids = []
+    old = os.environ.get("FP8GG_CONFIG")
+    try:
+        for c in range(_lib.load().f8f8bf16_num_configs()):
+            os.environ["FP8GG_CONFIG"] = str(c)
+            try:
+                F.plan(F.LAYOUT_STACKED, preshuffled, 2, 64, 64, 128)
+                ids.append(c)
+            except ValueError:
+                pass
+    finally:
+        if old is None:
+            os.environ.pop("FP8GG_CONFIG", None)
+        else:
+            os.environ["FP8GG_CONFIG"] = old
+    return ids
+
+
+PLAIN_CONFIGS = _configs(False)
+PRE_CONFIGS = _configs(True)
+
+
 @pytest.fixture
 def config_env():
     """Forces a kernel configuration for the duration of a test."""
@@ -98,7 +125,7 @@ STACKED_EDGES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", range(4))
+@pytest.mark.parametrize("cfg", PLAIN_CONFIGS)
 @pytest.mark.parametrize("case", range(len(STACKED_EDGES)))
 def test_stacked_edges_every_config(F, config_env, cfg, case):
     sizes, N, K, total_M = STACKED_EDGES[case]
@@ -117,7 +144,7 @@ PADDED_EDGES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", range(4))
+@pytest.mark.parametrize("cfg", PLAIN_CONFIGS)
 @pytest.mark.parametrize("case", range(len(PADDED_EDGES)))
 @pytest.mark.parametrize("zeroing", [True, False])
 def test_padded_edges_every_config(F, config_env, cfg, case, zeroing):
@@ -131,7 +158,7 @@ def test_padded_edges_every_config(F, config_env, cfg, case, zeroing):
 def test_overread_single_signed_neighbours(F, config_env):
     """Alternate groups get constant single-signed data, so any read past a group's
     rows, a row's K end or the N end accumulates coherently and shows."""
-    for cfg in range(4):
+    for cfg in PLAIN_CONFIGS:
         config_env(cfg)
         sizes = [37, 70, 5, 129, 0, 64]
         N, K = 264, 208
@@ -149,7 +176,7 @@ def test_overread_single_signed_neighbours(F, config_env):
 def test_poisoned_unread_regions(F, config_env):
     """NaN codes and NaN scales where nothing may be read: rows past sum(M_sizes),
     empty groups' weights, padding rows and their x_scale."""
-    for cfg in range(4):
+    for cfg in PLAIN_CONFIGS:
         config_env(cfg)
         sizes = [40, 0, 77]
         w = wl.make_stacked(sizes, 136, 144, seed=400 + cfg, total_M=150)
@@ -273,7 +300,7 @@ PRE_CASES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [None, 4, 5, 6])
+@pytest.mark.parametrize("cfg", [None] + PRE_CONFIGS)
 @pytest.mark.parametrize("case", range(len(PRE_CASES)))
 def test_preshuffled_matches_oracle_and_plain(F, config_env, cfg, case):
     layout, meta, em, N, K = PRE_CASES[case]
