@@ -95,6 +95,10 @@ int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, 
   if (per_group >= 512) return 7;   // 256x256, K stage 128
   if (per_group >= 128) return 9;   // 128x256, K stage 128
   if (per_group >= 48) return 2;
+  // At most one row per group on average: few groups hold rows, so spread each
+  // group's weights over many workgroups (32 columns each, K split over 4 waves).
+  const int64_t rows = layout == FP8GG_LAYOUT_STACKED ? M : G * M;
+  if (rows <= G) return 16;
   return 3;
 }
 

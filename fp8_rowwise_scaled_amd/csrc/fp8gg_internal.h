@@ -31,11 +31,12 @@ struct KernelConfig {
   int BK;       // K bytes per pipeline stage (64 or 128: one or two 32x32x64 MFMA steps)
   int WM, WN;   // waves along M and N (threads = 64 * WM * WN)
   int stages;   // LDS pipeline depth (X and W; X only when W is pre-shuffled)
-  int kind;     // 0: X and W through LDS; 1: same, software-pipelined; 2: pre-shuffled W
-  int wdepth;   // pre-shuffled: K steps of W fragments held in flight in registers
+  int kind;     // 0: X and W through LDS; 1: same, software-pipelined; 2: pre-shuffled W;
+                // 3: small M, W and X straight to registers with K split across waves
+  int wdepth;   // kinds 2, 3: K steps of fragments held in flight in registers
 };
 
-enum { kKindLds = 0, kKindLdsPipelined = 1, kKindPreshuffled = 2 };
+enum { kKindLds = 0, kKindLdsPipelined = 1, kKindPreshuffled = 2, kKindSkinny = 3 };
 
 extern const KernelConfig kConfigs[];
 extern const int kNumConfigs;
@@ -43,6 +44,7 @@ extern const int kNumConfigs;
 inline bool is_preshuffled(const KernelConfig& c) { return c.kind == kKindPreshuffled; }
 
 inline int lds_bytes(const KernelConfig& c) {
+  if (c.kind == kKindSkinny) return 3 * (c.BM / 32) * 16 * 64 * 4;
   return is_preshuffled(c) ? 2 * c.BM * c.BK : c.stages * (c.BM + c.BN) * c.BK;
 }
 

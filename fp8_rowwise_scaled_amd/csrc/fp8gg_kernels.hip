@@ -119,24 +119,32 @@ struct Tile {
 
 // Stacked: walk the groups with a running row prefix and tile prefix.  Counts are
 // clamped (negative -> 0, cumulative end -> M), so any metadata stays in bounds.
+// The counts are fetched eight at a time so that a call pays one memory round trip
+// per eight groups rather than one per group before its first operand load.
 template <int BM>
 __device__ __forceinline__ bool resolve_stacked(const GemmArgs& a, int64_t m_tile, Tile& t) {
   int64_t start = 0, tiles_before = 0;
-  for (int64_t g = 0; g < a.G; ++g) {
-    int64_t s = a.meta[g];
-    s = s < 0 ? 0 : s;
-    int64_t end = start + s;
-    end = end > a.M ? a.M : end;
-    const int64_t tiles = (end - start + BM - 1) / BM;
-    if (m_tile < tiles_before + tiles) {
-      t.g = g;
-      t.row_base = start + (m_tile - tiles_before) * BM;
-      t.row_end = end;
-      t.zero_end = end;
-      return true;
+  for (int64_t g0 = 0; g0 < a.G; g0 += 8) {
+    int64_t cnt[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt[i] = a.meta[g0 + i < a.G ? g0 + i : a.G - 1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (g0 + i >= a.G) break;
+      int64_t s = cnt[i] < 0 ? 0 : cnt[i];
+      int64_t end = start + s;
+      end = end > a.M ? a.M : end;
+      const int64_t tiles = (end - start + BM - 1) / BM;
+      if (m_tile < tiles_before + tiles) {
+        t.g = g0 + i;
+        t.row_base = start + (m_tile - tiles_before) * BM;
+        t.row_end = end;
+        t.zero_end = end;
+        return true;
+      }
+      tiles_before += tiles;
+      start = end;
     }
-    tiles_before += tiles;
-    start = end;
   }
   return false;
 }
@@ -666,6 +674,186 @@ gg_pre_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Small per-group M: stream W straight into registers, split K across waves
+// ---------------------------------------------------------------------------
+//
+// For a few rows per group the call is bound by reading W once from HBM, so the
+// work is spread over many workgroups: one per (group, 32 output columns, BM rows
+// of X), with the four waves of a workgroup splitting K.  Each wave keeps D MFMA
+// steps of W and X fragments in flight in a register ring (W rows are read in the
+// MFMA A-operand layout directly from the row-major weights; X rows come from L2).
+// The four partial sums are added through LDS in a fixed order (deterministic),
+// then the epilogue is the pre-shuffled kernel's (permlane32_swap, 16-byte stores).
+
+template <int LAYOUT, int BM, int D, bool KTAIL>
+__global__ void __launch_bounds__(256)
+gg_skinny_kernel(GemmArgs a) {
+  constexpr int FM = BM / 32;
+  constexpr int WAVES = 4;
+  static_assert(BM % 32 == 0, "BM must be a multiple of 32");
+
+  __shared__ __attribute__((aligned(16))) float red[(WAVES - 1) * FM * 16 * 64];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  const int64_t bid = blockIdx.x;
+  const int64_t n_tile = bid % a.n_tiles;
+  const int64_t rest = bid / a.n_tiles;
+  Tile t;
+  if (LAYOUT == kStacked) {
+    if (!resolve_stacked<BM>(a, rest, t)) return;
+  } else {
+    if (!resolve_padded<BM>(a, rest / a.m_tiles, rest % a.m_tiles, t)) return;
+  }
+  const int64_t N = a.N;
+  const int64_t K = a.K;
+  const int64_t n0 = n_tile * 32;
+  const int64_t tile_row_end = t.row_base + BM;
+  if (t.row_base >= t.row_end) {
+    const int64_t r1 = tile_row_end < t.zero_end ? tile_row_end : t.zero_end;
+    const int64_t c1 = n0 + 32 < N ? n0 + 32 : N;
+    zero_rect<256>(a.Y, N, t.row_base, r1, n0, c1);
+    return;
+  }
+
+  const int h = lane >> 5;
+  const int r32 = lane & 31;
+
+  // The epilogue's scales are fetched now so that their latency hides under the K loop.
+  const float* wsg = a.ws + t.g * N;
+  float wsv[4][4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t c = n0 + 8 * j + 4 * h;
+    v4f w4 = {0.f, 0.f, 0.f, 0.f};
+    if (c < N) w4 = *(const v4f*)(wsg + c);
+    wsv[j][0] = w4.x;
+    wsv[j][1] = w4.y;
+    wsv[j][2] = w4.z;
+    wsv[j][3] = w4.w;
+  }
+  float xsv[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int64_t m = t.row_base + 32 * fm + r32;
+    xsv[fm] = m < t.row_end ? a.xs[m] : 0.f;
+  }
+
+  int64_t wrow = n0 + r32;
+  wrow = wrow < N ? wrow : N - 1;                         // columns past N: result dropped
+  const uint8_t* wsrc = a.W + (t.g * N + wrow) * K + 32 * h;
+  const uint8_t* xsrc[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    int64_t row = t.row_base + 32 * fm + r32;
+    row = row < t.row_end ? row : t.row_end - 1;          // rows past the group: result dropped
+    xsrc[fm] = a.X + row * K + 32 * h;
+  }
+
+  const int nk = (int)((K + 63) / 64);
+  const int per = (nk + WAVES - 1) / WAVES;
+  const int kb = wave * per;
+  const int ke = kb + per < nk ? kb + per : nk;
+
+  // 32 bytes of one row at K step kt (two 16-byte chunks; chunks at or past K read 0).
+  auto load32 = [&](const uint8_t* src, int kt) -> v8i {
+    const int64_t ko = (int64_t)kt * 64;
+    const v4i* p0 = (const v4i*)(src + ko);
+    v4i lo, hi;
+    if (!KTAIL || ko + 64 <= K) {
+      lo = p0[0];
+      hi = p0[1];
+    } else {
+      const v4i z = {0, 0, 0, 0};
+      lo = (ko + 32 * h < K) ? p0[0] : z;
+      hi = (ko + 32 * h + 16 < K) ? p0[1] : z;
+    }
+    return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+  };
+
+  v16f acc[FM];
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) acc[fm] = v16f{0};
+  v8i wr[D], xr[D][FM];
+#pragma unroll
+  for (int d = 0; d < D; ++d)
+    if (kb + d < ke) {
+      wr[d] = load32(wsrc, kb + d);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm) xr[d][fm] = load32(xsrc[fm], kb + d);
+    }
+  for (int kt0 = kb; kt0 < ke; kt0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const int kt = kt0 + d;
+      if (kt < ke) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) acc[fm] = mfma_32x32x64_fp8(wr[d], xr[d][fm], acc[fm]);
+        if (kt + D < ke) {
+          wr[d] = load32(wsrc, kt + D);
+#pragma unroll
+          for (int fm = 0; fm < FM; ++fm) xr[d][fm] = load32(xsrc[fm], kt + D);
+        }
+      }
+    }
+  }
+
+  // Partial sums of waves 1..3 -> LDS; wave 0 adds them in wave order.
+  if (wave > 0) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) red[(((wave - 1) * FM + fm) * 16 + i) * 64 + lane] = acc[fm][i];
+  }
+  __syncthreads();
+  if (wave != 0) return;
+#pragma unroll
+  for (int w = 1; w < WAVES; ++w)
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[fm][i] += red[(((w - 1) * FM + fm) * 16 + i) * 64 + lane];
+
+  // Epilogue: MFMA row rho = 8*j + 4*h + tt of the block is column n0 + rho.
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    const int64_t m = t.row_base + 32 * fm + r32;
+    const bool write = m < t.row_end;
+    const bool zero = !write && m < t.zero_end;
+    uint16_t* yrow = a.Y + m * N;
+#pragma unroll
+    for (int jp = 0; jp < 2; ++jp) {
+      uint32_t e[2][2];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int j = 2 * jp + jj;
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+          const float v0 = (acc[fm][4 * j + 2 * pr] * xsv[fm]) * wsv[j][2 * pr];
+          const float v1 = (acc[fm][4 * j + 2 * pr + 1] * xsv[fm]) * wsv[j][2 * pr + 1];
+          e[jj][pr] = pack_bf16x2(v0, v1);
+        }
+      }
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(e[0][pr], e[1][pr], false, false);
+        e[0][pr] = sw[0];
+        e[1][pr] = sw[1];
+      }
+      const int64_t c = n0 + 16 * jp + 8 * h;
+      if (c < N) {
+        if (write)
+          *(v4i*)(yrow + c) = v4i{(int)e[0][0], (int)e[0][1], (int)e[1][0], (int)e[1][1]};
+        else if (zero)
+          *(v4i*)(yrow + c) = v4i{0, 0, 0, 0};
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Zero fill (K == 0): a plain kernel rather than a memset, so the call can be
 // captured into a graph without a memset node.
 // ---------------------------------------------------------------------------
@@ -680,7 +868,8 @@ __global__ void __launch_bounds__(256) zero_fill_kernel(v4i* __restrict__ y, int
 // ---------------------------------------------------------------------------
 
 // kind: 0 = both operands through LDS, 1 = same with the software-pipelined loop,
-//       2 = pre-shuffled W straight to registers (X through LDS).
+//       2 = pre-shuffled W straight to registers (X through LDS),
+//       3 = small M: W and X straight to registers, K split across the 4 waves.
 //                      BM   BN   BK  WM WN stages kind wdepth
 const KernelConfig kConfigs[] = {
     /* 0 */ {256, 256, 64, 2, 4, 4, 0, 0},
@@ -697,6 +886,9 @@ const KernelConfig kConfigs[] = {
     /* 11 */ {256, 256, 64, 2, 4, 4, 1, 0},
     /* 12 */ {256, 128, 128, 2, 2, 3, 0, 0},
     /* 13 */ {128, 128, 64, 2, 2, 4, 0, 0},
+    /* 14 */ {32, 32, 64, 1, 4, 0, 3, 8},
+    /* 15 */ {64, 32, 64, 1, 4, 0, 3, 8},
+    /* 16 */ {32, 32, 64, 1, 4, 0, 3, 4},
 };
 const int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -718,6 +910,15 @@ static hipError_t launch_pre(const GemmArgs& a, int64_t grid, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int LAYOUT, int BM, int D>
+static hipError_t launch_skinny(bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
+  if (k_tail)
+    hipLaunchKernelGGL((gg_skinny_kernel<LAYOUT, BM, D, true>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((gg_skinny_kernel<LAYOUT, BM, D, false>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 // One case per row of kConfigs (same order).
 template <int LAYOUT>
 static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
@@ -736,6 +937,9 @@ static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, i
     case 11: return launch_lds<LAYOUT, 256, 256, 64, 2, 4, 4, true>(k_tail, a, grid, s);
     case 12: return launch_lds<LAYOUT, 256, 128, 128, 2, 2, 3>(k_tail, a, grid, s);
     case 13: return launch_lds<LAYOUT, 128, 128, 64, 2, 2, 4>(k_tail, a, grid, s);
+    case 14: return launch_skinny<LAYOUT, 32, 8>(k_tail, a, grid, s);
+    case 15: return launch_skinny<LAYOUT, 64, 8>(k_tail, a, grid, s);
+    case 16: return launch_skinny<LAYOUT, 32, 4>(k_tail, a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -205,7 +205,11 @@ def test_deterministic(F):
     assert np.array_equal(a, b)
 
 
-def test_dynamic_equals_stacked_on_compacted_rows_bitwise(F):
+@pytest.mark.parametrize("cfg", PLAIN_CONFIGS)
+def test_dynamic_equals_stacked_on_compacted_rows_bitwise(F, config_env, cfg):
+    """Same kernel configuration on both sides: the padded call's valid rows equal the
+    stacked call on the compacted rows, bit for bit."""
+    config_env(cfg)
     d = wl.make_dynamic([17, 0, 256, 100], 256, 264, 208, seed=600)
     yd = run_dynamic(F, d).reshape(d.G, d.expected_m, d.N)
     z = d.zero_start_index_M
@@ -215,10 +219,14 @@ def test_dynamic_equals_stacked_on_compacted_rows_bitwise(F):
     assert np.array_equal(np.concatenate([yd[g, :z[g]] for g in range(d.G)]), ys)
 
 
-def test_k_tail_equals_zero_padded_k_bitwise(F):
+@pytest.mark.parametrize("cfg", PLAIN_CONFIGS)
+def test_k_tail_equals_zero_padded_k_bitwise(F, config_env, cfg):
+    """Same configuration: a K that stops mid-tile equals the same data zero-padded to
+    a whole number of tiles, bit for bit."""
+    config_env(cfg)
     w = wl.make_stacked([50, 130], 264, 144, seed=700)
     a = run_stacked(F, w)
-    pad = 192 - 144
+    pad = 256 - 144
     w2 = wl.Stacked(np.concatenate([w.XQ, np.zeros((w.total_M, pad), np.uint8)], 1),
                     np.concatenate([w.WQ, np.zeros((w.G, w.N, pad), np.uint8)], 2),
                     w.x_scale, w.w_scale, w.M_sizes)
@@ -303,18 +311,20 @@ PRE_CASES = [
 @pytest.mark.parametrize("cfg", [None] + PRE_CONFIGS)
 @pytest.mark.parametrize("case", range(len(PRE_CASES)))
 def test_preshuffled_matches_oracle_and_plain(F, config_env, cfg, case):
+    """Pre-shuffled vs oracle, and bitwise vs the plain LDS kernel of the same K order
+    (configuration 0 accumulates the K steps in the same sequence)."""
     layout, meta, em, N, K = PRE_CASES[case]
     print(f"case preshuffle cfg={cfg} {layout} {meta} em={em} N={N} K={K}", flush=True)
     if layout == "stacked":
         w = wl.make_stacked(meta, N, K, seed=1100 + case)
-        config_env(None)
+        config_env(0)
         plain = run_stacked(F, w)
         config_env(cfg)
         got = run_stacked(F, w, pre=True)
         P.assert_rows_match(got, oracle_stacked(w), label=f"pre cfg{cfg} case{case}")
     else:
         w = wl.make_dynamic(meta, em, N, K, seed=1100 + case)
-        config_env(None)
+        config_env(0)
         plain = run_dynamic(F, w)
         config_env(cfg)
         got = run_dynamic(F, w, pre=True)
