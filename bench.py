@@ -128,6 +128,48 @@ def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=3):
                       "(e4m3fn table decode, fp64 matmul per group, fp64 scales, bf16 RNE)"}
 
 
+def small_m_us_per_call(F, torch, totals=(1, 8, 32), calls_per_graph=64, replays=20):
+    """µs per call of the down-proj workload at small total_M, timed as the pages time
+    decode-sized GEMMs: many calls captured in one HIP graph (rotating over enough
+    input copies to defeat the Infinity Cache), replayed, divided by the call count."""
+    import workloads as wl
+    out = {}
+    dev = torch.device("cuda", 0)
+    for m in totals:
+        w = wl.moe_down(m)
+        _, nbytes, _, _ = algorithmic_work(w, "stacked")
+        rot = max(1, min(64, math.ceil(2 * MALL_BYTES / max(nbytes, 1))))
+        base = [torch.from_numpy(a).to(dev) for a in (w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)]
+        sets = [base] + [[t.clone() for t in base] for _ in range(rot - 1)]
+        outs = [torch.empty((w.total_M, w.N), dtype=torch.bfloat16, device=dev) for _ in range(rot)]
+
+        def calls():
+            for i in range(calls_per_graph):
+                s_ = sets[i % rot]
+                F.f8f8bf16_rowwise_grouped_stacked(*s_, out=outs[i % rot])
+        calls()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            calls()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(replays):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / (replays * calls_per_graph)
+        out[f"moe_down_M{m}"] = {"us_per_call": round(us, 3), "GB_per_s": round(nbytes / us / 1e3, 1),
+                                 "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "input_copies": rot}
+        log(f"small M: {w.name}: {us:.2f} us/call under graph replay ({nbytes / us / 1e3:.0f} GB/s, "
+            f"{rot} input copies)")
+        del sets, outs, base, g
+    return out
+
+
 def copy_calibration(nbytes):
     """A plain device copy of known size, profiled beside the GEMM to scale the
     HBM byte counters."""
@@ -148,6 +190,7 @@ def main():
     ap.add_argument("--workload", default="moe_gate_up", choices=WORKLOADS)
     ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate over (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-small-m", action="store_true", help="skip the graph-replayed small-M timings")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of this many bytes (for counter calibration)")
     args = ap.parse_args()
@@ -223,10 +266,11 @@ def main():
     durs = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
     avg = sum(durs) / len(durs)
     med = statistics.median(durs)
+    region = starts[0].elapsed_time(ends[-1]) * 1e-3 / args.steps
     ms_per_step = wall / args.steps * 1e3
     value = flop / (wall / args.steps) / 1e12
     log(f"per call: wall {ms_per_step * 1e3:.2f} us, kernel avg {avg * 1e6:.2f} us, median {med * 1e6:.2f} us, "
-        f"min {min(durs) * 1e6:.2f} us")
+        f"min {min(durs) * 1e6:.2f} us, timed region / calls {region * 1e6:.2f} us")
 
     mfma_bound = flop / (PEAK_FP8_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9)
     src_hash = kernel_source_hash()
@@ -270,6 +314,8 @@ def main():
         },
         "roofline": roof,
     }
+    if not args.no_small_m and args.workload == "moe_gate_up":
+        result["small_m"] = small_m_us_per_call(F, torch)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(w, layout, flop)

@@ -339,3 +339,29 @@ def test_preshuffled_refuses_partial_blocks(F):
     with pytest.raises(ValueError):
         F.f8f8bf16_rowwise_grouped_stacked_preshuffle(P.dev(w.XQ), P.dev(w.WQ), P.dev(w.x_scale),
                                                       P.dev(w.w_scale), P.dev(w.M_sizes))
+
+
+def test_graph_replay_matches_eager(F):
+    """Calls captured into a HIP graph and replayed several times, with eager work and
+    synchronisation between replays, give the eager result every time."""
+    ws = [wl.make_stacked([3, 0, 40, 1], 264, 208, seed=1300), wl.make_stacked([1, 0, 0, 0], 7168 // 4, 512,
+                                                                                 seed=1301)]
+    eager, graphs = [], []
+    for w in ws:
+        args = [P.dev(a) for a in (w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)]
+        out = torch.empty((w.total_M, w.N), dtype=torch.bfloat16, device="cuda")
+        F.f8f8bf16_rowwise_grouped_stacked(*args, out=out)
+        torch.cuda.synchronize()
+        eager.append(P.bits_of(out).copy())
+        g = torch.cuda.CUDAGraph()
+        gout = torch.empty_like(out)
+        with torch.cuda.graph(g):
+            F.f8f8bf16_rowwise_grouped_stacked(*args, out=gout)
+        graphs.append((g, gout, args))
+    for rep in range(4):
+        for (g, gout, args), want in zip(graphs, eager):
+            gout.view(torch.int16).fill_(P.SENTINEL)     # eager work between replays
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert np.array_equal(P.bits_of(gout), want), f"replay {rep} differs from eager"
