@@ -13,7 +13,10 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <map>
+#include <mutex>
 #include <string>
+#include <utility>
 
 #include "fp8gg.h"
 #include "fp8gg_internal.h"
@@ -92,14 +95,77 @@ int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, 
     if (per_group >= 48) return 5;
     return 6;
   }
-  if (per_group >= 512) return 7;   // 256x256, K stage 128
-  if (per_group >= 128) return 9;   // 128x256, K stage 128
+  const bool stacked = layout == FP8GG_LAYOUT_STACKED;
+  if (per_group >= 512) return stacked ? 16 : 7;   // 256x256, K stage 128 (persistent, split tail when stacked)
+  if (per_group >= 128) return 9;                  // 128x256, K stage 128
   if (per_group >= 48) return 2;
   // At most one row per group on average: few groups hold rows, so spread each
   // group's weights over many workgroups (32 columns each, K split over 4 waves).
-  const int64_t rows = layout == FP8GG_LAYOUT_STACKED ? M : G * M;
-  if (rows <= G) return 16;
+  const int64_t rows = stacked ? M : G * M;
+  if (rows <= G) return 15;
   return 3;
+}
+
+// Compute units of the current device (the persistent grid), cached per device.
+int device_cus() {
+  static std::mutex mu;
+  static std::map<int, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(dev);
+  if (it != cache.end()) return it->second;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+  cache[dev] = cus;
+  return cus;
+}
+
+// Split-tail workspace, one per (device, stream): calls on one stream run in order,
+// so they can share it; calls on different streams never do.  Allocated on first
+// use outside graph capture and kept for the life of the process.  Counters are
+// zeroed at allocation and every call leaves them zero.
+struct Workspace {
+  void* base = nullptr;
+  size_t bytes = 0;
+};
+
+fp8gg_status tail_workspace(hipStream_t stream, size_t need, Workspace* out, bool* available) {
+  static std::mutex mu;
+  static std::map<std::pair<int, hipStream_t>, Workspace> pool;
+  *available = false;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(FP8GG_ERR_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lock(mu);
+  Workspace& w = pool[std::make_pair(dev, stream)];
+  if (w.base && w.bytes >= need) {
+    *out = w;
+    *available = true;
+    return FP8GG_OK;
+  }
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return FP8GG_OK;
+  if (w.base) {
+    // Growing: the old buffer may still be in use by queued work on this stream.
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "workspace resize: %s", hipGetErrorString(e));
+    (void)hipFree(w.base);
+    w.base = nullptr;
+    w.bytes = 0;
+  }
+  void* p = nullptr;
+  hipError_t e = hipMalloc(&p, need);
+  if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "workspace allocation of %zu bytes: %s", need, hipGetErrorString(e));
+  e = hipMemset(p, 0, need);
+  if (e != hipSuccess) {
+    (void)hipFree(p);
+    return fail(FP8GG_ERR_HIP, "workspace clear: %s", hipGetErrorString(e));
+  }
+  w.base = p;
+  w.bytes = need;
+  *out = w;
+  *available = true;
+  return FP8GG_OK;
 }
 
 fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K,
@@ -125,6 +191,8 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
       return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_CONFIG=%d does not name a usable configuration", forced);
     cfg = forced;
   }
+  if (layout != FP8GG_LAYOUT_STACKED && fp8gg::kConfigs[cfg].kind == fp8gg::kKindSplitTail)
+    cfg = fp8gg::kConfigs[cfg].twin;   // the split tail is scheduled over the stacked layout only
   const fp8gg::KernelConfig& c = fp8gg::kConfigs[cfg];
   p->config_id = cfg;
   p->BM = c.BM;
@@ -141,6 +209,7 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
     int64_t ub = (M + c.BM - 1) / c.BM + G - 1;
     p->m_tiles = ub < M ? ub : M;
     p->grid = p->m_tiles * p->n_tiles;
+    p->split_tail = c.kind == fp8gg::kKindSplitTail ? 1 : 0;
   } else {
     p->m_tiles = (M + c.BM - 1) / c.BM;
     p->grid = p->m_tiles * p->n_tiles * G;
@@ -202,11 +271,34 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
   if (env_int("FP8GG_LOG", 0))
     std::fprintf(stderr,
                  "[fp8gg] layout=%d pre=%d G=%lld M=%lld N=%lld K=%lld -> cfg=%d tile=%dx%dx%d thr=%d st=%d "
-                 "ktail=%d ntail=%d grid=%lld (m_tiles=%lld n_tiles=%lld)\n",
+                 "ktail=%d ntail=%d grid=%lld (m_tiles=%lld n_tiles=%lld) split_tail=%d\n",
                  layout, preshuffled, (long long)G, (long long)M, (long long)N, (long long)K, p.config_id, p.BM,
                  p.BN, p.BK, p.threads, p.stages, p.k_tail, p.n_tail, (long long)p.grid, (long long)p.m_tiles,
-                 (long long)p.n_tiles);
-  hipError_t e = fp8gg::launch_gemm(layout, p.config_id, p.k_tail != 0, a, p.grid, s);
+                 (long long)p.n_tiles, p.split_tail);
+  const fp8gg::KernelConfig& cfg = fp8gg::kConfigs[p.config_id];
+  hipError_t e;
+  if (cfg.kind == fp8gg::kKindSplitTail) {
+    // One persistent workgroup per compute unit.  For tuning and tests,
+    // FP8GG_TAIL_GRID overrides the grid and FP8GG_TAIL_SPLIT the split factor.
+    const int forced_grid = env_int("FP8GG_TAIL_GRID", 0);
+    const int P = forced_grid > 0 ? forced_grid : device_cus();
+    const int force_split = env_int("FP8GG_TAIL_SPLIT", 0);
+    if (env_int("FP8GG_LOG", 0)) std::fprintf(stderr, "[fp8gg] persistent grid %d, forced split %d\n", P, force_split);
+    Workspace ws;
+    bool have = false;
+    st = tail_workspace(s, fp8gg::tail_workspace_bytes(cfg, P), &ws, &have);
+    if (st != FP8GG_OK) return st;
+    if (have) {
+      uint32_t* counters = static_cast<uint32_t*>(ws.base);
+      float* partials = reinterpret_cast<float*>(static_cast<char*>(ws.base) + fp8gg::tail_counters_bytes(P));
+      e = fp8gg::launch_gemm_tail(p.config_id, p.k_tail != 0, a, P, partials, counters, force_split, s);
+    } else {
+      // Captured before any workspace existed on this stream: the data-parallel twin.
+      e = fp8gg::launch_gemm(layout, cfg.twin, p.k_tail != 0, a, p.grid, s);
+    }
+  } else {
+    e = fp8gg::launch_gemm(layout, p.config_id, p.k_tail != 0, a, p.grid, s);
+  }
   if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }

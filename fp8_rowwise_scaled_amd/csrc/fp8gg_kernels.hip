@@ -100,6 +100,27 @@ __device__ __forceinline__ void wait_vmcnt_le(int n) {
 template <int BK>
 __device__ __forceinline__ int lds_swz(int p) { return (p / (256 / BK)) & (BK / 16 - 1); }
 
+// One 16-byte-per-lane copy from global memory straight into LDS: lane l's 16 bytes
+// land at LDS byte lds_base + 16*l (lds_base wave-uniform).  Written as inline
+// assembly so that the compiler's wait-count pass does not track it: the pass
+// cannot tell LDS slots apart when the slot index is a run-time value and would
+// otherwise drain every copy in flight before each LDS read.  The callers order
+// copies and reads themselves (wait_vmcnt_le, then a workgroup barrier).
+__device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :: "v"(src), "s"(lds_base) : "memory");
+}
+
+// Same, 4 bytes per lane: lane l's 4 bytes land at LDS byte lds_base + 4*l.
+__device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :: "v"(src), "s"(lds_base) : "memory");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(lds_ptr_t)p;
+}
+
 __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -180,100 +201,109 @@ __device__ __forceinline__ void zero_rect(uint16_t* Y, int64_t N, int64_t r0, in
 }
 
 // ---------------------------------------------------------------------------
-// The grouped GEMM kernel (plain W, both operands staged through LDS)
+// The grouped GEMM with plain W: both operands staged through LDS
 // ---------------------------------------------------------------------------
+//
+// LdsTile holds everything one workgroup needs to compute one BM x BN output tile
+// over a range of K stages: the per-thread copy descriptors, the LDS pipeline, the
+// MFMA loop and the scaled epilogue.  The data-parallel kernel runs one tile per
+// workgroup; the split-tail kernel runs a sequence of whole tiles and a K piece per
+// persistent workgroup.
 
-template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PIPE>
-__global__ void __launch_bounds__(WM * WN * 64)
-gg_lds_kernel(GemmArgs a) {
-  constexpr int NT = WM * WN * 64;
-  constexpr int CPR = BK / 16;          // 16-byte chunks per LDS row
-  constexpr int KS = BK / 64;           // MFMA K steps per stage
-  constexpr int TM = BM / WM;           // wave tile along M (rows of X)
-  constexpr int TN = BN / WN;           // wave tile along N (columns of Y)
-  constexpr int FM = TM / 32;           // 32x32 MFMA blocks per wave along M
-  constexpr int FN = TN / 32;           // ... along N
-  constexpr int A_CHUNKS = BM * BK / 16;
-  constexpr int B_CHUNKS = BN * BK / 16;
-  constexpr int A_LOADS = (A_CHUNKS + NT - 1) / NT;
-  constexpr int B_LOADS = (B_CHUNKS + NT - 1) / NT;
-  constexpr int A_BYTES = BM * BK;
-  constexpr int STAGE_BYTES = (BM + BN) * BK;
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL>
+struct LdsTile {
+  static constexpr int NT = WM * WN * 64;
+  static constexpr int CPR = BK / 16;          // 16-byte chunks per LDS row
+  static constexpr int KS = BK / 64;           // MFMA K steps per stage
+  static constexpr int TM = BM / WM;           // wave tile along M (rows of X)
+  static constexpr int TN = BN / WN;           // wave tile along N (columns of Y)
+  static constexpr int FM = TM / 32;           // 32x32 MFMA blocks per wave along M
+  static constexpr int FN = TN / 32;           // ... along N
+  static constexpr int A_CHUNKS = BM * BK / 16;
+  static constexpr int B_CHUNKS = BN * BK / 16;
+  static constexpr int A_LOADS = (A_CHUNKS + NT - 1) / NT;
+  static constexpr int B_LOADS = (B_CHUNKS + NT - 1) / NT;
+  static constexpr int A_BYTES = BM * BK;
+  static constexpr int STAGE_BYTES = (BM + BN) * BK;
+  static constexpr int SMEM_BYTES = STAGES * STAGE_BYTES;
+  static constexpr int ACC_FLOATS = FM * FN * 16;   // accumulator floats per thread
+  // Copies per thread per stage when every wave issues the same number (the
+  // persistent kernel requires it).
+  static constexpr int LOADS_PER_STAGE = A_LOADS + B_LOADS;
+  static constexpr bool EVEN_LOADS = A_CHUNKS % NT == 0 && B_CHUNKS % NT == 0;
   static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be a multiple of 32");
   static_assert(A_CHUNKS % 64 == 0 && B_CHUNKS % 64 == 0, "tile rows must be a multiple of 16");
   static_assert(BK == 64 || BK == 128, "BK is 64 or 128");
+  static_assert(STAGES >= 2, "at least two LDS stages");
 
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[STAGES * STAGE_BYTES];
+  typedef v16f Acc[FM][FN];
+  typedef v4i Packed[FM][FN][2];   // bf16 outputs, eight columns per vector (see scale())
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave / WN;
-  const int wn = wave % WN;
-
-  // ---- which tile ----
-  const int64_t bid = blockIdx.x;
-  const int64_t n_tile = bid % a.n_tiles;
-  const int64_t rest = bid / a.n_tiles;
-  Tile t;
-  if (LAYOUT == kStacked) {
-    if (!resolve_stacked<BM>(a, rest, t)) return;
-  } else {
-    if (!resolve_padded<BM>(a, rest / a.m_tiles, rest % a.m_tiles, t)) return;
-  }
-  const int64_t N = a.N;
-  const int64_t K = a.K;
-  const int64_t n0 = n_tile * BN;
-  const int64_t tile_row_end = t.row_base + BM;
-
-  if (t.row_base >= t.row_end) {
-    // Entirely padding (padded layout with zeroing): no K loop.
-    const int64_t r1 = tile_row_end < t.zero_end ? tile_row_end : t.zero_end;
-    const int64_t c1 = n0 + BN < N ? n0 + BN : N;
-    zero_rect<NT>(a.Y, N, t.row_base, r1, n0, c1);
-    return;
-  }
-
-  // ---- per-thread copy descriptors (global source at k = 0) ----
-  // Chunk q of a stage (16 bytes) lands at LDS byte 16*q: row p = q / CPR, physical
-  // chunk q % CPR, which holds logical chunk (q % CPR) ^ lds_swz<BK>(p).
+  uint8_t* smem;
+  int tid, lane, wave, wm, wn, h, r32;
+  int loads_per_stage;
   const uint8_t* a_src[A_LOADS];
   int a_kc[A_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int q = i * NT + tid;
-    const int p = (q / CPR) % BM;
-    const int c = (q % CPR) ^ lds_swz<BK>(p);
-    int64_t row = t.row_base + p;
-    row = row < t.row_end ? row : t.row_end - 1;   // rows past the group: any valid row, result dropped
-    a_src[i] = a.X + row * K + c * 16;
-    a_kc[i] = c * 16;
-  }
   const uint8_t* b_src[B_LOADS];
   int b_kc[B_LOADS];
-  const uint8_t* Wg = a.W + t.g * N * K;
+
+  __device__ __forceinline__ void init(uint8_t* smem_) {
+    smem = smem_;
+    tid = threadIdx.x;
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    wm = wave / WN;
+    wn = wave % WN;
+    h = lane >> 5;
+    r32 = lane & 31;
+    // Loads this thread issues per stage (the vmcnt unit of one stage); waves whose
+    // chunk range ends inside a partial round issue fewer.
+    loads_per_stage = 0;
 #pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) {
-    const int q = i * NT + tid;
-    const int p = (q / CPR) % BN;
-    const int c = (q % CPR) ^ lds_swz<BK>(p);
-    // MFMA order: LDS row p = wn_*TN + 32*fn + rho holds output column
-    // wn_*TN + h*16*FN + 16*fn + 4*j + tt, rho = 8*j + 4*h + tt.
-    const int wn_ = p / TN;
-    const int pp = p % TN;
-    const int fn = pp >> 5;
-    const int rho = pp & 31;
-    const int nl = wn_ * TN + ((rho >> 2) & 1) * 16 * FN + 16 * fn + 4 * (rho >> 3) + (rho & 3);
-    int64_t n = n0 + nl;
-    n = n < N ? n : N - 1;                            // columns past N: result dropped
-    b_src[i] = Wg + n * K + c * 16;
-    b_kc[i] = c * 16;
+    for (int i = 0; i < A_LOADS; ++i) loads_per_stage += (A_CHUNKS % NT == 0 || i * NT + wave * 64 < A_CHUNKS);
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) loads_per_stage += (B_CHUNKS % NT == 0 || i * NT + wave * 64 < B_CHUNKS);
   }
 
-  const int nk = (int)((K + BK - 1) / BK);
+  // Copy descriptors (global source at k = 0) for the tile at rows t, columns n0.
+  // Chunk q of a stage (16 bytes) lands at LDS byte 16*q: row p = q / CPR, physical
+  // chunk q % CPR, which holds logical chunk (q % CPR) ^ lds_swz<BK>(p).
+  __device__ __forceinline__ void setup(const GemmArgs& a, const Tile& t, int64_t n0) {
+    const int64_t N = a.N, K = a.K;
+#pragma unroll
+    for (int i = 0; i < A_LOADS; ++i) {
+      const int q = i * NT + tid;
+      const int p = (q / CPR) % BM;
+      const int c = (q % CPR) ^ lds_swz<BK>(p);
+      int64_t row = t.row_base + p;
+      row = row < t.row_end ? row : t.row_end - 1;   // rows past the group: any valid row, result dropped
+      a_src[i] = a.X + row * K + c * 16;
+      a_kc[i] = c * 16;
+    }
+    const uint8_t* Wg = a.W + t.g * N * K;
+#pragma unroll
+    for (int i = 0; i < B_LOADS; ++i) {
+      const int q = i * NT + tid;
+      const int p = (q / CPR) % BN;
+      const int c = (q % CPR) ^ lds_swz<BK>(p);
+      // MFMA order: LDS row p = wn_*TN + 32*fn + rho holds output column
+      // wn_*TN + h*16*FN + 16*fn + 4*j + tt, rho = 8*j + 4*h + tt.
+      const int wn_ = p / TN;
+      const int pp = p % TN;
+      const int fn = pp >> 5;
+      const int rho = pp & 31;
+      const int nl = wn_ * TN + ((rho >> 2) & 1) * 16 * FN + 16 * fn + 4 * (rho >> 3) + (rho & 3);
+      int64_t n = n0 + nl;
+      n = n < N ? n : N - 1;                            // columns past N: result dropped
+      b_src[i] = Wg + n * K + c * 16;
+      b_kc[i] = c * 16;
+    }
+  }
 
-  auto issue = [&](int kt) {
-    uint8_t* sbase = smem + (kt % STAGES) * STAGE_BYTES;
+  // Copies of K stage kt into LDS slot `slot`; on the last stage (KTAIL) chunks at
+  // or past K are read from the zero page.
+  __device__ __forceinline__ void issue(int kt, int slot, int nk, int64_t K) {
+    uint8_t* sbase = smem + slot * STAGE_BYTES;
     const int64_t koff = (int64_t)kt * BK;
     const bool last = KTAIL && (kt == nk - 1);
 #pragma unroll
@@ -281,7 +311,7 @@ gg_lds_kernel(GemmArgs a) {
       if (A_CHUNKS % NT == 0 || i * NT + wave * 64 < A_CHUNKS) {
         const uint8_t* src = a_src[i] + koff;
         if (last && koff + a_kc[i] >= K) src = g_zero16;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src, (lds_ptr_t)(sbase + (i * NT + wave * 64) * 16), 16, 0, 0);
+        copy16_to_lds(src, lds_addr(sbase + (i * NT + wave * 64) * 16));
       }
     }
 #pragma unroll
@@ -289,33 +319,16 @@ gg_lds_kernel(GemmArgs a) {
       if (B_CHUNKS % NT == 0 || i * NT + wave * 64 < B_CHUNKS) {
         const uint8_t* src = b_src[i] + koff;
         if (last && koff + b_kc[i] >= K) src = g_zero16;
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)src,
-                                         (lds_ptr_t)(sbase + A_BYTES + (i * NT + wave * 64) * 16), 16, 0, 0);
+        copy16_to_lds(src, lds_addr(sbase + A_BYTES + (i * NT + wave * 64) * 16));
       }
     }
-  };
-  // Loads this thread issues per stage (the vmcnt unit of one stage); waves whose
-  // chunk range ends inside a partial round issue fewer.
-  int loads_per_stage = 0;
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) loads_per_stage += (A_CHUNKS % NT == 0 || i * NT + wave * 64 < A_CHUNKS);
-#pragma unroll
-  for (int i = 0; i < B_LOADS; ++i) loads_per_stage += (B_CHUNKS % NT == 0 || i * NT + wave * 64 < B_CHUNKS);
+  }
 
-  v16f acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{0};
-
-  const int h = lane >> 5;
-  const int r32 = lane & 31;
-
-  // MFMA operands of stage kt from LDS: for MFMA step ks of the stage, lane (h, r32)
+  // MFMA operands of the stage in LDS slot `slot`: for MFMA step ks, lane (h, r32)
   // takes row r32 of each 32-row block, bytes [64*ks + 32h, +32) (logical chunks
   // 4ks + 2h and 4ks + 2h + 1).
-  auto read_frags = [&](int kt, v8i (&xf)[KS][FM], v8i (&wf)[KS][FN]) {
-    const uint8_t* sA = smem + (kt % STAGES) * STAGE_BYTES;
+  __device__ __forceinline__ void read_frags(int slot, v8i (&xf)[KS][FM], v8i (&wf)[KS][FN]) const {
+    const uint8_t* sA = smem + slot * STAGE_BYTES;
     const uint8_t* sB = sA + A_BYTES;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
@@ -336,116 +349,490 @@ gg_lds_kernel(GemmArgs a) {
         wf[ks][fn] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
     }
-  };
-  auto mfmas = [&](const v8i (&xf)[KS][FM], const v8i (&wf)[KS][FN]) {
+  }
+
+  // acc += the tile's products over K stages [kb, ke).  Every thread of the
+  // workgroup must call it; it starts by waiting until the workgroup has finished
+  // reading LDS from any previous call, so LdsTile can be reused tile after tile.
+  // Issues the first STAGES - 1 stages of K range [kb, ke).  It starts with a
+  // workgroup barrier: every wave must be done reading LDS (from a previous tile)
+  // before the copies overwrite it.
+  __device__ __forceinline__ void prologue(int kb, int ke, int nk, int64_t K) {
+    block_barrier();
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s)
+      if (kb + s < ke) issue(kb + s, s, nk, K);
+  }
+
+  // acc += the tile's products over K stages [kb, ke), whose first STAGES - 1
+  // stages prologue() has issued.  Every thread of the workgroup must call it.
+  __device__ __forceinline__ void mainloop(int kb, int ke, int nk, int64_t K, Acc& acc) {
+    for (int kt = kb; kt < ke; ++kt) {
+      const int j = kt - kb;
+      // Stage kt has landed once at most (stages issued after it) loads of this
+      // thread are outstanding (vector memory operations complete in order, so
+      // any younger stores only make the wait stricter); the barrier then makes
+      // every thread's copies visible and frees the slot that the next issue
+      // overwrites.
+      const int ahead = ke - 1 - kt;
+      if (ahead >= STAGES - 2) wait_vmcnt_le((STAGES - 2) * loads_per_stage);
+      else wait_vmcnt_le(0);
+      block_barrier();
+      if (kt + STAGES - 1 < ke) issue(kt + STAGES - 1, (j + STAGES - 1) % STAGES, nk, K);
+      v8i xf[KS][FM], wf[KS][FN];
+      read_frags(j % STAGES, xf, wf);
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wf[ks][fn], xf[ks][fm], acc[fm][fn]);
+    }
+  }
+
+  // acc += the products of the stage in LDS slot `slot` (all waves, after the
+  // barrier that follows that stage's copies).
+  __device__ __forceinline__ void compute(int slot, Acc& acc) const {
+    v8i xf[KS][FM], wf[KS][FN];
+    read_frags(slot, xf, wf);
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
       for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wf[ks][fn], xf[ks][fm], acc[fm][fn]);
-  };
+  }
 
-  if constexpr (!PIPE) {
-    // Prologue: stages 0 .. STAGES-2 in flight.
-#pragma unroll
-    for (int s = 0; s < STAGES - 1; ++s)
-      if (s < nk) issue(s);
-    for (int kt = 0; kt < nk; ++kt) {
-      // Tile kt has landed once at most (tiles issued after it) loads of this thread
-      // are outstanding; then the barrier makes every thread's copies visible and
-      // frees the stage that the next issue overwrites.
-      const int ahead = nk - 1 - kt;
-      if (ahead >= STAGES - 2) wait_vmcnt_le((STAGES - 2) * loads_per_stage);
-      else wait_vmcnt_le(0);
-      block_barrier();
-      if (kt + STAGES - 1 < nk) issue(kt + STAGES - 1);
-      v8i xf[KS][FM], wf[KS][FN];
-      read_frags(kt, xf, wf);
-      mfmas(xf, wf);
-    }
-  } else {
-    // Software-pipelined loop: while the MFMAs of step s run on registers read
-    // during step s-1, the operands of step s+1 are read from LDS into the other
-    // register set and the copies of steps s+2 .. s+STAGES-1 are in flight.
-    // Prologue: copies of steps 0 .. STAGES-1 (every stage starts free).
-#pragma unroll
-    for (int s = 0; s < STAGES; ++s)
-      if (s < nk) issue(s);
-    {
-      const int issued = nk < STAGES ? nk : STAGES;
-      wait_vmcnt_le((issued - 1) * loads_per_stage);
-    }
-    block_barrier();
-    v8i xa[KS][FM], wa[KS][FN], xb[KS][FM], wb[KS][FN];
-    read_frags(0, xa, wa);
-
-    auto step = [&](int s, const v8i (&xc)[KS][FM], const v8i (&wc)[KS][FN], v8i (&xn)[KS][FM],
-                    v8i (&wn_)[KS][FN]) {
-      // This wave's reads of step s are complete (the stage may be refilled after
-      // the barrier), and step s+1's copies have landed.
-      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0)
-      if (s + 1 < nk) {
-        const int issued_last = (s + STAGES - 1 < nk - 1) ? s + STAGES - 1 : nk - 1;
-        wait_vmcnt_le((issued_last - (s + 1)) * loads_per_stage);
+  // The tile's scales as an LDS block of BN + BM floats: w_scale[g, n0 .. n0+BN)
+  // then x_scale[row_base .. row_base+BM), copied 64 floats per wave (4 bytes per
+  // lane) by the same copy engine as the operands, so they travel with a K stage.
+  // Columns past N and rows past the group read a valid neighbour (never stored).
+  // Every wave issues exactly one copy, the waves beyond the block into a dummy
+  // word, so that a stage carrying scales adds one to every wave's count.
+  static constexpr int SCALE_FLOATS = BN + BM;
+  __device__ __forceinline__ void issue_scales(const GemmArgs& a, const Tile& t, int64_t n0, float* sbuf,
+                                               float* dummy) const {
+    static_assert(SCALE_FLOATS % 64 == 0 && SCALE_FLOATS <= NT, "one scale copy per wave");
+    const int f = wave * 64 + lane;
+    const float* src;
+    float* dst;
+    if (wave < SCALE_FLOATS / 64) {
+      if (f < BN) {
+        int64_t c = n0 + f;
+        c = c < a.N ? c : a.N - 1;
+        src = a.ws + t.g * a.N + c;
+      } else {
+        int64_t r = t.row_base + (f - BN);
+        r = r < t.row_end ? r : t.row_end - 1;
+        src = a.xs + r;
       }
-      block_barrier();
-      if (s + STAGES < nk) issue(s + STAGES);
-      if (s + 1 < nk) read_frags(s + 1, xn, wn_);
-      mfmas(xc, wc);
-    };
-    for (int s = 0; s < nk; s += 2) {
-      step(s, xa, wa, xb, wb);
-      if (s + 1 < nk) step(s + 1, xb, wb, xa, wa);
+      dst = sbuf + wave * 64;
+    } else {
+      src = a.ws + t.g * a.N;
+      dst = dummy;
     }
+    copy4_to_lds(src, lds_addr(dst));
   }
 
-  // ---- epilogue: y = bf16((acc * x_scale[m]) * w_scale[g, n]) ----
-  // Lane (h, r32) holds, for block (fm, fn), slot i = 4*j + tt, output row
-  // wm*TM + 32*fm + r32 and column col0 + 16*fn + i.
-  const int64_t col0 = n0 + wn * TN + h * 16 * FN;
-  const float* wsg = a.ws + t.g * N;
-  float wsv[16 * FN];
+  // scale() with the scales taken from an LDS block written by issue_scales.
+  __device__ __forceinline__ void scale_lds(const Acc& acc, const float* sbuf, Packed& pk) const {
+    const float* wsl = sbuf + wn * TN + h * 16 * FN;
 #pragma unroll
-  for (int v = 0; v < 4 * FN; ++v) {
-    const int64_t c = col0 + 4 * v;
-    v4f w4 = {0.f, 0.f, 0.f, 0.f};
-    if (c < N) w4 = *(const v4f*)(wsg + c);
-    wsv[4 * v + 0] = w4.x;
-    wsv[4 * v + 1] = w4.y;
-    wsv[4 * v + 2] = w4.z;
-    wsv[4 * v + 3] = w4.w;
-  }
+    for (int fm = 0; fm < FM; ++fm) {
+      const float xsv = sbuf[BN + wm * TM + 32 * fm + r32];
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int64_t m = t.row_base + wm * TM + 32 * fm + r32;
-    if (m < t.row_end) {
-      const float xsv = a.xs[m];
-      uint16_t* yrow = a.Y + m * N;
+      for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-      for (int s = 0; s < 2 * FN; ++s) {           // 8 columns per 16-byte store
-        const int64_t c = col0 + 8 * s;
-        if (c < N) {
-          const int fn = s >> 1;
-          const int base = (s & 1) * 8;
-          uint32_t pk[4];
+        for (int half = 0; half < 2; ++half) {
+          const v4f w0 = *(const v4f*)(wsl + 16 * fn + 8 * half);
+          const v4f w1 = *(const v4f*)(wsl + 16 * fn + 8 * half + 4);
+          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+          uint32_t q[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const float v0 = (acc[fm][fn][base + 2 * e] * xsv) * wsv[16 * fn + base + 2 * e];
-            const float v1 = (acc[fm][fn][base + 2 * e + 1] * xsv) * wsv[16 * fn + base + 2 * e + 1];
-            pk[e] = pack_bf16x2(v0, v1);
+            const int i = 8 * half + 2 * e;
+            q[e] = pack_bf16x2((acc[fm][fn][i] * xsv) * wv[2 * e], (acc[fm][fn][i + 1] * xsv) * wv[2 * e + 1]);
           }
-          *(v4i*)(yrow + c) = v4i{(int)pk[0], (int)pk[1], (int)pk[2], (int)pk[3]};
+          pk[fm][fn][half] = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+        }
+    }
+  }
+
+  __device__ __forceinline__ void run(int kb, int ke, int nk, int64_t K, Acc& acc) {
+    prologue(kb, ke, nk, K);
+    mainloop(kb, ke, nk, K, acc);
+  }
+
+  // The epilogue, y = bf16((acc * x_scale[m]) * w_scale[g, n]) under row and
+  // column masks, in two halves so that a persistent workgroup can issue the next
+  // tile's first copies between them: scale() loads the scales and turns the
+  // accumulators into packed bf16 pairs, store() writes them (and writes rows
+  // [row_end, zero_end) as zero).  Lane (h, r32) holds, for block (fm, fn), slot
+  // i = 4*j + tt, output row wm*TM + 32*fm + r32 and column col0 + 16*fn + i; pair
+  // q of Packed[fm][fn] holds slots 2q and 2q + 1.
+
+  __device__ __forceinline__ void scale(const GemmArgs& a, const Tile& t, int64_t n0, const Acc& acc,
+                                        Packed& pk) const {
+    const int64_t N = a.N;
+    const int64_t col0 = n0 + wn * TN + h * 16 * FN;
+    const float* wsg = a.ws + t.g * N;
+    float wsv[16 * FN];
+#pragma unroll
+    for (int v = 0; v < 4 * FN; ++v) {
+      const int64_t c = col0 + 4 * v;
+      v4f w4 = {0.f, 0.f, 0.f, 0.f};
+      if (c < N) w4 = *(const v4f*)(wsg + c);
+      wsv[4 * v + 0] = w4.x;
+      wsv[4 * v + 1] = w4.y;
+      wsv[4 * v + 2] = w4.z;
+      wsv[4 * v + 3] = w4.w;
+    }
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int64_t m = t.row_base + wm * TM + 32 * fm + r32;
+      const float xsv = m < t.row_end ? a.xs[m] : 0.f;   // rows past the group are never stored
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          uint32_t q[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int i = 8 * half + 2 * e;
+            q[e] = pack_bf16x2((acc[fm][fn][i] * xsv) * wsv[16 * fn + i],
+                               (acc[fm][fn][i + 1] * xsv) * wsv[16 * fn + i + 1]);
+          }
+          pk[fm][fn][half] = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+        }
+    }
+  }
+
+  __device__ __forceinline__ void store(const GemmArgs& a, const Tile& t, int64_t n0, const Packed& pk) const {
+    const int64_t N = a.N;
+    const int64_t col0 = n0 + wn * TN + h * 16 * FN;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int64_t m = t.row_base + wm * TM + 32 * fm + r32;
+      if (m < t.row_end) {
+        uint16_t* yrow = a.Y + m * N;
+#pragma unroll
+        for (int s = 0; s < 2 * FN; ++s) {           // 8 columns per 16-byte store
+          const int64_t c = col0 + 8 * s;
+          if (c < N) *(v4i*)(yrow + c) = pk[fm][s >> 1][s & 1];
+        }
+      } else if (m < t.zero_end) {
+        uint16_t* yrow = a.Y + m * N;
+#pragma unroll
+        for (int s = 0; s < 2 * FN; ++s) {
+          const int64_t c = col0 + 8 * s;
+          if (c < N) *(v4i*)(yrow + c) = v4i{0, 0, 0, 0};
         }
       }
-    } else if (m < t.zero_end) {
-      uint16_t* yrow = a.Y + m * N;
-#pragma unroll
-      for (int s = 0; s < 2 * FN; ++s) {
-        const int64_t c = col0 + 8 * s;
-        if (c < N) *(v4i*)(yrow + c) = v4i{0, 0, 0, 0};
-      }
     }
+  }
+
+  __device__ __forceinline__ void epilogue(const GemmArgs& a, const Tile& t, int64_t n0, const Acc& acc) const {
+    Packed pk;
+    scale(a, t, n0, acc, pk);
+    store(a, t, n0, pk);
+  }
+
+  // Accumulators <-> a partial-sum slot of ACC_FLOATS * NT floats.  Quad q of the
+  // accumulator registers (floats 4q .. 4q+3) of all NT threads is NT consecutive
+  // 16-byte vectors, so every access is a coalesced 16-byte-per-lane vector access.
+  // Loads go one 16-float block at a time (the empty asm keeps the compiler from
+  // hoisting every block's loads ahead of the additions, which would need a second
+  // accumulator's worth of registers).
+  __device__ __forceinline__ v4f* quad(float* slot, int blk, int q) const {
+    return reinterpret_cast<v4f*>(slot) + (int64_t)(blk * 4 + q) * NT + tid;
+  }
+  __device__ __forceinline__ const v4f* quad(const float* slot, int blk, int q) const {
+    return reinterpret_cast<const v4f*>(slot) + (int64_t)(blk * 4 + q) * NT + tid;
+  }
+  __device__ __forceinline__ void store_partial(float* slot, const Acc& acc) const {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v16f& c = acc[fm][fn];
+          *quad(slot, fm * FN + fn, q) = v4f{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
+        }
+  }
+  template <bool ADD>
+  __device__ __forceinline__ void gather_partial(const float* slot, Acc& acc) const {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        v4f v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = *quad(slot, fm * FN + fn, q);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            acc[fm][fn][4 * q + j] = ADD ? acc[fm][fn][4 * q + j] + v[q][j] : v[q][j];
+        asm volatile("" ::: "memory");
+      }
+  }
+  __device__ __forceinline__ void load_partial(const float* slot, Acc& acc) const { gather_partial<false>(slot, acc); }
+  __device__ __forceinline__ void add_partial(const float* slot, Acc& acc) const { gather_partial<true>(slot, acc); }
+};
+
+// Data-parallel kernel: one output tile per workgroup, whole K.
+template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL>
+__global__ void __launch_bounds__(WM * WN * 64)
+gg_lds_kernel(GemmArgs a) {
+  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL> E;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
+
+  const int64_t bid = blockIdx.x;
+  const int64_t n_tile = bid % a.n_tiles;
+  const int64_t rest = bid / a.n_tiles;
+  Tile t;
+  if (LAYOUT == kStacked) {
+    if (!resolve_stacked<BM>(a, rest, t)) return;
+  } else {
+    if (!resolve_padded<BM>(a, rest / a.m_tiles, rest % a.m_tiles, t)) return;
+  }
+  const int64_t n0 = n_tile * BN;
+  if (t.row_base >= t.row_end) {
+    // Entirely padding (padded layout with zeroing): no K loop.
+    const int64_t tile_row_end = t.row_base + BM;
+    const int64_t r1 = tile_row_end < t.zero_end ? tile_row_end : t.zero_end;
+    const int64_t c1 = n0 + BN < a.N ? n0 + BN : a.N;
+    zero_rect<E::NT>(a.Y, a.N, t.row_base, r1, n0, c1);
+    return;
+  }
+  E e;
+  e.init(smem);
+  e.setup(a, t, n0);
+  typename E::Acc acc;
+#pragma unroll
+  for (int i = 0; i < E::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < E::FN; ++j) acc[i][j] = v16f{0};
+  const int nk = (int)((a.K + BK - 1) / BK);
+  e.run(0, nk, nk, a.K, acc);
+  e.epilogue(a, t, n0, acc);
+}
+
+// Number of M tiles over all groups (stacked layout), with the resolver's clamping.
+template <int BM>
+__device__ __forceinline__ int64_t count_m_tiles(const GemmArgs& a) {
+  int64_t start = 0, tiles = 0;
+  for (int64_t g0 = 0; g0 < a.G; g0 += 8) {
+    int64_t cnt[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt[i] = a.meta[g0 + i < a.G ? g0 + i : a.G - 1];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (g0 + i >= a.G) break;
+      const int64_t s = cnt[i] < 0 ? 0 : cnt[i];
+      int64_t end = start + s;
+      end = end > a.M ? a.M : end;
+      tiles += (end - start + BM - 1) / BM;
+      start = end;
+    }
+  }
+  return tiles;
+}
+
+// Persistent kernel with a split last wave (stacked layout).
+//
+// Schedule.  A grid of P workgroups, one per compute unit, walks the T output
+// tiles in data-parallel order: workgroup w computes whole tiles w, w + P, ...
+// When T is not a multiple of P, the last wave of rem = T % P tiles would keep
+// P - rem compute units idle for a whole tile.  Instead each of those rem tiles is
+// cut along K into s pieces (s from tail_split, or forced by the caller) computed
+// by s different workgroups at once.  Piece p of remainder tile i runs on
+// workgroup p * rem + i and covers K stages [p * nk / s, (p + 1) * nk / s).  Each
+// piece stores its fp32 partial sums in its workgroup's workspace slot and bumps
+// the tile's counter; the piece that arrives last reloads all s partials and adds
+// them in piece order (so the result does not depend on arrival order), writes the
+// output tile and resets the counter to zero.  No workgroup ever waits for another.
+//
+// Pipeline.  A workgroup's items (whole tiles, then at most one piece) form one
+// stream of K stages through the LDS ring: while the last stages of one item are
+// multiplied, the first stages of the next are already being copied, and the
+// finished tile's epilogue runs with them in flight.  Each item's scales travel
+// with its first stage into one of two LDS scale blocks, so the epilogue reads no
+// global memory.  Copies of an item two ahead wait until the item before it is
+// done, which keeps two scale blocks enough.  The wait before each stage counts
+// the copies issued after that stage exactly (stores issued since then only make
+// it stricter: vector memory operations complete in order).
+//
+// Workspace: counters [P] uint32 (zero between calls), then P slots of
+// E::ACC_FLOATS * E::NT floats.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL>
+__global__ void __launch_bounds__(WM * WN * 64)
+gg_tail_kernel(GemmArgs a, float* partials, uint32_t* counters, int force_split) {
+  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL> E;
+  constexpr int64_t SLOT = (int64_t)E::ACC_FLOATS * E::NT;
+  // Deferring a finished tile's stores by one stage keeps them out of the next
+  // stage's wait; it needs the packed outputs live across one more MFMA step,
+  // which fits the register budget of the smaller tiles only.
+  constexpr bool DEFER_STORES = E::ACC_FLOATS <= 64;
+  static_assert(E::EVEN_LOADS, "the stage wait counts assume equal copies per wave");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) float scales[2][E::SCALE_FLOATS];
+  __shared__ __attribute__((aligned(16))) float scale_dummy[64];
+  __shared__ uint32_t is_finisher;
+
+  const int64_t P = gridDim.x;
+  const int64_t w = blockIdx.x;
+  const int nk = (int)((a.K + BK - 1) / BK);
+  const int64_t T = count_m_tiles<BM>(a) * a.n_tiles;
+  const int s = tail_split(T, P, nk, E::STAGE_BYTES, SLOT * 4, force_split);
+  const int64_t rem = s > 1 ? T % P : 0;
+  const int64_t whole = T - rem;
+
+  E e;
+  e.init(smem);
+
+  struct Item {
+    Tile t;
+    int64_t tile, n0;
+    int kb, ke, seq;
+    bool piece;
+  };
+  int64_t next = w;
+  bool piece_taken = rem == 0 || w >= rem * s;
+  auto take = [&](Item& it, int seq) -> bool {
+    it.kb = 0;
+    it.ke = nk;
+    it.piece = false;
+    it.seq = seq;
+    if (next < whole) {
+      it.tile = next;
+      next += P;
+    } else if (!piece_taken) {
+      piece_taken = true;
+      it.piece = true;
+      it.tile = whole + w % rem;
+      const int64_t p = w / rem;
+      it.kb = (int)(p * nk / s);
+      it.ke = (int)((p + 1) * nk / s);
+    } else {
+      return false;
+    }
+    resolve_stacked<BM>(a, it.tile / a.n_tiles, it.t);
+    it.n0 = (it.tile % a.n_tiles) * BN;
+    return true;
+  };
+
+  Item C;                       // the item whose stages are being multiplied
+  if (!take(C, 0)) return;
+  Item I = C;                   // the item whose stages are being copied
+  bool more = true;             // items may remain after I
+  int kt_i = I.kb;
+  int u_i = 0, u_c = 0;         // stages issued / multiplied so far (LDS slot = u % STAGES)
+  int ahead = 0;                // stages issued and not yet multiplied
+  uint32_t firsts = 0;          // bit j: the j-th oldest of those is an item's first stage
+  e.setup(a, I.t, I.n0);
+
+  auto issue_next = [&]() {
+    if (kt_i == I.ke) {
+      if (!more || I.seq != C.seq) return;
+      Item nx;
+      if (!take(nx, I.seq + 1)) {
+        more = false;
+        return;
+      }
+      I = nx;
+      kt_i = I.kb;
+      e.setup(a, I.t, I.n0);
+    }
+    const bool first = kt_i == I.kb;
+    e.issue(kt_i, u_i % STAGES, nk, a.K);
+    if (first) e.issue_scales(a, I.t, I.n0, scales[I.seq & 1], scale_dummy);
+    firsts |= (uint32_t)first << ahead;
+    ++ahead;
+    ++kt_i;
+    ++u_i;
+  };
+
+#pragma unroll
+  for (int j = 0; j < STAGES - 1; ++j) issue_next();
+
+  // One step of the stage stream: wait for stage u_c, make it visible, issue the
+  // next copies, multiply.
+  auto step = [&](typename E::Acc& acc, bool stores, const Tile& st, int64_t sn0, const typename E::Packed& pk) {
+    // Stage u_c has landed once only the copies issued after it are outstanding:
+    // L per younger stage, plus one for each younger stage that carries scales.
+    if (STAGES == 2 || ahead == 1) {
+      wait_vmcnt_le(0);
+    } else if (STAGES == 3) {
+      if (firsts & 2u) wait_vmcnt_le(E::LOADS_PER_STAGE + 1);
+      else wait_vmcnt_le(E::LOADS_PER_STAGE);
+    } else {
+      wait_vmcnt_le((ahead - 1) * E::LOADS_PER_STAGE + __builtin_popcount(firsts >> 1));
+    }
+    block_barrier();
+    if (stores) e.store(a, st, sn0, pk);
+    issue_next();
+    e.compute(u_c % STAGES, acc);
+    ++u_c;
+    --ahead;
+    firsts >>= 1;
+  };
+
+  typename E::Packed pk;
+  Tile st = C.t;                // tile of the stores deferred into the next item's first stage
+  int64_t sn0 = 0;
+  bool pending = false;
+  for (;;) {
+    typename E::Acc acc;
+#pragma unroll
+    for (int i = 0; i < E::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < E::FN; ++j) acc[i][j] = v16f{0};
+    // The first stage of the item is peeled off: it carries the previous tile's
+    // deferred stores, so the loop over the remaining stages carries only acc.
+    step(acc, DEFER_STORES && pending, st, sn0, pk);
+    pending = false;
+    for (int kt = C.kb + 1; kt < C.ke; ++kt) step(acc, false, st, sn0, pk);
+
+    const float* sbuf = scales[C.seq & 1];
+    if (C.piece) {
+      const int64_t i = C.tile - whole;
+      e.store_partial(partials + w * SLOT, acc);
+      // Every thread's stores have completed at the barrier.  An agent-scope release
+      // fence (L2 write-back) publishes them before the counter moves; the
+      // finisher's acquire fence after the counter (L2 invalidate) pairs with the
+      // other pieces' releases through the counter.  Only the finisher invalidates:
+      // an invalidate also drops lines that other workgroups of this XCD are using.
+      __syncthreads();
+      if (e.tid == 0) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+        const uint32_t before = atomicAdd(&counters[i], 1u);
+        const bool last = before == (uint32_t)(s - 1);
+        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        is_finisher = last ? 1u : 0u;
+      }
+      __syncthreads();
+      if (is_finisher) {
+        e.load_partial(partials + i * SLOT, acc);
+        for (int p = 1; p < s; ++p) e.add_partial(partials + (p * rem + i) * SLOT, acc);
+        if (e.tid == 0) counters[i] = 0;
+        e.scale_lds(acc, sbuf, pk);
+        e.store(a, C.t, C.n0, pk);
+      }
+      return;                   // a piece is always a workgroup's last item
+    }
+    e.scale_lds(acc, sbuf, pk);
+    const bool last_item = I.seq == C.seq;   // nothing was taken after C
+    if (DEFER_STORES && !last_item) {
+      st = C.t;
+      sn0 = C.n0;
+      pending = true;
+    } else {
+      e.store(a, C.t, C.n0, pk);
+    }
+    if (last_item) return;
+    C = I;
   }
 }
 
@@ -867,40 +1254,54 @@ __global__ void __launch_bounds__(256) zero_fill_kernel(v4i* __restrict__ y, int
 // Configuration table and launch dispatch
 // ---------------------------------------------------------------------------
 
-// kind: 0 = both operands through LDS, 1 = same with the software-pipelined loop,
+// kind: 0 = both operands through LDS (one tile per workgroup),
 //       2 = pre-shuffled W straight to registers (X through LDS),
-//       3 = small M: W and X straight to registers, K split across the 4 waves.
-//                      BM   BN   BK  WM WN stages kind wdepth
+//       3 = small M: W and X straight to registers, K split across the 4 waves,
+//       4 = kind 0 on a persistent grid with a split last wave (stacked layout).
+//                      BM   BN   BK  WM WN stages kind wdepth twin
 const KernelConfig kConfigs[] = {
-    /* 0 */ {256, 256, 64, 2, 4, 4, 0, 0},
-    /* 1 */ {128, 256, 64, 2, 4, 4, 0, 0},
-    /* 2 */ {64, 256, 64, 1, 4, 2, 0, 0},
-    /* 3 */ {32, 128, 64, 1, 4, 2, 0, 0},
-    /* 4 */ {128, 256, 64, 1, 4, 2, 2, 2},
-    /* 5 */ {64, 256, 64, 1, 4, 2, 2, 4},
-    /* 6 */ {32, 128, 64, 1, 4, 2, 2, 4},
-    /* 7 */ {256, 256, 128, 2, 4, 2, 0, 0},
-    /* 8 */ {256, 128, 128, 2, 4, 3, 0, 0},
-    /* 9 */ {128, 256, 128, 2, 4, 3, 0, 0},
-    /* 10 */ {128, 128, 128, 2, 2, 4, 0, 0},
-    /* 11 */ {256, 256, 64, 2, 4, 4, 1, 0},
-    /* 12 */ {256, 128, 128, 2, 2, 3, 0, 0},
-    /* 13 */ {128, 128, 64, 2, 2, 4, 0, 0},
-    /* 14 */ {32, 32, 64, 1, 4, 0, 3, 8},
-    /* 15 */ {64, 32, 64, 1, 4, 0, 3, 8},
-    /* 16 */ {32, 32, 64, 1, 4, 0, 3, 4},
+    /* 0 */ {256, 256, 64, 2, 4, 4, 0, 0, 0},
+    /* 1 */ {128, 256, 64, 2, 4, 4, 0, 0, 0},
+    /* 2 */ {64, 256, 64, 1, 4, 2, 0, 0, 0},
+    /* 3 */ {32, 128, 64, 1, 4, 2, 0, 0, 0},
+    /* 4 */ {128, 256, 64, 1, 4, 2, 2, 2, 0},
+    /* 5 */ {64, 256, 64, 1, 4, 2, 2, 4, 0},
+    /* 6 */ {32, 128, 64, 1, 4, 2, 2, 4, 0},
+    /* 7 */ {256, 256, 128, 2, 4, 2, 0, 0, 0},
+    /* 8 */ {256, 128, 128, 2, 4, 3, 0, 0, 0},
+    /* 9 */ {128, 256, 128, 2, 4, 3, 0, 0, 0},
+    /* 10 */ {128, 128, 128, 2, 2, 4, 0, 0, 0},
+    /* 11 */ {256, 128, 128, 2, 2, 3, 0, 0, 0},
+    /* 12 */ {128, 128, 64, 2, 2, 4, 0, 0, 0},
+    /* 13 */ {32, 32, 64, 1, 4, 0, 3, 8, 0},
+    /* 14 */ {64, 32, 64, 1, 4, 0, 3, 8, 0},
+    /* 15 */ {32, 32, 64, 1, 4, 0, 3, 4, 0},
+    /* 16 */ {256, 256, 128, 2, 4, 2, 4, 0, 7},
+    /* 17 */ {128, 256, 128, 2, 4, 3, 4, 0, 9},
 };
 const int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool PIPE = false>
+template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES>
 static hipError_t launch_lds(bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
   const dim3 block(WM * WN * 64);
   if (k_tail)
-    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, true, PIPE>), dim3((uint32_t)grid), block,
-                       0, s, a);
+    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, true>), dim3((uint32_t)grid), block, 0, s, a);
   else
-    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, false, PIPE>), dim3((uint32_t)grid), block,
-                       0, s, a);
+    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, false>), dim3((uint32_t)grid), block, 0, s,
+                       a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+static hipError_t launch_tail(bool k_tail, const GemmArgs& a, int grid, float* partials, uint32_t* counters,
+                              int force_split, hipStream_t s) {
+  const dim3 block(WM * WN * 64);
+  if (k_tail)
+    hipLaunchKernelGGL((gg_tail_kernel<BM, BN, BK, WM, WN, STAGES, true>), dim3((uint32_t)grid), block, 0, s, a,
+                       partials, counters, force_split);
+  else
+    hipLaunchKernelGGL((gg_tail_kernel<BM, BN, BK, WM, WN, STAGES, false>), dim3((uint32_t)grid), block, 0, s, a,
+                       partials, counters, force_split);
   return hipGetLastError();
 }
 
@@ -919,7 +1320,8 @@ static hipError_t launch_skinny(bool k_tail, const GemmArgs& a, int64_t grid, hi
   return hipGetLastError();
 }
 
-// One case per row of kConfigs (same order).
+// One case per row of kConfigs (same order).  Split-tail rows (16, 17) go through
+// launch_gemm_tail; without a workspace the caller launches their twin here.
 template <int LAYOUT>
 static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
   switch (config_id) {
@@ -934,12 +1336,20 @@ static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, i
     case 8: return launch_lds<LAYOUT, 256, 128, 128, 2, 4, 3>(k_tail, a, grid, s);
     case 9: return launch_lds<LAYOUT, 128, 256, 128, 2, 4, 3>(k_tail, a, grid, s);
     case 10: return launch_lds<LAYOUT, 128, 128, 128, 2, 2, 4>(k_tail, a, grid, s);
-    case 11: return launch_lds<LAYOUT, 256, 256, 64, 2, 4, 4, true>(k_tail, a, grid, s);
-    case 12: return launch_lds<LAYOUT, 256, 128, 128, 2, 2, 3>(k_tail, a, grid, s);
-    case 13: return launch_lds<LAYOUT, 128, 128, 64, 2, 2, 4>(k_tail, a, grid, s);
-    case 14: return launch_skinny<LAYOUT, 32, 8>(k_tail, a, grid, s);
-    case 15: return launch_skinny<LAYOUT, 64, 8>(k_tail, a, grid, s);
-    case 16: return launch_skinny<LAYOUT, 32, 4>(k_tail, a, grid, s);
+    case 11: return launch_lds<LAYOUT, 256, 128, 128, 2, 2, 3>(k_tail, a, grid, s);
+    case 12: return launch_lds<LAYOUT, 128, 128, 64, 2, 2, 4>(k_tail, a, grid, s);
+    case 13: return launch_skinny<LAYOUT, 32, 8>(k_tail, a, grid, s);
+    case 14: return launch_skinny<LAYOUT, 64, 8>(k_tail, a, grid, s);
+    case 15: return launch_skinny<LAYOUT, 32, 4>(k_tail, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_tail(int config_id, bool k_tail, const GemmArgs& a, int grid, float* partials,
+                            uint32_t* counters, int force_split, hipStream_t s) {
+  switch (config_id) {
+    case 16: return launch_tail<256, 256, 128, 2, 4, 2>(k_tail, a, grid, partials, counters, force_split, s);
+    case 17: return launch_tail<128, 256, 128, 2, 4, 3>(k_tail, a, grid, partials, counters, force_split, s);
     default: return hipErrorInvalidValue;
   }
 }

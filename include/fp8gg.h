@@ -18,8 +18,19 @@
  *     (contiguous); there are no stride arguments.  The caller owns every buffer.
  *   - fp8 operands are raw e4m3fn bytes (uint8_t); Y is raw bf16 bits (uint16_t).
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is only
- *     enqueued: no entry point allocates device memory, copies between host and
- *     device, or synchronises, so every call may be captured into a HIP graph.
+ *     enqueued: no entry point copies between host and device or synchronises.
+ *     Every call may be captured into a HIP graph.
+ *   - Workspace: stacked calls with at least 128 rows per group (on average) run on
+ *     a persistent grid, one workgroup per compute unit, whose last partial wave of
+ *     output tiles is split along K; the pieces' fp32 partial sums go through a
+ *     workspace.  The library allocates it on the first such call on a given
+ *     stream (one partial tile per compute unit plus counters: 64 MB on MI355X)
+ *     and keeps it for the life of the process; calls on one stream share it (they
+ *     run in order), calls on different streams never do.  A call made while its
+ *     stream is being captured never allocates: if the stream has no workspace
+ *     yet, it runs the equivalent data-parallel kernel instead.  Either way the
+ *     results are deterministic: the partial sums of a split tile are added in a
+ *     fixed order.
  *   - Device-side metadata (M_sizes, zero_start_index_M) is never read by the host.
  *     The kernels clamp it (negative counts -> 0, cumulative row ends -> total_M,
  *     valid rows -> [0, expected_m]), so inconsistent metadata can never cause an
@@ -146,9 +157,12 @@ typedef struct {
   int32_t n_tail;     /* 1 if N % BN != 0 (the last N tile is masked)               */
   int64_t m_tiles;    /* stacked: upper bound of M tiles; padded: tiles per slab    */
   int64_t n_tiles;
-  int64_t grid;       /* workgroups launched by the GEMM kernel                     */
+  int64_t grid;       /* workgroups of the data-parallel schedule (one per tile)     */
   int32_t zero_fill;  /* 1 if the call zero-fills Y instead (K == 0)                */
   int32_t lds_bytes;  /* LDS per workgroup                                          */
+  int32_t split_tail; /* 1: persistent grid (one workgroup per compute unit) whose
+                         last partial wave is split along K; the grid above is then
+                         the tile count of the data-parallel schedule               */
 } fp8gg_plan;
 
 enum { FP8GG_LAYOUT_STACKED = 0, FP8GG_LAYOUT_PADDED = 1 };

@@ -99,3 +99,13 @@ def test_entry_points_refuse_before_any_gpu_call():
 
 def test_num_configs():
     assert _lib.load().f8f8bf16_num_configs() >= 1
+
+
+def test_every_configuration_fits_lds(monkeypatch):
+    """Each compiled configuration's LDS footprint fits a compute unit (160 KiB)."""
+    for cfg in range(_lib.load().f8f8bf16_num_configs()):
+        monkeypatch.setenv("FP8GG_CONFIG", str(cfg))
+        pre = cfg in (4, 5, 6)
+        p = F.plan(F.LAYOUT_STACKED, pre, 8, 4096, 4096, 7168)
+        assert p["config_id"] == cfg
+        assert 0 < p["lds_bytes"] <= 160 * 1024, (cfg, p["lds_bytes"])
