@@ -86,9 +86,12 @@ fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int6
 // Fixed selector (measured on MI355X; no benchmarking inside a call).  The key is
 // the rows one group contributes on average -- total_M normalised by G for the
 // stacked layout -- because a tile only ever sees one group.
+// Compute units the selector plans for (MI355X).  Only a heuristic: the persistent
+// grid itself is sized from the device at launch.
+constexpr int64_t kPlanCus = 256;
+
 int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
   (void)K;
-  (void)N;
   const int64_t per_group = layout == FP8GG_LAYOUT_STACKED ? (G > 0 ? (M + G - 1) / G : M) : M;
   if (preshuffled) {
     if (per_group >= 128) return 4;
@@ -96,14 +99,24 @@ int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, 
     return 6;
   }
   const bool stacked = layout == FP8GG_LAYOUT_STACKED;
-  if (per_group >= 512) return stacked ? 16 : 7;   // 256x256, K stage 128 (persistent, split tail when stacked)
+  if (per_group >= 512) {
+    if (stacked) return 16;   // 256x256, K stage 128, persistent with a split last wave
+    // Padded: 256x256 tiles unless they make fewer than two waves (padding tiles
+    // retire at once, so the busy ones are fewer still); then 128x256.
+    const int64_t tiles = G * ((M + 255) / 256) * ((N + 255) / 256);
+    return tiles >= 2 * kPlanCus ? 7 : 9;
+  }
   if (per_group >= 128) return 9;                  // 128x256, K stage 128
   if (per_group >= 48) return 2;
-  // At most one row per group on average: few groups hold rows, so spread each
-  // group's weights over many workgroups (32 columns each, K split over 4 waves).
+  // Small M: the weights stream from HBM once, so what matters is how many bytes
+  // each compute unit keeps in flight.  Fewer rows than groups: few groups hold
+  // rows, so each group's weights are spread over many workgroups (32 columns each,
+  // K split over 4 waves, straight to registers).  Otherwise 32-row tiles with a
+  // deep LDS pipeline: 32 x 64 for at most two rows per group, 32 x 128 above.
   const int64_t rows = stacked ? M : G * M;
-  if (rows <= G) return 15;
-  return 3;
+  if (rows < G) return 15;
+  if (per_group <= 2) return 21;
+  return 18;
 }
 
 // Compute units of the current device (the persistent grid), cached per device.

@@ -64,31 +64,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, l) | ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
 }
 
+// s_waitcnt immediate with only the vector-memory counter constrained to <= n
+// (gfx9 encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14; expcnt (bits
+// 6:4) and lgkmcnt (bits 11:8) left at their maxima).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
-  // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-  // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt bits 6:4, lgkmcnt 11:8).
+  // The instruction takes an immediate: a switch over the counts the kernels use
+  // (every count a compile-time constant folds to one instruction).
   switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
-    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
-    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
-    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
-    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
-    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
-    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
-    case 8: __builtin_amdgcn_s_waitcnt(0x0F78); break;
-    case 9: __builtin_amdgcn_s_waitcnt(0x0F79); break;
-    case 10: __builtin_amdgcn_s_waitcnt(0x0F7A); break;
-    case 11: __builtin_amdgcn_s_waitcnt(0x0F7B); break;
-    case 12: __builtin_amdgcn_s_waitcnt(0x0F7C); break;
-    case 13: __builtin_amdgcn_s_waitcnt(0x0F7D); break;
-    case 14: __builtin_amdgcn_s_waitcnt(0x0F7E); break;
-    case 15: __builtin_amdgcn_s_waitcnt(0x0F7F); break;
-    case 16: __builtin_amdgcn_s_waitcnt(0x4F70); break;
-    case 18: __builtin_amdgcn_s_waitcnt(0x4F72); break;
-    case 20: __builtin_amdgcn_s_waitcnt(0x4F74); break;
-    case 24: __builtin_amdgcn_s_waitcnt(0x4F78); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;  // anything else: wait for all
+#define FP8GG_WAIT_CASE(k) \
+  case k: __builtin_amdgcn_s_waitcnt(vmcnt_imm(k)); break;
+    FP8GG_WAIT_CASE(1) FP8GG_WAIT_CASE(2) FP8GG_WAIT_CASE(3) FP8GG_WAIT_CASE(4) FP8GG_WAIT_CASE(5)
+    FP8GG_WAIT_CASE(6) FP8GG_WAIT_CASE(7) FP8GG_WAIT_CASE(8) FP8GG_WAIT_CASE(9) FP8GG_WAIT_CASE(10)
+    FP8GG_WAIT_CASE(11) FP8GG_WAIT_CASE(12) FP8GG_WAIT_CASE(13) FP8GG_WAIT_CASE(14) FP8GG_WAIT_CASE(15)
+    FP8GG_WAIT_CASE(16) FP8GG_WAIT_CASE(18) FP8GG_WAIT_CASE(20) FP8GG_WAIT_CASE(24) FP8GG_WAIT_CASE(30)
+    FP8GG_WAIT_CASE(32) FP8GG_WAIT_CASE(36) FP8GG_WAIT_CASE(40) FP8GG_WAIT_CASE(42) FP8GG_WAIT_CASE(48)
+#undef FP8GG_WAIT_CASE
+    default: __builtin_amdgcn_s_waitcnt(vmcnt_imm(0)); break;  // 0, or a count not listed: wait for all
   }
 }
 
@@ -138,33 +131,57 @@ struct Tile {
   int64_t zero_end;   // rows [row_end, zero_end) are written as zero
 };
 
+// Counts of groups g0 .. g0+7 (indices past G read group G-1 and are ignored by the
+// callers).  A whole block of eight in bounds is read as one 64-byte struct, which
+// the compiler turns into a single scalar load.
+struct alignas(8) Counts8 {
+  int64_t v[8];
+};
+__device__ __forceinline__ void load_counts8(const int64_t* meta, int64_t g0, int64_t G, int64_t (&cnt)[8]) {
+  if (g0 + 8 <= G) {
+    const Counts8 c = *reinterpret_cast<const Counts8*>(meta + g0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt[i] = c.v[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) cnt[i] = meta[g0 + i < G ? g0 + i : G - 1];
+  }
+}
+
 // Stacked: walk the groups with a running row prefix and tile prefix.  Counts are
 // clamped (negative -> 0, cumulative end -> M), so any metadata stays in bounds.
-// The counts are fetched eight at a time so that a call pays one memory round trip
-// per eight groups rather than one per group before its first operand load.
+// Each block of eight counts is fetched, and its row ends and tile counts are
+// computed, before the search looks at any of them: a call pays one memory round
+// trip per eight groups before its first operand load (a search that could stop
+// early would let the compiler fetch the counts one by one, each behind a wait).
 template <int BM>
 __device__ __forceinline__ bool resolve_stacked(const GemmArgs& a, int64_t m_tile, Tile& t) {
   int64_t start = 0, tiles_before = 0;
   for (int64_t g0 = 0; g0 < a.G; g0 += 8) {
     int64_t cnt[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cnt[i] = a.meta[g0 + i < a.G ? g0 + i : a.G - 1];
+    load_counts8(a.meta, g0, a.G, cnt);
+    int64_t end[8], tiles[8];
+    int64_t s0 = start;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (g0 + i >= a.G) break;
-      int64_t s = cnt[i] < 0 ? 0 : cnt[i];
-      int64_t end = start + s;
-      end = end > a.M ? a.M : end;
-      const int64_t tiles = (end - start + BM - 1) / BM;
-      if (m_tile < tiles_before + tiles) {
+      const int64_t c = (g0 + i < a.G && cnt[i] > 0) ? cnt[i] : 0;
+      int64_t e = s0 + c;
+      e = e > a.M ? a.M : e;
+      tiles[i] = (e - s0 + BM - 1) / BM;
+      end[i] = e;
+      s0 = e;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (m_tile < tiles_before + tiles[i]) {
         t.g = g0 + i;
         t.row_base = start + (m_tile - tiles_before) * BM;
-        t.row_end = end;
-        t.zero_end = end;
+        t.row_end = end[i];
+        t.zero_end = end[i];
         return true;
       }
-      tiles_before += tiles;
-      start = end;
+      tiles_before += tiles[i];
+      start = end[i];
     }
   }
   return false;
@@ -625,13 +642,11 @@ __device__ __forceinline__ int64_t count_m_tiles(const GemmArgs& a) {
   int64_t start = 0, tiles = 0;
   for (int64_t g0 = 0; g0 < a.G; g0 += 8) {
     int64_t cnt[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) cnt[i] = a.meta[g0 + i < a.G ? g0 + i : a.G - 1];
+    load_counts8(a.meta, g0, a.G, cnt);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      if (g0 + i >= a.G) break;
-      const int64_t s = cnt[i] < 0 ? 0 : cnt[i];
-      int64_t end = start + s;
+      const int64_t c = (g0 + i < a.G && cnt[i] > 0) ? cnt[i] : 0;
+      int64_t end = start + c;
       end = end > a.M ? a.M : end;
       tiles += (end - start + BM - 1) / BM;
       start = end;
@@ -1278,6 +1293,13 @@ const KernelConfig kConfigs[] = {
     /* 15 */ {32, 32, 64, 1, 4, 0, 3, 4, 0},
     /* 16 */ {256, 256, 128, 2, 4, 2, 4, 0, 7},
     /* 17 */ {128, 256, 128, 2, 4, 3, 4, 0, 9},
+    /* 18 */ {32, 128, 128, 1, 4, 3, 0, 0, 0},
+    /* 19 */ {32, 128, 64, 1, 4, 4, 0, 0, 0},
+    /* 20 */ {32, 128, 128, 1, 4, 4, 0, 0, 0},
+    /* 21 */ {32, 64, 128, 1, 2, 4, 0, 0, 0},
+    /* 22 */ {32, 64, 128, 1, 2, 6, 0, 0, 0},
+    /* 23 */ {32, 128, 128, 1, 4, 6, 0, 0, 0},
+    /* 24 */ {32, 64, 128, 1, 2, 8, 0, 0, 0},
 };
 const int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1341,6 +1363,13 @@ static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, i
     case 13: return launch_skinny<LAYOUT, 32, 8>(k_tail, a, grid, s);
     case 14: return launch_skinny<LAYOUT, 64, 8>(k_tail, a, grid, s);
     case 15: return launch_skinny<LAYOUT, 32, 4>(k_tail, a, grid, s);
+    case 18: return launch_lds<LAYOUT, 32, 128, 128, 1, 4, 3>(k_tail, a, grid, s);
+    case 19: return launch_lds<LAYOUT, 32, 128, 64, 1, 4, 4>(k_tail, a, grid, s);
+    case 20: return launch_lds<LAYOUT, 32, 128, 128, 1, 4, 4>(k_tail, a, grid, s);
+    case 21: return launch_lds<LAYOUT, 32, 64, 128, 1, 2, 4>(k_tail, a, grid, s);
+    case 22: return launch_lds<LAYOUT, 32, 64, 128, 1, 2, 6>(k_tail, a, grid, s);
+    case 23: return launch_lds<LAYOUT, 32, 128, 128, 1, 4, 6>(k_tail, a, grid, s);
+    case 24: return launch_lds<LAYOUT, 32, 64, 128, 1, 2, 8>(k_tail, a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
