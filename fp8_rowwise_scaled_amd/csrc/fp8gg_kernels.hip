@@ -104,6 +104,14 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_base
                :: "v"(src), "s"(lds_base) : "memory");
 }
 
+// Same with the non-temporal hint, for data that one workgroup reads once (the
+// weights of a small-M call): it streams past the caches instead of displacing
+// what other workgroups reuse.
+__device__ __forceinline__ void copy16_to_lds_stream(const void* src, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+               :: "v"(src), "s"(lds_base) : "memory");
+}
+
 // Same, 4 bytes per lane: lane l's 4 bytes land at LDS byte lds_base + 4*l.
 __device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
@@ -244,6 +252,8 @@ struct LdsTile {
   static constexpr int STAGE_BYTES = (BM + BN) * BK;
   static constexpr int SMEM_BYTES = STAGES * STAGE_BYTES;
   static constexpr int ACC_FLOATS = FM * FN * 16;   // accumulator floats per thread
+  // 32-row tiles serve small M: every byte of W is read by one workgroup only.
+  static constexpr bool STREAM_W = BM <= 32;
   // Copies per thread per stage when every wave issues the same number (the
   // persistent kernel requires it).
   static constexpr int LOADS_PER_STAGE = A_LOADS + B_LOADS;
@@ -336,7 +346,8 @@ struct LdsTile {
       if (B_CHUNKS % NT == 0 || i * NT + wave * 64 < B_CHUNKS) {
         const uint8_t* src = b_src[i] + koff;
         if (last && koff + b_kc[i] >= K) src = g_zero16;
-        copy16_to_lds(src, lds_addr(sbase + A_BYTES + (i * NT + wave * 64) * 16));
+        if (STREAM_W) copy16_to_lds_stream(src, lds_addr(sbase + A_BYTES + (i * NT + wave * 64) * 16));
+        else copy16_to_lds(src, lds_addr(sbase + A_BYTES + (i * NT + wave * 64) * 16));
       }
     }
   }
