@@ -93,12 +93,19 @@ constexpr int64_t kPlanCus = 256;
 int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
   (void)K;
   const int64_t per_group = layout == FP8GG_LAYOUT_STACKED ? (G > 0 ? (M + G - 1) / G : M) : M;
+  const bool stacked = layout == FP8GG_LAYOUT_STACKED;
   if (preshuffled) {
+    // The same tiles as for plain W, reading pre-shuffled blocks.
+    if (per_group >= 512) {
+      if (stacked) return 26;
+      const int64_t tiles = G * ((M + 255) / 256) * ((N + 255) / 256);
+      return tiles >= 2 * kPlanCus ? 25 : 4;
+    }
     if (per_group >= 128) return 4;
     if (per_group >= 48) return 5;
+    if (per_group <= 2) return 27;
     return 6;
   }
-  const bool stacked = layout == FP8GG_LAYOUT_STACKED;
   if (per_group >= 512) {
     if (stacked) return 16;   // 256x256, K stage 128, persistent with a split last wave
     // Padded: 256x256 tiles unless they make fewer than two waves (padding tiles

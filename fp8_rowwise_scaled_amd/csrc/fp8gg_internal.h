@@ -31,19 +31,20 @@ struct KernelConfig {
   int BK;       // K bytes per pipeline stage (64 or 128: one or two 32x32x64 MFMA steps)
   int WM, WN;   // waves along M and N (threads = 64 * WM * WN)
   int stages;   // LDS pipeline depth (X and W; X only when W is pre-shuffled)
-  int kind;     // 0: X and W through LDS; 2: pre-shuffled W; 3: small M, W and X straight
-                // to registers with K split across waves; 4: kind 0 on a persistent grid
-                // whose last wave is split along K (stacked layout)
-  int wdepth;   // kinds 2, 3: K steps of fragments held in flight in registers
+  int kind;     // 0: X and W through LDS; 3: small M, W and X straight to registers with
+                // K split across waves; 4: kind 0 on a persistent grid whose last wave
+                // is split along K (stacked layout)
+  int wdepth;   // kind 3: K steps of fragments held in flight in registers
   int twin;     // kind 4: the kind-0 configuration with the same tile (used without workspace)
+  int pre;      // 1: W pre-shuffled by f8f8bf16_shuffle_b (the _preshuffle entry points)
 };
 
-enum { kKindLds = 0, kKindPreshuffled = 2, kKindSkinny = 3, kKindSplitTail = 4 };
+enum { kKindLds = 0, kKindSkinny = 3, kKindSplitTail = 4 };
 
 extern const KernelConfig kConfigs[];
 extern const int kNumConfigs;
 
-inline bool is_preshuffled(const KernelConfig& c) { return c.kind == kKindPreshuffled; }
+inline bool is_preshuffled(const KernelConfig& c) { return c.pre != 0; }
 
 // Split-tail workspace for a grid of P workgroups: P uint32 counters first (at a
 // fixed offset whatever the configuration, so a workspace shared by several
@@ -89,7 +90,6 @@ __host__ __device__ inline int tail_split(int64_t T, int64_t P, int64_t nk, int6
 
 inline int lds_bytes(const KernelConfig& c) {
   if (c.kind == kKindSkinny) return 3 * (c.BM / 32) * 16 * 64 * 4;
-  if (is_preshuffled(c)) return 2 * c.BM * c.BK;
   const int stages = c.stages * (c.BM + c.BN) * c.BK;
   // split tail: two scale blocks, a dummy word per lane and the finisher flag
   return c.kind == kKindSplitTail ? stages + 2 * (c.BM + c.BN) * 4 + 256 + 4 : stages;

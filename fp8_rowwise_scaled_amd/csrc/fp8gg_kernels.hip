@@ -235,7 +235,10 @@ __device__ __forceinline__ void zero_rect(uint16_t* Y, int64_t N, int64_t r0, in
 // workgroup; the split-tail kernel runs a sequence of whole tiles and a K piece per
 // persistent workgroup.
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL>
+// PRE: W comes pre-shuffled (f8f8bf16_shuffle_b's layout): each 32-row, 64-byte-K
+// block of W is 2048 contiguous bytes already in MFMA-operand order, so a stage's W
+// copy is a linear copy of whole blocks and its fragments read with no swizzle.
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PRE = false>
 struct LdsTile {
   static constexpr int NT = WM * WN * 64;
   static constexpr int CPR = BK / 16;          // 16-byte chunks per LDS row
@@ -265,6 +268,13 @@ struct LdsTile {
 
   typedef v16f Acc[FM][FN];
   typedef v4i Packed[FM][FN][2];   // bf16 outputs, eight columns per vector (see scale())
+
+  // First of the 16 consecutive tile columns that lane (h, r32) holds in block fn.
+  // Plain W rows are placed in LDS so that a lane's columns run on across blocks;
+  // pre-shuffled blocks are in MFMA order within each 32-column block.
+  __device__ __forceinline__ int col_of(int fn) const {
+    return wn * TN + (PRE ? 32 * fn + 16 * h : 16 * FN * h + 16 * fn);
+  }
 
   uint8_t* smem;
   int tid, lane, wave, wm, wn, h, r32;
@@ -307,6 +317,22 @@ struct LdsTile {
       a_src[i] = a.X + row * K + c * 16;
       a_kc[i] = c * 16;
     }
+    if constexpr (PRE) {
+      // A stage is BN/32 N blocks x KS K blocks of 2048 bytes, copied linearly:
+      // chunk q is byte 16*(q % 128) of stage block q / 128 = (N block j, K block ks).
+      const int64_t nbn = N / 32, nbk = K / 64;
+#pragma unroll
+      for (int i = 0; i < B_LOADS; ++i) {
+        const int q = i * NT + tid;
+        const int bq = (q / 128) % (BN / 32 * KS);
+        const int j = bq / KS, ks = bq % KS;
+        int64_t nb = n0 / 32 + j;
+        nb = nb < nbn ? nb : nbn - 1;                   // blocks past N: result dropped
+        b_src[i] = a.W + ((t.g * nbn + nb) * nbk + ks) * 2048 + (q % 128) * 16;
+        b_kc[i] = ks * 64;
+      }
+      return;
+    }
     const uint8_t* Wg = a.W + t.g * N * K;
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
@@ -341,10 +367,11 @@ struct LdsTile {
         copy16_to_lds(src, lds_addr(sbase + (i * NT + wave * 64) * 16));
       }
     }
+    const int64_t bkoff = PRE ? (int64_t)kt * KS * 2048 : koff;   // pre-shuffled: KS blocks per stage
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       if (B_CHUNKS % NT == 0 || i * NT + wave * 64 < B_CHUNKS) {
-        const uint8_t* src = b_src[i] + koff;
+        const uint8_t* src = b_src[i] + bkoff;
         if (last && koff + b_kc[i] >= K) src = g_zero16;
         if (STREAM_W) copy16_to_lds_stream(src, lds_addr(sbase + A_BYTES + (i * NT + wave * 64) * 16));
         else copy16_to_lds(src, lds_addr(sbase + A_BYTES + (i * NT + wave * 64) * 16));
@@ -370,10 +397,19 @@ struct LdsTile {
       }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
-        const int p = wn * TN + 32 * fn + r32;
-        const int sw = lds_swz<BK>(p);
-        const v4i lo = *(const v4i*)(sB + p * BK + (((4 * ks + 2 * h) ^ sw) * 16));
-        const v4i hi = *(const v4i*)(sB + p * BK + (((4 * ks + 2 * h + 1) ^ sw) * 16));
+        v4i lo, hi;
+        if constexpr (PRE) {
+          // Block layout: bytes 16*lane of the first 1024 hold the lane's first 16
+          // operand bytes, of the second 1024 its last 16.
+          const uint8_t* blk = sB + ((wn * FN + fn) * KS + ks) * 2048;
+          lo = *(const v4i*)(blk + lane * 16);
+          hi = *(const v4i*)(blk + 1024 + lane * 16);
+        } else {
+          const int p = wn * TN + 32 * fn + r32;
+          const int sw = lds_swz<BK>(p);
+          lo = *(const v4i*)(sB + p * BK + (((4 * ks + 2 * h) ^ sw) * 16));
+          hi = *(const v4i*)(sB + p * BK + (((4 * ks + 2 * h + 1) ^ sw) * 16));
+        }
         wf[ks][fn] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       }
     }
@@ -464,7 +500,6 @@ struct LdsTile {
 
   // scale() with the scales taken from an LDS block written by issue_scales.
   __device__ __forceinline__ void scale_lds(const Acc& acc, const float* sbuf, Packed& pk) const {
-    const float* wsl = sbuf + wn * TN + h * 16 * FN;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const float xsv = sbuf[BN + wm * TM + 32 * fm + r32];
@@ -472,8 +507,9 @@ struct LdsTile {
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
-          const v4f w0 = *(const v4f*)(wsl + 16 * fn + 8 * half);
-          const v4f w1 = *(const v4f*)(wsl + 16 * fn + 8 * half + 4);
+          const float* wl = sbuf + col_of(fn) + 8 * half;
+          const v4f w0 = *(const v4f*)(wl);
+          const v4f w1 = *(const v4f*)(wl + 4);
           const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
           uint32_t q[4];
 #pragma unroll
@@ -502,12 +538,11 @@ struct LdsTile {
   __device__ __forceinline__ void scale(const GemmArgs& a, const Tile& t, int64_t n0, const Acc& acc,
                                         Packed& pk) const {
     const int64_t N = a.N;
-    const int64_t col0 = n0 + wn * TN + h * 16 * FN;
     const float* wsg = a.ws + t.g * N;
     float wsv[16 * FN];
 #pragma unroll
     for (int v = 0; v < 4 * FN; ++v) {
-      const int64_t c = col0 + 4 * v;
+      const int64_t c = n0 + col_of(v / 4) + 4 * (v % 4);
       v4f w4 = {0.f, 0.f, 0.f, 0.f};
       if (c < N) w4 = *(const v4f*)(wsg + c);
       wsv[4 * v + 0] = w4.x;
@@ -537,7 +572,6 @@ struct LdsTile {
 
   __device__ __forceinline__ void store(const GemmArgs& a, const Tile& t, int64_t n0, const Packed& pk) const {
     const int64_t N = a.N;
-    const int64_t col0 = n0 + wn * TN + h * 16 * FN;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int64_t m = t.row_base + wm * TM + 32 * fm + r32;
@@ -545,14 +579,14 @@ struct LdsTile {
         uint16_t* yrow = a.Y + m * N;
 #pragma unroll
         for (int s = 0; s < 2 * FN; ++s) {           // 8 columns per 16-byte store
-          const int64_t c = col0 + 8 * s;
+          const int64_t c = n0 + col_of(s >> 1) + 8 * (s & 1);
           if (c < N) *(v4i*)(yrow + c) = pk[fm][s >> 1][s & 1];
         }
       } else if (m < t.zero_end) {
         uint16_t* yrow = a.Y + m * N;
 #pragma unroll
         for (int s = 0; s < 2 * FN; ++s) {
-          const int64_t c = col0 + 8 * s;
+          const int64_t c = n0 + col_of(s >> 1) + 8 * (s & 1);
           if (c < N) *(v4i*)(yrow + c) = v4i{0, 0, 0, 0};
         }
       }
@@ -610,10 +644,10 @@ struct LdsTile {
 };
 
 // Data-parallel kernel: one output tile per workgroup, whole K.
-template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL>
+template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PRE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gg_lds_kernel(GemmArgs a) {
-  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL> E;
+  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL, PRE> E;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
 
   const int64_t bid = blockIdx.x;
@@ -692,10 +726,10 @@ __device__ __forceinline__ int64_t count_m_tiles(const GemmArgs& a) {
 //
 // Workspace: counters [P] uint32 (zero between calls), then P slots of
 // E::ACC_FLOATS * E::NT floats.
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PRE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gg_tail_kernel(GemmArgs a, float* partials, uint32_t* counters, int force_split) {
-  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL> E;
+  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL, PRE> E;
   constexpr int64_t SLOT = (int64_t)E::ACC_FLOATS * E::NT;
   // Deferring a finished tile's stores by one stage keeps them out of the next
   // stage's wait; it needs the packed outputs live across one more MFMA step,
@@ -863,226 +897,40 @@ gg_tail_kernel(GemmArgs a, float* partials, uint32_t* counters, int force_split)
 }
 
 // ---------------------------------------------------------------------------
-// Pre-shuffled W: the grouped GEMM with W read straight into registers
+// Pre-shuffled W
 // ---------------------------------------------------------------------------
 //
 // Layout of the pre-shuffled weights (also declared with f8f8bf16_shuffle_b): for
 // group g, 32-row block nb and 64-byte K block kb, the 2048 bytes at
-// ((g * N/32 + nb) * K/64 + kb) * 2048 hold, at offset 32*l for lane l, the bytes
-// W[g, 32*nb + l % 32, 64*kb + 32*(l / 32) .. +32).  That is exactly the MFMA A
-// operand of one 32x32x64 step, so a wave fetches it with one contiguous 2 KB read
-// and W never passes through LDS.  X still goes global -> LDS (double-buffered) and
-// is shared by the waves of a workgroup, which all split N (one wave row).
-//
-// W fragments are prefetched WDEPTH K steps ahead into a register ring; the K loop
-// is unrolled by WDEPTH so that every ring slot is a compile-time register.
+// ((g * N/32 + nb) * K/64 + kb) * 2048 hold the MFMA A operand of one 32x32x64
+// step, lane l's 32 bytes split into halves: bytes [16*l, +16) and
+// [1024 + 16*l, +16) hold W[g, 32*nb + perm32(l % 32), 64*kb + 32*(l / 32) .. +16)
+// and the next 16 bytes, with perm32(r) = 16*((r >> 2) & 1) + 4*(r >> 3) + (r & 3).
+// A block is one contiguous 2 KB copy; its halves read back from LDS with no bank
+// conflicts; and perm32 puts W rows in MFMA order, so lane (h, r32) accumulates
+// the 16 consecutive output columns 32*nb + 16*h .. +16.  The K blocks of one
+// 32-row block follow each other, so a row block's K stream is contiguous.
+
+__device__ __forceinline__ int perm32(int r) { return 16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3); }
 
 __global__ void __launch_bounds__(256) shuffle_b_kernel(const v4i* __restrict__ W, v4i* __restrict__ Ws,
                                                         int64_t G, int64_t N, int64_t K) {
-  // One 16-byte output chunk per iteration: chunk o of block b is lane (o % 128) / 2,
-  // half o % 2 of the block's 2048 bytes.
+  // One 16-byte output chunk per iteration: chunk o of block blk is half
+  // (o % 128) / 64, lane o % 64 of the block's 2048 bytes.
   const int64_t nb_n = N / 32, nb_k = K / 64;
   const int64_t total = G * N * K / 16;
   for (int64_t o = (int64_t)blockIdx.x * 256 + threadIdx.x; o < total; o += (int64_t)gridDim.x * 256) {
     const int64_t blk = o / 128;
     const int within = (int)(o % 128);
-    const int lane = within >> 1;
-    const int half = within & 1;
+    const int half = within >> 6;
+    const int lane = within & 63;
     const int64_t kb = blk % nb_k;
     const int64_t gnb = blk / nb_k;         // g * N/32 + nb
     const int64_t g = gnb / nb_n;
     const int64_t nb = gnb % nb_n;
-    const int64_t row = nb * 32 + (lane & 31);
+    const int64_t row = nb * 32 + perm32(lane & 31);
     const int64_t col = kb * 64 + (lane >> 5) * 32 + half * 16;
     Ws[o] = W[((g * N + row) * K + col) / 16];
-  }
-}
-
-template <int LAYOUT, int BM, int BN, int WN, int WDEPTH>
-__global__ void __launch_bounds__(WN * 64)
-gg_pre_kernel(GemmArgs a) {
-  constexpr int NT = WN * 64;
-  constexpr int BK = 64;                // one MFMA K step per stage (the shuffle's K block)
-  constexpr int TN = BN / WN;           // wave tile along N
-  constexpr int FM = BM / 32;
-  constexpr int FN = TN / 32;
-  constexpr int A_CHUNKS = BM * BK / 16;
-  constexpr int A_LOADS = (A_CHUNKS + NT - 1) / NT;
-  constexpr int STAGE_BYTES = BM * BK;
-  static_assert(BM % 32 == 0 && TN % 32 == 0, "tiles must be multiples of 32");
-  static_assert(A_CHUNKS % 64 == 0, "tile rows must be a multiple of 16");
-
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[2 * STAGE_BYTES];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-
-  const int64_t bid = blockIdx.x;
-  const int64_t n_tile = bid % a.n_tiles;
-  const int64_t rest = bid / a.n_tiles;
-  Tile t;
-  if (LAYOUT == kStacked) {
-    if (!resolve_stacked<BM>(a, rest, t)) return;
-  } else {
-    if (!resolve_padded<BM>(a, rest / a.m_tiles, rest % a.m_tiles, t)) return;
-  }
-  const int64_t N = a.N;
-  const int64_t K = a.K;
-  const int64_t n0 = n_tile * BN;
-  const int64_t tile_row_end = t.row_base + BM;
-
-  if (t.row_base >= t.row_end) {
-    const int64_t r1 = tile_row_end < t.zero_end ? tile_row_end : t.zero_end;
-    const int64_t c1 = n0 + BN < N ? n0 + BN : N;
-    zero_rect<NT>(a.Y, N, t.row_base, r1, n0, c1);
-    return;
-  }
-
-  const uint8_t* a_src[A_LOADS];
-#pragma unroll
-  for (int i = 0; i < A_LOADS; ++i) {
-    const int q = i * NT + tid;
-    const int p = (q >> 2) % BM;
-    const int c = (q & 3) ^ lds_swz<64>(p);
-    int64_t row = t.row_base + p;
-    row = row < t.row_end ? row : t.row_end - 1;
-    a_src[i] = a.X + row * K + c * 16;
-  }
-  const int64_t nblk_n = N / 32;
-  const int64_t nblk_k = K / 64;
-  const uint8_t* w_src[FN];
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    int64_t nb = n0 / 32 + wn_block(wave, TN) + fn;
-    nb = nb < nblk_n ? nb : nblk_n - 1;            // blocks past N: result dropped
-    w_src[fn] = a.W + ((t.g * nblk_n + nb) * nblk_k) * 2048 + lane * 32;
-  }
-
-  const int nk = (int)(K / BK);
-  auto issue_x = [&](int kt) {
-    uint8_t* sbase = smem + (kt & 1) * STAGE_BYTES;
-    const int64_t koff = (int64_t)kt * BK;
-#pragma unroll
-    for (int i = 0; i < A_LOADS; ++i)
-      if (A_CHUNKS % NT == 0 || i * NT + wave * 64 < A_CHUNKS)
-        __builtin_amdgcn_global_load_lds((gbl_ptr_t)(a_src[i] + koff),
-                                         (lds_ptr_t)(sbase + (i * NT + wave * 64) * 16), 16, 0, 0);
-  };
-  auto load_w = [&](int kt, v8i (&dst)[FN]) {
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-      const v4i* p = (const v4i*)(w_src[fn] + (int64_t)kt * 2048);
-      const v4i lo = p[0];
-      const v4i hi = p[1];
-      dst[fn] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-    }
-  };
-
-  v16f acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = v16f{0};
-
-  v8i wr[WDEPTH][FN];
-#pragma unroll
-  for (int d = 0; d < WDEPTH; ++d)
-    if (d < nk) load_w(d, wr[d]);
-  asm volatile("" ::: "memory");
-  issue_x(0);
-
-  const int h = lane >> 5;
-  const int r32 = lane & 31;
-
-  for (int kt0 = 0; kt0 < nk; kt0 += WDEPTH) {
-#pragma unroll
-    for (int d = 0; d < WDEPTH; ++d) {
-      const int kt = kt0 + d;
-      if (kt < nk) {
-        // X(kt) was the last copy issued before the W loads of step kt-1+WDEPTH.
-        if (kt == 0) wait_vmcnt_le(0);
-        else wait_vmcnt_le(kt - 1 + WDEPTH < nk ? 2 * FN : 0);
-        block_barrier();
-        if (kt + 1 < nk) issue_x(kt + 1);
-        asm volatile("" ::: "memory");
-        const uint8_t* sA = smem + (kt & 1) * STAGE_BYTES;
-        v8i xf[FM];
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm) {
-          const int p = 32 * fm + r32;
-          const int sw = lds_swz<64>(p);
-          const v4i lo = *(const v4i*)(sA + p * 64 + (((2 * h) ^ sw) * 16));
-          const v4i hi = *(const v4i*)(sA + p * 64 + (((2 * h + 1) ^ sw) * 16));
-          xf[fm] = v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
-        }
-#pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wr[d][fn], xf[fm], acc[fm][fn]);
-        if (kt + WDEPTH < nk) load_w(kt + WDEPTH, wr[d]);
-      }
-    }
-  }
-
-  // ---- epilogue ----
-  // MFMA row rho of block fn is column n0 + wave*TN + 32*fn + rho; lane (h, r32) slot
-  // i = 4*j + tt holds rho = 8*j + 4*h + tt.  After scaling and packing, lanes h and
-  // h+32 trade j-groups with permlane32_swap so that each lane owns 8 consecutive
-  // columns per (fn, pair of j) and stores 16 bytes.
-  const int64_t cw = n0 + (int64_t)wave * TN;
-  const float* wsg = a.ws + t.g * N;
-  float wsv[FN][4][4];
-#pragma unroll
-  for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t c = cw + 32 * fn + 8 * j + 4 * h;
-      v4f w4 = {0.f, 0.f, 0.f, 0.f};
-      if (c < N) w4 = *(const v4f*)(wsg + c);
-      wsv[fn][j][0] = w4.x;
-      wsv[fn][j][1] = w4.y;
-      wsv[fn][j][2] = w4.z;
-      wsv[fn][j][3] = w4.w;
-    }
-#pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int64_t m = t.row_base + 32 * fm + r32;
-    const bool write = m < t.row_end;
-    const bool zero = !write && m < t.zero_end;
-    const float xsv = write ? a.xs[m] : 0.f;
-    uint16_t* yrow = a.Y + m * N;
-#pragma unroll
-    for (int fn = 0; fn < FN; ++fn) {
-#pragma unroll
-      for (int jp = 0; jp < 2; ++jp) {          // j pairs (0,1) and (2,3)
-        uint32_t e[2][2];                         // [j parity][packed pair]
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const int j = 2 * jp + jj;
-#pragma unroll
-          for (int pr = 0; pr < 2; ++pr) {
-            const float v0 = (acc[fm][fn][4 * j + 2 * pr] * xsv) * wsv[fn][j][2 * pr];
-            const float v1 = (acc[fm][fn][4 * j + 2 * pr + 1] * xsv) * wsv[fn][j][2 * pr + 1];
-            e[jj][pr] = pack_bf16x2(v0, v1);
-          }
-        }
-        // lanes < 32 keep j even and take the partner's j even; lanes >= 32 keep j odd
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-          const auto sw = __builtin_amdgcn_permlane32_swap(e[0][pr], e[1][pr], false, false);
-          e[0][pr] = sw[0];
-          e[1][pr] = sw[1];
-        }
-        const int64_t c = cw + 32 * fn + 16 * jp + 8 * h;
-        if (c < N) {
-          if (write)
-            *(v4i*)(yrow + c) = v4i{(int)e[0][0], (int)e[0][1], (int)e[1][0], (int)e[1][1]};
-          else if (zero)
-            *(v4i*)(yrow + c) = v4i{0, 0, 0, 0};
-        }
-      }
-    }
   }
 }
 
@@ -1281,18 +1129,18 @@ __global__ void __launch_bounds__(256) zero_fill_kernel(v4i* __restrict__ y, int
 // ---------------------------------------------------------------------------
 
 // kind: 0 = both operands through LDS (one tile per workgroup),
-//       2 = pre-shuffled W straight to registers (X through LDS),
 //       3 = small M: W and X straight to registers, K split across the 4 waves,
 //       4 = kind 0 on a persistent grid with a split last wave (stacked layout).
-//                      BM   BN   BK  WM WN stages kind wdepth twin
+// pre: 1 = W pre-shuffled (the _preshuffle entry points), 0 = plain W.
+//                      BM   BN   BK  WM WN stages kind wdepth twin pre
 const KernelConfig kConfigs[] = {
     /* 0 */ {256, 256, 64, 2, 4, 4, 0, 0, 0},
     /* 1 */ {128, 256, 64, 2, 4, 4, 0, 0, 0},
     /* 2 */ {64, 256, 64, 1, 4, 2, 0, 0, 0},
     /* 3 */ {32, 128, 64, 1, 4, 2, 0, 0, 0},
-    /* 4 */ {128, 256, 64, 1, 4, 2, 2, 2, 0},
-    /* 5 */ {64, 256, 64, 1, 4, 2, 2, 4, 0},
-    /* 6 */ {32, 128, 64, 1, 4, 2, 2, 4, 0},
+    /* 4 */ {128, 256, 128, 2, 4, 3, 0, 0, 0, 1},
+    /* 5 */ {64, 256, 128, 1, 4, 2, 0, 0, 0, 1},
+    /* 6 */ {32, 128, 128, 1, 4, 3, 0, 0, 0, 1},
     /* 7 */ {256, 256, 128, 2, 4, 2, 0, 0, 0},
     /* 8 */ {256, 128, 128, 2, 4, 3, 0, 0, 0},
     /* 9 */ {128, 256, 128, 2, 4, 3, 0, 0, 0},
@@ -1311,36 +1159,34 @@ const KernelConfig kConfigs[] = {
     /* 22 */ {32, 64, 128, 1, 2, 6, 0, 0, 0},
     /* 23 */ {32, 128, 128, 1, 4, 6, 0, 0, 0},
     /* 24 */ {32, 64, 128, 1, 2, 8, 0, 0, 0},
+    /* 25 */ {256, 256, 128, 2, 4, 2, 0, 0, 0, 1},
+    /* 26 */ {256, 256, 128, 2, 4, 2, 4, 0, 25, 1},
+    /* 27 */ {32, 64, 128, 1, 2, 4, 0, 0, 0, 1},
 };
 const int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
-template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES>
+template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool PRE = false>
 static hipError_t launch_lds(bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
   const dim3 block(WM * WN * 64);
   if (k_tail)
-    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, true>), dim3((uint32_t)grid), block, 0, s, a);
+    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, true, PRE>), dim3((uint32_t)grid), block,
+                       0, s, a);
   else
-    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, false>), dim3((uint32_t)grid), block, 0, s,
-                       a);
+    hipLaunchKernelGGL((gg_lds_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, false, PRE>), dim3((uint32_t)grid), block,
+                       0, s, a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool PRE = false>
 static hipError_t launch_tail(bool k_tail, const GemmArgs& a, int grid, float* partials, uint32_t* counters,
                               int force_split, hipStream_t s) {
   const dim3 block(WM * WN * 64);
   if (k_tail)
-    hipLaunchKernelGGL((gg_tail_kernel<BM, BN, BK, WM, WN, STAGES, true>), dim3((uint32_t)grid), block, 0, s, a,
+    hipLaunchKernelGGL((gg_tail_kernel<BM, BN, BK, WM, WN, STAGES, true, PRE>), dim3((uint32_t)grid), block, 0, s, a,
                        partials, counters, force_split);
   else
-    hipLaunchKernelGGL((gg_tail_kernel<BM, BN, BK, WM, WN, STAGES, false>), dim3((uint32_t)grid), block, 0, s, a,
-                       partials, counters, force_split);
-  return hipGetLastError();
-}
-
-template <int LAYOUT, int BM, int BN, int WN, int WDEPTH>
-static hipError_t launch_pre(const GemmArgs& a, int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL((gg_pre_kernel<LAYOUT, BM, BN, WN, WDEPTH>), dim3((uint32_t)grid), dim3(WN * 64), 0, s, a);
+    hipLaunchKernelGGL((gg_tail_kernel<BM, BN, BK, WM, WN, STAGES, false, PRE>), dim3((uint32_t)grid), block, 0, s,
+                       a, partials, counters, force_split);
   return hipGetLastError();
 }
 
@@ -1362,9 +1208,9 @@ static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, i
     case 1: return launch_lds<LAYOUT, 128, 256, 64, 2, 4, 4>(k_tail, a, grid, s);
     case 2: return launch_lds<LAYOUT, 64, 256, 64, 1, 4, 2>(k_tail, a, grid, s);
     case 3: return launch_lds<LAYOUT, 32, 128, 64, 1, 4, 2>(k_tail, a, grid, s);
-    case 4: return launch_pre<LAYOUT, 128, 256, 4, 2>(a, grid, s);
-    case 5: return launch_pre<LAYOUT, 64, 256, 4, 4>(a, grid, s);
-    case 6: return launch_pre<LAYOUT, 32, 128, 4, 4>(a, grid, s);
+    case 4: return launch_lds<LAYOUT, 128, 256, 128, 2, 4, 3, true>(k_tail, a, grid, s);
+    case 5: return launch_lds<LAYOUT, 64, 256, 128, 1, 4, 2, true>(k_tail, a, grid, s);
+    case 6: return launch_lds<LAYOUT, 32, 128, 128, 1, 4, 3, true>(k_tail, a, grid, s);
     case 7: return launch_lds<LAYOUT, 256, 256, 128, 2, 4, 2>(k_tail, a, grid, s);
     case 8: return launch_lds<LAYOUT, 256, 128, 128, 2, 4, 3>(k_tail, a, grid, s);
     case 9: return launch_lds<LAYOUT, 128, 256, 128, 2, 4, 3>(k_tail, a, grid, s);
@@ -1381,6 +1227,8 @@ static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, i
     case 22: return launch_lds<LAYOUT, 32, 64, 128, 1, 2, 6>(k_tail, a, grid, s);
     case 23: return launch_lds<LAYOUT, 32, 128, 128, 1, 4, 6>(k_tail, a, grid, s);
     case 24: return launch_lds<LAYOUT, 32, 64, 128, 1, 2, 8>(k_tail, a, grid, s);
+    case 25: return launch_lds<LAYOUT, 256, 256, 128, 2, 4, 2, true>(k_tail, a, grid, s);
+    case 27: return launch_lds<LAYOUT, 32, 64, 128, 1, 2, 4, true>(k_tail, a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1390,6 +1238,7 @@ hipError_t launch_gemm_tail(int config_id, bool k_tail, const GemmArgs& a, int g
   switch (config_id) {
     case 16: return launch_tail<256, 256, 128, 2, 4, 2>(k_tail, a, grid, partials, counters, force_split, s);
     case 17: return launch_tail<128, 256, 128, 2, 4, 3>(k_tail, a, grid, partials, counters, force_split, s);
+    case 26: return launch_tail<256, 256, 128, 2, 4, 2, true>(k_tail, a, grid, partials, counters, force_split, s);
     default: return hipErrorInvalidValue;
   }
 }

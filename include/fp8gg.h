@@ -134,8 +134,9 @@ fp8gg_status f8f8bf16_rowwise_grouped_dynamic_preshuffle(
  * overlap WQ).  Byte layout: for group g, N-block nb (FP8GG_SHUFFLE_N rows) and
  * K-block kb (FP8GG_SHUFFLE_K bytes), the 2048-byte block at
  *     ((g * N/32 + nb) * K/64 + kb) * 2048
- * holds, for lane l in [0, 64), the 32 bytes WQ[g, nb*32 + (l % 32),
- * kb*64 + (l / 32)*32 .. +32) at offset l*32.  Same shape rules as the
+ * holds, for lane l in [0, 64) and half h in {0, 1}, at offset h*1024 + l*16, the
+ * 16 bytes WQ[g, nb*32 + perm32(l % 32), kb*64 + (l / 32)*32 + h*16 .. +16), with
+ * perm32(r) = 16*((r >> 2) & 1) + 4*(r >> 3) + (r & 3).  Same shape rules as the
  * preshuffled GEMMs.
  */
 fp8gg_status f8f8bf16_shuffle_b(const uint8_t* WQ, uint8_t* WQs,

@@ -284,10 +284,14 @@ def test_refusals_raise(F):
 
 def shuffle_reference(WQ: np.ndarray) -> np.ndarray:
     """The pre-shuffled byte order stated in include/fp8gg.h, written with numpy:
-    block (g, nb, kb) of 2048 bytes holds, at 32*l, W[g, 32nb + l%32, 64kb + 32(l/32) .. +32)."""
+    block (g, nb, kb) of 2048 bytes holds, at h*1024 + 16*l, the 16 bytes
+    W[g, 32nb + perm32(l%32), 64kb + 32(l/32) + 16h .. +16)."""
     G, N, K = WQ.shape
-    v = WQ.reshape(G, N // 32, 32, K // 64, 2, 32)          # g, nb, r, kb, half, byte
-    v = v.transpose(0, 1, 3, 4, 2, 5)                        # g, nb, kb, half, r, byte  (lane = half*32 + r)
+    perm = np.array([16 * ((r >> 2) & 1) + 4 * (r >> 3) + (r & 3) for r in range(32)])
+    assert sorted(perm) == list(range(32))
+    v = WQ.reshape(G, N // 32, 32, K // 64, 2, 2, 16)      # g, nb, row, kb, l/32, h, byte
+    v = v[:, :, perm]                                       # row slot r' holds row perm32(r')
+    v = v.transpose(0, 1, 3, 5, 4, 2, 6)                    # g, nb, kb, h, l/32, r', byte
     return np.ascontiguousarray(v).reshape(G, N, K)
 
 

@@ -185,6 +185,35 @@ def test_other_grid_sizes(F, env, grid):
     P.assert_rows_match(got, ref, label=f"grid {grid}")
 
 
+@pytest.mark.parametrize("split", [None, 3])
+def test_preshuffled_persistent_kernel(F, env, split):
+    """The persistent kernel on pre-shuffled weights (configuration 26), whole and
+    split tiles, against the oracle and bitwise against its data-parallel twin when
+    unsplit."""
+    sizes, N = tail_shape(256, 256, extra_tiles=37)
+    w, ref = case(sizes, N, 2048, seed=1426)
+    print(f"case preshuffled persistent sizes={sizes} split={split}", flush=True)
+    args = [P.dev(a) for a in (w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)]
+    args[1] = F.f8f8bf16_shuffle_b(args[1])
+
+    def run_pre():
+        whole, out = P.guarded_output((w.total_M, w.N))
+        F.f8f8bf16_rowwise_grouped_stacked_preshuffle(*args, out=out)
+        torch.cuda.synchronize()
+        P.check_guards(whole)
+        return P.bits_of(out)
+
+    env(config=26, tail_split=split)
+    got = run_pre()
+    P.assert_rows_match(got, ref, label=f"preshuffled persistent split={split}")
+    assert np.array_equal(run_pre(), got)
+    if split is None:
+        env(config=26, tail_split=1)
+        unsplit = run_pre()
+        env(config=25, tail_split=None)
+        assert np.array_equal(unsplit, run_pre())
+
+
 def test_split_tail_on_a_second_stream(F, env):
     BM, BN, _ = TAIL_CONFIGS[17]
     sizes, N = tail_shape(BM, BN, extra_tiles=5)

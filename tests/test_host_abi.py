@@ -105,7 +105,9 @@ def test_every_configuration_fits_lds(monkeypatch):
     """Each compiled configuration's LDS footprint fits a compute unit (160 KiB)."""
     for cfg in range(_lib.load().f8f8bf16_num_configs()):
         monkeypatch.setenv("FP8GG_CONFIG", str(cfg))
-        pre = cfg in (4, 5, 6)
-        p = F.plan(F.LAYOUT_STACKED, pre, 8, 4096, 4096, 7168)
+        try:                                  # a configuration serves plain or pre-shuffled W
+            p = F.plan(F.LAYOUT_STACKED, False, 8, 4096, 4096, 7168)
+        except ValueError:
+            p = F.plan(F.LAYOUT_STACKED, True, 8, 4096, 4096, 7168)
         assert p["config_id"] == cfg
         assert 0 < p["lds_bytes"] <= 160 * 1024, (cfg, p["lds_bytes"])
