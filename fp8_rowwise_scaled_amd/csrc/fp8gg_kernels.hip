@@ -943,8 +943,9 @@ __global__ void __launch_bounds__(256) shuffle_b_kernel(const v4i* __restrict__ 
 // of X), with the four waves of a workgroup splitting K.  Each wave keeps D MFMA
 // steps of W and X fragments in flight in a register ring (W rows are read in the
 // MFMA A-operand layout directly from the row-major weights; X rows come from L2).
-// The four partial sums are added through LDS in a fixed order (deterministic),
-// then the epilogue is the pre-shuffled kernel's (permlane32_swap, 16-byte stores).
+// The four partial sums are added through LDS in a fixed order (deterministic).
+// A lane's accumulators are then 4-column runs of natural-order W rows; the
+// epilogue pairs lanes 32 apart with permlane32_swap to form 16-byte stores.
 
 template <int LAYOUT, int BM, int D, bool KTAIL>
 __global__ void __launch_bounds__(256)
