@@ -59,12 +59,13 @@ constexpr int kMaxTailSplit = 16;
 // Number of K pieces for each tile of the last, partial wave of a persistent grid
 // of P workgroups over T tiles of nk K stages (1: no split).  With rem = T % P
 // tiles left over, s pieces per tile need rem * s <= P workgroups and at least one
-// stage each.  Cost of the last wave, in tenths of a stage time (measured on
-// MI355X with the 128 x 256 tile, the partial tile about 2.7 stages of bytes):
-//   unsplit:  8 * nk                 (a wave with few busy compute units streams
-//                                     each stage about 1.4x faster)
-//   split:   11 * ceil(nk / s)       (longest piece, all compute units busy)
-//          + (26 + 8 * s) * r        (partial write and L2 write-back fence, then
+// stage each.  Cost of the last wave, in tenths of a stage time (fitted on MI355X
+// to device timestamps of the 128 x 256 tile and to gate_up's 256 x 256 tail timed
+// at s = 1, 3, 4, 5):
+//   unsplit:  10 * nk                (few busy compute units stream faster, but
+//                                     the whole K loop is on the critical path)
+//   split:    11 * ceil(nk / s)      (longest piece, all compute units busy)
+//          + (26 + 16 * s) * r       (partial write and L2 write-back fence, then
 //                                     the finisher's reload of s partials),
 // r = partial bytes / stage bytes.  force > 0 requests a split factor instead,
 // clamped to what the shape allows.
@@ -77,9 +78,9 @@ __host__ __device__ inline int tail_split(int64_t T, int64_t P, int64_t nk, int6
   if (smax > kMaxTailSplit) smax = kMaxTailSplit;
   if (force > 0) return (int)(force < smax ? force : smax);
   int best = 1;
-  int64_t best_cost = 8 * nk * stage_bytes;
+  int64_t best_cost = 10 * nk * stage_bytes;
   for (int s = 2; s <= smax; ++s) {
-    const int64_t cost = 11 * ((nk + s - 1) / s) * stage_bytes + (26 + 8 * (int64_t)s) * partial_bytes;
+    const int64_t cost = 11 * ((nk + s - 1) / s) * stage_bytes + (26 + 16 * (int64_t)s) * partial_bytes;
     if (cost < best_cost) {
       best = s;
       best_cost = cost;

@@ -602,8 +602,8 @@ struct LdsTile {
   // Accumulators <-> a partial-sum slot of ACC_FLOATS * NT floats.  Quad q of the
   // accumulator registers (floats 4q .. 4q+3) of all NT threads is NT consecutive
   // 16-byte vectors, so every access is a coalesced 16-byte-per-lane vector access.
-  // Loads go one 16-float block at a time (the empty asm keeps the compiler from
-  // hoisting every block's loads ahead of the additions, which would need a second
+  // Loads go a batch of blocks at a time (the empty asm keeps the compiler from
+  // hoisting every batch's loads ahead of the additions, which would need a second
   // accumulator's worth of registers).
   __device__ __forceinline__ v4f* quad(float* slot, int blk, int q) const {
     return reinterpret_cast<v4f*>(slot) + (int64_t)(blk * 4 + q) * NT + tid;
@@ -624,20 +624,29 @@ struct LdsTile {
   }
   template <bool ADD>
   __device__ __forceinline__ void gather_partial(const float* slot, Acc& acc) const {
+    // GROUP blocks of 16 floats per batch: 4 * GROUP 16-byte loads in flight per
+    // thread (a finisher reloads several partial tiles and is otherwise latency-bound).
+    constexpr int BLOCKS = FM * FN;
+    constexpr int GROUP = BLOCKS < 4 ? BLOCKS : 4;
+    static_assert(BLOCKS % GROUP == 0, "partial blocks come in whole batches");
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int b0 = 0; b0 < BLOCKS; b0 += GROUP) {
+      v4f v[GROUP][4];
 #pragma unroll
-      for (int fn = 0; fn < FN; ++fn) {
-        v4f v[4];
+      for (int g = 0; g < GROUP; ++g)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) v[q] = *quad(slot, fm * FN + fn, q);
+        for (int q = 0; q < 4; ++q) v[g][q] = *quad(slot, b0 + g, q);
+#pragma unroll
+      for (int g = 0; g < GROUP; ++g) {
+        const int fm = (b0 + g) / FN, fn = (b0 + g) % FN;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int j = 0; j < 4; ++j)
-            acc[fm][fn][4 * q + j] = ADD ? acc[fm][fn][4 * q + j] + v[q][j] : v[q][j];
-        asm volatile("" ::: "memory");
+            acc[fm][fn][4 * q + j] = ADD ? acc[fm][fn][4 * q + j] + v[g][q][j] : v[g][q][j];
       }
+      asm volatile("" ::: "memory");
+    }
   }
   __device__ __forceinline__ void load_partial(const float* slot, Acc& acc) const { gather_partial<false>(slot, acc); }
   __device__ __forceinline__ void add_partial(const float* slot, Acc& acc) const { gather_partial<true>(slot, acc); }
