@@ -48,8 +48,6 @@ def build(verbose: bool = False, extra: list[str] | None = None) -> str:
     def compile_one(pair):
         src, obj = pair
         cmd = [hipcc, *COMMON, *(extra or []), "-c", src, "-o", obj]
-        if src.endswith(".cpp"):
-            cmd[1:1] = ["-x", "hip"] if False else []
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = "\n".join(l for l in (r.stdout + r.stderr).splitlines()
                         if "packed-fp32-ops" not in l)

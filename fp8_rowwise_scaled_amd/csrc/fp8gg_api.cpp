@@ -80,6 +80,14 @@ fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int6
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "a dimension exceeds 2^31-256");
   if (layout == FP8GG_LAYOUT_PADDED && G * M > lim)
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "G*expected_m exceeds 2^31-256");
+  // Every tensor's byte count (and so every 64-bit offset the kernels form) stays
+  // far below overflow; 2^48 bytes is beyond any device memory.
+  const int64_t rows = layout == FP8GG_LAYOUT_STACKED ? M : G * M;
+  const int64_t cap = int64_t(1) << 48;
+  auto too_big = [cap](int64_t a, int64_t b) { return a > 0 && b > cap / a; };
+  if (too_big(rows, K) || too_big(G, N) || (G * N > 0 && too_big(G * N, K)) || too_big(rows, 2 * N))
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "a tensor would exceed 2^48 bytes (G=%lld M=%lld N=%lld K=%lld)",
+                (long long)G, (long long)M, (long long)N, (long long)K);
   return FP8GG_OK;
 }
 
@@ -143,28 +151,25 @@ int device_cus() {
 
 // Split-tail workspace, one per (device, stream): calls on one stream run in order,
 // so they can share it; calls on different streams never do.  Allocated on first
-// use outside graph capture and kept for the life of the process.  Counters are
-// zeroed at allocation and every call leaves them zero.
+// use (never during graph capture: captured calls do not use it at all) and kept
+// for the life of the process.  Counters are zeroed at allocation and every call
+// leaves them zero.
 struct Workspace {
   void* base = nullptr;
   size_t bytes = 0;
 };
 
-fp8gg_status tail_workspace(hipStream_t stream, size_t need, Workspace* out, bool* available) {
+fp8gg_status tail_workspace(hipStream_t stream, size_t need, Workspace* out) {
   static std::mutex mu;
   static std::map<std::pair<int, hipStream_t>, Workspace> pool;
-  *available = false;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return fail(FP8GG_ERR_HIP, "hipGetDevice failed");
   std::lock_guard<std::mutex> lock(mu);
   Workspace& w = pool[std::make_pair(dev, stream)];
   if (w.base && w.bytes >= need) {
     *out = w;
-    *available = true;
     return FP8GG_OK;
   }
-  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-  if (hipStreamIsCapturing(stream, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return FP8GG_OK;
   if (w.base) {
     // Growing: the old buffer may still be in use by queued work on this stream.
     hipError_t e = hipStreamSynchronize(stream);
@@ -176,7 +181,7 @@ fp8gg_status tail_workspace(hipStream_t stream, size_t need, Workspace* out, boo
   void* p = nullptr;
   hipError_t e = hipMalloc(&p, need);
   if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "workspace allocation of %zu bytes: %s", need, hipGetErrorString(e));
-  e = hipMemset(p, 0, need);
+  e = hipMemsetAsync(p, 0, need, stream);   // ordered before this call's kernel (never captured)
   if (e != hipSuccess) {
     (void)hipFree(p);
     return fail(FP8GG_ERR_HIP, "workspace clear: %s", hipGetErrorString(e));
@@ -184,7 +189,6 @@ fp8gg_status tail_workspace(hipStream_t stream, size_t need, Workspace* out, boo
   w.base = p;
   w.bytes = need;
   *out = w;
-  *available = true;
   return FP8GG_OK;
 }
 
@@ -304,17 +308,29 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
     const int P = forced_grid > 0 ? forced_grid : device_cus();
     const int force_split = env_int("FP8GG_TAIL_SPLIT", 0);
     if (env_int("FP8GG_LOG", 0)) std::fprintf(stderr, "[fp8gg] persistent grid %d, forced split %d\n", P, force_split);
-    Workspace ws;
-    bool have = false;
-    st = tail_workspace(s, fp8gg::tail_workspace_bytes(cfg, P), &ws, &have);
-    if (st != FP8GG_OK) return st;
-    if (have) {
+    // A call captured into a graph runs the data-parallel twin instead: a graph then
+    // holds no library-owned memory and may be replayed on any stream, alongside
+    // eager calls that use this stream's workspace.
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    hipError_t ce = hipStreamIsCapturing(s, &cs);
+    if (ce != hipSuccess) return fail(FP8GG_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(ce));
+    if (cs != hipStreamCaptureStatusNone) {
+      e = fp8gg::launch_gemm(layout, cfg.twin, p.k_tail != 0, a, p.grid, s);
+    } else {
+      // Sized for the largest tile at this grid, so that switching configurations
+      // never has to grow (synchronise and reallocate) the workspace.
+      size_t need = fp8gg::tail_workspace_bytes(cfg, P);
+      for (int c = 0; c < fp8gg::kNumConfigs; ++c)
+        if (fp8gg::kConfigs[c].kind == fp8gg::kKindSplitTail) {
+          const size_t b = fp8gg::tail_workspace_bytes(fp8gg::kConfigs[c], P);
+          need = b > need ? b : need;
+        }
+      Workspace ws;
+      st = tail_workspace(s, need, &ws);
+      if (st != FP8GG_OK) return st;
       uint32_t* counters = static_cast<uint32_t*>(ws.base);
       float* partials = reinterpret_cast<float*>(static_cast<char*>(ws.base) + fp8gg::tail_counters_bytes(P));
       e = fp8gg::launch_gemm_tail(p.config_id, p.k_tail != 0, a, P, partials, counters, force_split, s);
-    } else {
-      // Captured before any workspace existed on this stream: the data-parallel twin.
-      e = fp8gg::launch_gemm(layout, cfg.twin, p.k_tail != 0, a, p.grid, s);
     }
   } else {
     e = fp8gg::launch_gemm(layout, p.config_id, p.k_tail != 0, a, p.grid, s);

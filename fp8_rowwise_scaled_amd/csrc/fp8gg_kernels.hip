@@ -94,14 +94,16 @@ template <int BK>
 __device__ __forceinline__ int lds_swz(int p) { return (p / (256 / BK)) & (BK / 16 - 1); }
 
 // One 16-byte-per-lane copy from global memory straight into LDS: lane l's 16 bytes
-// land at LDS byte lds_base + 16*l (lds_base wave-uniform).  Written as inline
+// land at LDS byte lds_base + 16*l.  lds_base is wave-uniform by construction; the
+// readfirstlane states it, so that it always reaches M0 through a scalar register
+// even where the compiler cannot prove the uniformity itself.  Written as inline
 // assembly so that the compiler's wait-count pass does not track it: the pass
 // cannot tell LDS slots apart when the slot index is a run-time value and would
 // otherwise drain every copy in flight before each LDS read.  The callers order
 // copies and reads themselves (wait_vmcnt_le, then a workgroup barrier).
 __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-               :: "v"(src), "s"(lds_base) : "memory");
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory");
 }
 
 // Same with the non-temporal hint, for data that one workgroup reads once (the
@@ -109,13 +111,13 @@ __device__ __forceinline__ void copy16_to_lds(const void* src, uint32_t lds_base
 // what other workgroups reuse.
 __device__ __forceinline__ void copy16_to_lds_stream(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
-               :: "v"(src), "s"(lds_base) : "memory");
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory");
 }
 
 // Same, 4 bytes per lane: lane l's 4 bytes land at LDS byte lds_base + 4*l.
 __device__ __forceinline__ void copy4_to_lds(const void* src, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
-               :: "v"(src), "s"(lds_base) : "memory");
+               :: "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base)) : "memory");
 }
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -207,9 +209,6 @@ __device__ __forceinline__ bool resolve_padded(const GemmArgs& a, int64_t g, int
   t.zero_end = a.zeroing ? slab + a.M : slab + valid;
   return t.row_base < t.zero_end;
 }
-
-// First 32-column block of wave w's slice when each wave covers TN columns.
-__device__ __forceinline__ int64_t wn_block(int w, int TN) { return (int64_t)w * (TN / 32); }
 
 // Writes zeros into rows [r0, r1) x columns [c0, c1) of Y (16-byte vectors).
 template <int NT>

@@ -20,21 +20,23 @@
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is only
  *     enqueued: no entry point copies between host and device or synchronises.
  *     Every call may be captured into a HIP graph.
- *   - Workspace: stacked calls with at least 128 rows per group (on average) run on
+ *   - Workspace: stacked calls with at least 512 rows per group (on average) run on
  *     a persistent grid, one workgroup per compute unit, whose last partial wave of
- *     output tiles is split along K; the pieces' fp32 partial sums go through a
+ *     output tiles may be split along K; the pieces' fp32 partial sums go through a
  *     workspace.  The library allocates it on the first such call on a given
  *     stream (one partial tile per compute unit plus counters: 64 MB on MI355X)
  *     and keeps it for the life of the process; calls on one stream share it (they
  *     run in order), calls on different streams never do.  A call made while its
- *     stream is being captured never allocates: if the stream has no workspace
- *     yet, it runs the equivalent data-parallel kernel instead.  Either way the
- *     results are deterministic: the partial sums of a split tile are added in a
- *     fixed order.
+ *     stream is being captured never touches the workspace: it runs the equivalent
+ *     data-parallel kernel, so a graph holds no library-owned memory and may be
+ *     replayed on any stream.  Either way the results are deterministic: the
+ *     partial sums of a split tile are added in a fixed order.
  *   - Device-side metadata (M_sizes, zero_start_index_M) is never read by the host.
  *     The kernels clamp it (negative counts -> 0, cumulative row ends -> total_M,
  *     valid rows -> [0, expected_m]), so inconsistent metadata can never cause an
  *     out-of-bounds access; the values computed for it are then unspecified.
+ *   - Size limits: every dimension (and G * expected_m) below 2^31 - 256, every
+ *     tensor below 2^48 bytes (FP8GG_ERR_UNSUPPORTED_SHAPE otherwise).
  *   - Shape rules: K % 16 == 0 and N % 8 == 0 (a 16-byte load granule along K and
  *     an 8-column store granule along N; MSLK #471 commits on the K-tail and N-tail
  *     variants).  K need not be a multiple of the K tile, N not of the N tile.

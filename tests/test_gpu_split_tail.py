@@ -225,19 +225,27 @@ def test_split_tail_on_a_second_stream(F, env):
     assert np.array_equal(a, b)
 
 
-def test_split_tail_under_graph_capture(F, env):
-    """A captured call on a stream with no workspace runs the data-parallel twin;
-    replays match the oracle every time."""
-    BM, BN, _ = TAIL_CONFIGS[16]
+@pytest.mark.parametrize("warm", [False, True])
+def test_split_tail_under_graph_capture(F, env, warm):
+    """A captured call runs the data-parallel twin, whether or not the capturing
+    stream already has a workspace (warm: an eager call on it first); replays match
+    the oracle every time and the twin bitwise."""
+    BM, BN, twin = TAIL_CONFIGS[16]
     sizes, N = tail_shape(BM, BN, extra_tiles=11)
     w, ref = case(sizes, N, 1024, seed=1700)
-    env(config=16, tail_split=None)
     args = [P.dev(a) for a in (w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)]
+    env(config=twin, tail_split=None)
+    expect = run(F, w)
+    env(config=16, tail_split=None)
     out = torch.empty((w.total_M, N), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.Stream()
+    if warm:
+        with torch.cuda.stream(stream):
+            F.f8f8bf16_rowwise_grouped_stacked(*args, out=out)
+        torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
+    with torch.cuda.graph(g, stream=stream):
         F.f8f8bf16_rowwise_grouped_stacked(*args, out=out)
-    first = None
     for rep in range(3):
         out.view(torch.int16).fill_(P.SENTINEL)
         torch.cuda.synchronize()
@@ -245,9 +253,7 @@ def test_split_tail_under_graph_capture(F, env):
         torch.cuda.synchronize()
         got = P.bits_of(out)
         P.assert_rows_match(got, ref, label=f"graph replay {rep}")
-        if first is None:
-            first = got.copy()
-        assert np.array_equal(got, first)
+        assert np.array_equal(got, expect)
 
 
 def test_gate_up_default_plan_is_split_tail(F):

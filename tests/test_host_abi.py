@@ -111,3 +111,18 @@ def test_every_configuration_fits_lds(monkeypatch):
             p = F.plan(F.LAYOUT_STACKED, True, 8, 4096, 4096, 7168)
         assert p["config_id"] == cfg
         assert 0 < p["lds_bytes"] <= 160 * 1024, (cfg, p["lds_bytes"])
+
+
+@pytest.mark.parametrize("G,M,N,K", [
+    (1 << 20, 1024, 1 << 20, 1 << 20),   # W would be 2^60 bytes
+    (1, 1 << 30, 8, 1 << 20),            # X would be 2^50 bytes
+    (1, 1 << 30, 1 << 20, 16),           # Y would be 2^51 bytes
+])
+def test_plan_refuses_tensors_past_2_to_48_bytes(G, M, N, K):
+    with pytest.raises(ValueError, match="2\\^48"):
+        F.plan(F.LAYOUT_STACKED, False, G, M, N, K)
+
+
+def test_plan_accepts_large_but_sane_shapes():
+    p = F.plan(F.LAYOUT_STACKED, False, 256, 1 << 20, 8192, 8192)   # W 16 GiB, X 8 GiB
+    assert p["config_id"] >= 0
