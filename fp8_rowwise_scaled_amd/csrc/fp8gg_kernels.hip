@@ -21,14 +21,17 @@
 //     operand (MFMA rows = output columns n) and X the "B" operand (MFMA columns =
 //     output rows m), so each lane's accumulators cover consecutive output columns
 //     of one row and the epilogue stores 16-byte vectors.
-//   * A and B tiles of 64 K-bytes are copied global -> LDS with
-//     global_load_lds_dwordx4 (no staging registers), several stages deep.
-//   * LDS rows are 64 bytes (four 16-byte chunks), XOR-swizzled per row (lds_swz)
-//     so that the MFMA operand reads (consecutive rows at one logical chunk) are
-//     bank-conflict free.
+//   * X and W tiles of BK = 64 or 128 K-bytes per stage are copied global -> LDS
+//     with global_load_lds_dwordx4 (no staging registers), 2 to 4 stages deep.
+//   * LDS rows are BK bytes, XOR-swizzled per row (lds_swz) so that the MFMA
+//     operand reads (consecutive rows at one logical chunk) are bank-conflict free;
+//     pre-shuffled W arrives as whole 2 KB operand blocks and needs no swizzle.
 //   * W rows are placed in LDS in "MFMA order": LDS row 32*fn + rho of a wave's
 //     slice holds the output column that MFMA row rho of block fn produces in the
 //     chosen lane -> column map, so the loads do the permutation for free.
+//   * Large stacked calls run on a persistent grid whose LDS ring continues from
+//     one tile to the next (gg_tail_kernel); small-M calls use 32-row tiles with a
+//     deep ring, or stream W straight into registers (gg_skinny_kernel).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -225,7 +228,7 @@ __device__ __forceinline__ void zero_rect(uint16_t* Y, int64_t N, int64_t r0, in
 }
 
 // ---------------------------------------------------------------------------
-// The grouped GEMM with plain W: both operands staged through LDS
+// The grouped GEMM with both operands staged through LDS (plain or pre-shuffled W)
 // ---------------------------------------------------------------------------
 //
 // LdsTile holds everything one workgroup needs to compute one BM x BN output tile
