@@ -45,7 +45,7 @@ class Plan(ctypes.Structure):
         ("grid", ctypes.c_int64),
         ("zero_fill", ctypes.c_int32),
         ("lds_bytes", ctypes.c_int32),
-        ("split_tail", ctypes.c_int32),
+        ("persistent", ctypes.c_int32),
     ]
 
     def as_dict(self) -> dict:

@@ -149,49 +149,6 @@ int device_cus() {
   return cus;
 }
 
-// Split-tail workspace, one per (device, stream): calls on one stream run in order,
-// so they can share it; calls on different streams never do.  Allocated on first
-// use (never during graph capture: captured calls do not use it at all) and kept
-// for the life of the process.  Counters are zeroed at allocation and every call
-// leaves them zero.
-struct Workspace {
-  void* base = nullptr;
-  size_t bytes = 0;
-};
-
-fp8gg_status tail_workspace(hipStream_t stream, size_t need, Workspace* out) {
-  static std::mutex mu;
-  static std::map<std::pair<int, hipStream_t>, Workspace> pool;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(FP8GG_ERR_HIP, "hipGetDevice failed");
-  std::lock_guard<std::mutex> lock(mu);
-  Workspace& w = pool[std::make_pair(dev, stream)];
-  if (w.base && w.bytes >= need) {
-    *out = w;
-    return FP8GG_OK;
-  }
-  if (w.base) {
-    // Growing: the old buffer may still be in use by queued work on this stream.
-    hipError_t e = hipStreamSynchronize(stream);
-    if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "workspace resize: %s", hipGetErrorString(e));
-    (void)hipFree(w.base);
-    w.base = nullptr;
-    w.bytes = 0;
-  }
-  void* p = nullptr;
-  hipError_t e = hipMalloc(&p, need);
-  if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "workspace allocation of %zu bytes: %s", need, hipGetErrorString(e));
-  e = hipMemsetAsync(p, 0, need, stream);   // ordered before this call's kernel (never captured)
-  if (e != hipSuccess) {
-    (void)hipFree(p);
-    return fail(FP8GG_ERR_HIP, "workspace clear: %s", hipGetErrorString(e));
-  }
-  w.base = p;
-  w.bytes = need;
-  *out = w;
-  return FP8GG_OK;
-}
-
 fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K,
                        fp8gg_plan* p) {
   std::memset(p, 0, sizeof *p);
@@ -215,8 +172,8 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
       return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_CONFIG=%d does not name a usable configuration", forced);
     cfg = forced;
   }
-  if (layout != FP8GG_LAYOUT_STACKED && fp8gg::kConfigs[cfg].kind == fp8gg::kKindSplitTail)
-    cfg = fp8gg::kConfigs[cfg].twin;   // the split tail is scheduled over the stacked layout only
+  if (layout != FP8GG_LAYOUT_STACKED && fp8gg::kConfigs[cfg].kind == fp8gg::kKindPersistent)
+    cfg = fp8gg::kConfigs[cfg].twin;   // the persistent schedule covers the stacked layout only
   const fp8gg::KernelConfig& c = fp8gg::kConfigs[cfg];
   p->config_id = cfg;
   p->BM = c.BM;
@@ -233,7 +190,7 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
     int64_t ub = (M + c.BM - 1) / c.BM + G - 1;
     p->m_tiles = ub < M ? ub : M;
     p->grid = p->m_tiles * p->n_tiles;
-    p->split_tail = c.kind == fp8gg::kKindSplitTail ? 1 : 0;
+    p->persistent = c.kind == fp8gg::kKindPersistent ? 1 : 0;
   } else {
     p->m_tiles = (M + c.BM - 1) / c.BM;
     p->grid = p->m_tiles * p->n_tiles * G;
@@ -295,43 +252,22 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
   if (env_int("FP8GG_LOG", 0))
     std::fprintf(stderr,
                  "[fp8gg] layout=%d pre=%d G=%lld M=%lld N=%lld K=%lld -> cfg=%d tile=%dx%dx%d thr=%d st=%d "
-                 "ktail=%d ntail=%d grid=%lld (m_tiles=%lld n_tiles=%lld) split_tail=%d\n",
+                 "ktail=%d ntail=%d grid=%lld (m_tiles=%lld n_tiles=%lld) persistent=%d\n",
                  layout, preshuffled, (long long)G, (long long)M, (long long)N, (long long)K, p.config_id, p.BM,
                  p.BN, p.BK, p.threads, p.stages, p.k_tail, p.n_tail, (long long)p.grid, (long long)p.m_tiles,
-                 (long long)p.n_tiles, p.split_tail);
+                 (long long)p.n_tiles, p.persistent);
   const fp8gg::KernelConfig& cfg = fp8gg::kConfigs[p.config_id];
   hipError_t e;
-  if (cfg.kind == fp8gg::kKindSplitTail) {
+  if (cfg.kind == fp8gg::kKindPersistent) {
     // One persistent workgroup per compute unit.  For tuning and tests,
-    // FP8GG_TAIL_GRID overrides the grid and FP8GG_TAIL_SPLIT the split factor.
+    // FP8GG_TAIL_GRID overrides the grid and FP8GG_TAIL the remainder mode
+    // (0 automatic, 1 whole tiles, 2 quarter tiles).
     const int forced_grid = env_int("FP8GG_TAIL_GRID", 0);
     const int P = forced_grid > 0 ? forced_grid : device_cus();
-    const int force_split = env_int("FP8GG_TAIL_SPLIT", 0);
-    if (env_int("FP8GG_LOG", 0)) std::fprintf(stderr, "[fp8gg] persistent grid %d, forced split %d\n", P, force_split);
-    // A call captured into a graph runs the data-parallel twin instead: a graph then
-    // holds no library-owned memory and may be replayed on any stream, alongside
-    // eager calls that use this stream's workspace.
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    hipError_t ce = hipStreamIsCapturing(s, &cs);
-    if (ce != hipSuccess) return fail(FP8GG_ERR_HIP, "hipStreamIsCapturing: %s", hipGetErrorString(ce));
-    if (cs != hipStreamCaptureStatusNone) {
-      e = fp8gg::launch_gemm(layout, cfg.twin, p.k_tail != 0, a, p.grid, s);
-    } else {
-      // Sized for the largest tile at this grid, so that switching configurations
-      // never has to grow (synchronise and reallocate) the workspace.
-      size_t need = fp8gg::tail_workspace_bytes(cfg, P);
-      for (int c = 0; c < fp8gg::kNumConfigs; ++c)
-        if (fp8gg::kConfigs[c].kind == fp8gg::kKindSplitTail) {
-          const size_t b = fp8gg::tail_workspace_bytes(fp8gg::kConfigs[c], P);
-          need = b > need ? b : need;
-        }
-      Workspace ws;
-      st = tail_workspace(s, need, &ws);
-      if (st != FP8GG_OK) return st;
-      uint32_t* counters = static_cast<uint32_t*>(ws.base);
-      float* partials = reinterpret_cast<float*>(static_cast<char*>(ws.base) + fp8gg::tail_counters_bytes(P));
-      e = fp8gg::launch_gemm_tail(p.config_id, p.k_tail != 0, a, P, partials, counters, force_split, s);
-    }
+    const int tail_mode = env_int("FP8GG_TAIL", 0);
+    if (tail_mode < 0 || tail_mode > 2) return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_TAIL=%d is not 0, 1 or 2", tail_mode);
+    if (env_int("FP8GG_LOG", 0)) std::fprintf(stderr, "[fp8gg] persistent grid %d, tail mode %d\n", P, tail_mode);
+    e = fp8gg::launch_gemm_persistent(p.config_id, p.k_tail != 0, a, P, tail_mode, s);
   } else {
     e = fp8gg::launch_gemm(layout, p.config_id, p.k_tail != 0, a, p.grid, s);
   }

@@ -234,14 +234,15 @@ __device__ __forceinline__ void zero_rect(uint16_t* Y, int64_t N, int64_t r0, in
 // LdsTile holds everything one workgroup needs to compute one BM x BN output tile
 // over a range of K stages: the per-thread copy descriptors, the LDS pipeline, the
 // MFMA loop and the scaled epilogue.  The data-parallel kernel runs one tile per
-// workgroup; the split-tail kernel runs a sequence of whole tiles and a K piece per
-// persistent workgroup.
+// workgroup; the persistent kernel runs a sequence of whole tiles, then quarter
+// tiles, per workgroup.
 
 // PRE: W comes pre-shuffled (f8f8bf16_shuffle_b's layout): each 32-row, 64-byte-K
 // block of W is 2048 contiguous bytes already in MFMA-operand order, so a stage's W
 // copy is a linear copy of whole blocks and its fragments read with no swizzle.
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PRE = false>
 struct LdsTile {
+  static constexpr int BM_ = BM, BN_ = BN, STAGES_ = STAGES;
   static constexpr int NT = WM * WN * 64;
   static constexpr int CPR = BK / 16;          // 16-byte chunks per LDS row
   static constexpr int KS = BK / 64;           // MFMA K steps per stage
@@ -461,6 +462,10 @@ struct LdsTile {
   __device__ __forceinline__ void compute(int slot, Acc& acc) const {
     v8i xf[KS][FM], wf[KS][FN];
     read_frags(slot, xf, wf);
+    mfmas(xf, wf, acc);
+  }
+
+  __device__ __forceinline__ static void mfmas(const v8i (&xf)[KS][FM], const v8i (&wf)[KS][FN], Acc& acc) {
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
@@ -600,58 +605,6 @@ struct LdsTile {
     scale(a, t, n0, acc, pk);
     store(a, t, n0, pk);
   }
-
-  // Accumulators <-> a partial-sum slot of ACC_FLOATS * NT floats.  Quad q of the
-  // accumulator registers (floats 4q .. 4q+3) of all NT threads is NT consecutive
-  // 16-byte vectors, so every access is a coalesced 16-byte-per-lane vector access.
-  // Loads go a batch of blocks at a time (the empty asm keeps the compiler from
-  // hoisting every batch's loads ahead of the additions, which would need a second
-  // accumulator's worth of registers).
-  __device__ __forceinline__ v4f* quad(float* slot, int blk, int q) const {
-    return reinterpret_cast<v4f*>(slot) + (int64_t)(blk * 4 + q) * NT + tid;
-  }
-  __device__ __forceinline__ const v4f* quad(const float* slot, int blk, int q) const {
-    return reinterpret_cast<const v4f*>(slot) + (int64_t)(blk * 4 + q) * NT + tid;
-  }
-  __device__ __forceinline__ void store_partial(float* slot, const Acc& acc) const {
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const v16f& c = acc[fm][fn];
-          *quad(slot, fm * FN + fn, q) = v4f{c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]};
-        }
-  }
-  template <bool ADD>
-  __device__ __forceinline__ void gather_partial(const float* slot, Acc& acc) const {
-    // GROUP blocks of 16 floats per batch: 4 * GROUP 16-byte loads in flight per
-    // thread (a finisher reloads several partial tiles and is otherwise latency-bound).
-    constexpr int BLOCKS = FM * FN;
-    constexpr int GROUP = BLOCKS < 4 ? BLOCKS : 4;
-    static_assert(BLOCKS % GROUP == 0, "partial blocks come in whole batches");
-#pragma unroll
-    for (int b0 = 0; b0 < BLOCKS; b0 += GROUP) {
-      v4f v[GROUP][4];
-#pragma unroll
-      for (int g = 0; g < GROUP; ++g)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[g][q] = *quad(slot, b0 + g, q);
-#pragma unroll
-      for (int g = 0; g < GROUP; ++g) {
-        const int fm = (b0 + g) / FN, fn = (b0 + g) % FN;
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int j = 0; j < 4; ++j)
-            acc[fm][fn][4 * q + j] = ADD ? acc[fm][fn][4 * q + j] + v[g][q][j] : v[g][q][j];
-      }
-      asm volatile("" ::: "memory");
-    }
-  }
-  __device__ __forceinline__ void load_partial(const float* slot, Acc& acc) const { gather_partial<false>(slot, acc); }
-  __device__ __forceinline__ void add_partial(const float* slot, Acc& acc) const { gather_partial<true>(slot, acc); }
 };
 
 // Data-parallel kernel: one output tile per workgroup, whole K.
@@ -711,54 +664,44 @@ __device__ __forceinline__ int64_t count_m_tiles(const GemmArgs& a) {
   return tiles;
 }
 
-// Persistent kernel with a split last wave (stacked layout).
+// Persistent kernel (stacked layout).
 //
 // Schedule.  A grid of P workgroups, one per compute unit, walks the T output
 // tiles in data-parallel order: workgroup w computes whole tiles w, w + P, ...
-// When T is not a multiple of P, the last wave of rem = T % P tiles would keep
-// P - rem compute units idle for a whole tile.  Instead each of those rem tiles is
-// cut along K into s pieces (s from tail_split, or forced by the caller) computed
-// by s different workgroups at once.  Piece p of remainder tile i runs on
-// workgroup p * rem + i and covers K stages [p * nk / s, (p + 1) * nk / s).  Each
-// piece stores its fp32 partial sums in its workgroup's workspace slot and bumps
-// the tile's counter; the piece that arrives last reloads all s partials and adds
-// them in piece order (so the result does not depend on arrival order), writes the
-// output tile and resets the counter to zero.  No workgroup ever waits for another.
+// When T is not a multiple of P, the rem = T % P tiles of the last round would keep
+// P - rem compute units idle for a whole tile.  When 4 * rem <= 2 * P those tiles
+// are computed as quarter tiles instead, (BM/2) x (BN/2) each: quarter q of
+// remainder tile i is quarter number 4i + q, and workgroup w computes quarters w,
+// w + P, ... once its whole tiles are done (quarters past the group's rows or past
+// N are skipped).  A quarter copies half the operand bytes of a whole tile and
+// takes about 0.3 of its time, so the last round costs 0.3 (one round of quarters)
+// or 0.6 (two) of a whole tile instead of 1.  Each output element is computed by
+// one workgroup in the same K order as in the data-parallel kernel, so the result
+// is bitwise that of the data-parallel kernel whatever the grid.
 //
-// Pipeline.  A workgroup's items (whole tiles, then at most one piece) form one
-// stream of K stages through the LDS ring: while the last stages of one item are
-// multiplied, the first stages of the next are already being copied, and the
-// finished tile's epilogue runs with them in flight.  Each item's scales travel
-// with its first stage into one of two LDS scale blocks, so the epilogue reads no
-// global memory.  Copies of an item two ahead wait until the item before it is
-// done, which keeps two scale blocks enough.  The wait before each stage counts
-// the copies issued after that stage exactly (stores issued since then only make
-// it stricter: vector memory operations complete in order).
+// Pipeline.  A workgroup's whole tiles form one stream of K stages through the LDS
+// ring: while the last stages of one tile are multiplied, the first stages of the
+// next are already being copied, and the finished tile's epilogue runs with them
+// in flight.  Each tile's scales travel with its first stage into one of two LDS
+// scale blocks, so the epilogue reads no global memory.  Copies of a tile two ahead
+// wait until the tile before it is done, which keeps two scale blocks enough.  The
+// wait before each stage counts the copies issued after that stage exactly (stores
+// issued since then only make it stricter: vector memory operations complete in
+// order).  Quarter tiles run one after another, each with its own prologue.
 //
-// Workspace: counters [P] uint32 (zero between calls), then P slots of
-// E::ACC_FLOATS * E::NT floats.
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PRE>
-__global__ void __launch_bounds__(WM * WN * 64)
-gg_tail_kernel(GemmArgs a, float* partials, uint32_t* counters, int force_split) {
-  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL, PRE> E;
-  constexpr int64_t SLOT = (int64_t)E::ACC_FLOATS * E::NT;
+// tail_mode: 0 chooses quarters by the rule above, 1 never uses them, 2 always
+// does when rem > 0.
+template <typename E>
+__device__ __forceinline__ void persistent_whole_tiles(const GemmArgs& a, int64_t w, int64_t P, int64_t whole,
+                                                       int nk, uint8_t* smem, float (*scales)[E::SCALE_FLOATS],
+                                                       float* scale_dummy) {
+  constexpr int STAGES = E::STAGES_;
   // Deferring a finished tile's stores by one stage keeps them out of the next
   // stage's wait; it needs the packed outputs live across one more MFMA step,
   // which fits the register budget of the smaller tiles only.
   constexpr bool DEFER_STORES = E::ACC_FLOATS <= 64;
   static_assert(E::EVEN_LOADS, "the stage wait counts assume equal copies per wave");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
-  __shared__ __attribute__((aligned(16))) float scales[2][E::SCALE_FLOATS];
-  __shared__ __attribute__((aligned(16))) float scale_dummy[64];
-  __shared__ uint32_t is_finisher;
-
-  const int64_t P = gridDim.x;
-  const int64_t w = blockIdx.x;
-  const int nk = (int)((a.K + BK - 1) / BK);
-  const int64_t T = count_m_tiles<BM>(a) * a.n_tiles;
-  const int s = tail_split(T, P, nk, E::STAGE_BYTES, SLOT * 4, force_split);
-  const int64_t rem = s > 1 ? T % P : 0;
-  const int64_t whole = T - rem;
+  if (w >= whole) return;
 
   E e;
   e.init(smem);
@@ -766,46 +709,31 @@ gg_tail_kernel(GemmArgs a, float* partials, uint32_t* counters, int force_split)
   struct Item {
     Tile t;
     int64_t tile, n0;
-    int kb, ke, seq;
-    bool piece;
+    int seq;
   };
   int64_t next = w;
-  bool piece_taken = rem == 0 || w >= rem * s;
   auto take = [&](Item& it, int seq) -> bool {
-    it.kb = 0;
-    it.ke = nk;
-    it.piece = false;
+    if (next >= whole) return false;
+    it.tile = next;
     it.seq = seq;
-    if (next < whole) {
-      it.tile = next;
-      next += P;
-    } else if (!piece_taken) {
-      piece_taken = true;
-      it.piece = true;
-      it.tile = whole + w % rem;
-      const int64_t p = w / rem;
-      it.kb = (int)(p * nk / s);
-      it.ke = (int)((p + 1) * nk / s);
-    } else {
-      return false;
-    }
-    resolve_stacked<BM>(a, it.tile / a.n_tiles, it.t);
-    it.n0 = (it.tile % a.n_tiles) * BN;
+    next += P;
+    resolve_stacked<E::BM_>(a, it.tile / a.n_tiles, it.t);
+    it.n0 = (it.tile % a.n_tiles) * E::BN_;
     return true;
   };
 
-  Item C;                       // the item whose stages are being multiplied
-  if (!take(C, 0)) return;
-  Item I = C;                   // the item whose stages are being copied
-  bool more = true;             // items may remain after I
-  int kt_i = I.kb;
+  Item C;                       // the tile whose stages are being multiplied
+  take(C, 0);
+  Item I = C;                   // the tile whose stages are being copied
+  bool more = true;             // tiles may remain after I
+  int kt_i = 0;
   int u_i = 0, u_c = 0;         // stages issued / multiplied so far (LDS slot = u % STAGES)
   int ahead = 0;                // stages issued and not yet multiplied
-  uint32_t firsts = 0;          // bit j: the j-th oldest of those is an item's first stage
+  uint32_t firsts = 0;          // bit j: the j-th oldest of those is a tile's first stage
   e.setup(a, I.t, I.n0);
 
   auto issue_next = [&]() {
-    if (kt_i == I.ke) {
+    if (kt_i == nk) {
       if (!more || I.seq != C.seq) return;
       Item nx;
       if (!take(nx, I.seq + 1)) {
@@ -813,10 +741,10 @@ gg_tail_kernel(GemmArgs a, float* partials, uint32_t* counters, int force_split)
         return;
       }
       I = nx;
-      kt_i = I.kb;
+      kt_i = 0;
       e.setup(a, I.t, I.n0);
     }
-    const bool first = kt_i == I.kb;
+    const bool first = kt_i == 0;
     e.issue(kt_i, u_i % STAGES, nk, a.K);
     if (first) e.issue_scales(a, I.t, I.n0, scales[I.seq & 1], scale_dummy);
     firsts |= (uint32_t)first << ahead;
@@ -851,7 +779,7 @@ gg_tail_kernel(GemmArgs a, float* partials, uint32_t* counters, int force_split)
   };
 
   typename E::Packed pk;
-  Tile st = C.t;                // tile of the stores deferred into the next item's first stage
+  Tile st = C.t;                // tile of the stores deferred into the next tile's first stage
   int64_t sn0 = 0;
   bool pending = false;
   for (;;) {
@@ -860,50 +788,66 @@ gg_tail_kernel(GemmArgs a, float* partials, uint32_t* counters, int force_split)
     for (int i = 0; i < E::FM; ++i)
 #pragma unroll
       for (int j = 0; j < E::FN; ++j) acc[i][j] = v16f{0};
-    // The first stage of the item is peeled off: it carries the previous tile's
+    // The first stage of the tile is peeled off: it carries the previous tile's
     // deferred stores, so the loop over the remaining stages carries only acc.
     step(acc, DEFER_STORES && pending, st, sn0, pk);
     pending = false;
-    for (int kt = C.kb + 1; kt < C.ke; ++kt) step(acc, false, st, sn0, pk);
+    for (int kt = 1; kt < nk; ++kt) step(acc, false, st, sn0, pk);
 
-    const float* sbuf = scales[C.seq & 1];
-    if (C.piece) {
-      const int64_t i = C.tile - whole;
-      e.store_partial(partials + w * SLOT, acc);
-      // Every thread's stores have completed at the barrier.  An agent-scope release
-      // fence (L2 write-back) publishes them before the counter moves; the
-      // finisher's acquire fence after the counter (L2 invalidate) pairs with the
-      // other pieces' releases through the counter.  Only the finisher invalidates:
-      // an invalidate also drops lines that other workgroups of this XCD are using.
-      __syncthreads();
-      if (e.tid == 0) {
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-        const uint32_t before = atomicAdd(&counters[i], 1u);
-        const bool last = before == (uint32_t)(s - 1);
-        if (last) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-        is_finisher = last ? 1u : 0u;
-      }
-      __syncthreads();
-      if (is_finisher) {
-        e.load_partial(partials + i * SLOT, acc);
-        for (int p = 1; p < s; ++p) e.add_partial(partials + (p * rem + i) * SLOT, acc);
-        if (e.tid == 0) counters[i] = 0;
-        e.scale_lds(acc, sbuf, pk);
-        e.store(a, C.t, C.n0, pk);
-      }
-      return;                   // a piece is always a workgroup's last item
-    }
-    e.scale_lds(acc, sbuf, pk);
-    const bool last_item = I.seq == C.seq;   // nothing was taken after C
-    if (DEFER_STORES && !last_item) {
+    e.scale_lds(acc, scales[C.seq & 1], pk);
+    const bool last_tile = I.seq == C.seq;   // nothing was taken after C
+    if (DEFER_STORES && !last_tile) {
       st = C.t;
       sn0 = C.n0;
       pending = true;
     } else {
       e.store(a, C.t, C.n0, pk);
     }
-    if (last_item) return;
+    if (last_tile) return;
     C = I;
+  }
+}
+
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PRE>
+__global__ void __launch_bounds__(WM * WN * 64)
+gg_persistent_kernel(GemmArgs a, int tail_mode) {
+  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL, PRE> E;
+  // Quarter tiles reuse the LDS ring with as many stages as fit (at most 8).
+  constexpr int Q_STAGE_BYTES = (BM + BN) / 2 * BK;
+  constexpr int Q_STAGES = E::SMEM_BYTES / Q_STAGE_BYTES < 8 ? E::SMEM_BYTES / Q_STAGE_BYTES : 8;
+  typedef LdsTile<BM / 2, BN / 2, BK, WM, WN, Q_STAGES, KTAIL, PRE> Q;
+  static_assert(Q::SMEM_BYTES <= E::SMEM_BYTES, "quarter tiles reuse the LDS ring");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) float scales[2][E::SCALE_FLOATS];
+  __shared__ __attribute__((aligned(16))) float scale_dummy[64];
+
+  const int64_t P = gridDim.x;
+  const int64_t w = blockIdx.x;
+  const int nk = (int)((a.K + BK - 1) / BK);
+  const int64_t T = count_m_tiles<BM>(a) * a.n_tiles;
+  const int64_t rem = tail_quarters(T, P, tail_mode) ? T % P : 0;
+  const int64_t whole = T - rem;
+
+  persistent_whole_tiles<E>(a, w, P, whole, nk, smem, scales, scale_dummy);
+
+  for (int64_t qn = w; qn < 4 * rem; qn += P) {
+    const int64_t tile = whole + qn / 4;
+    const int q = (int)(qn % 4);
+    Tile t;
+    resolve_stacked<BM>(a, tile / a.n_tiles, t);
+    t.row_base += (q >> 1) * (BM / 2);
+    const int64_t n0 = (tile % a.n_tiles) * BN + (q & 1) * (BN / 2);
+    if (t.row_base >= t.row_end || n0 >= a.N) continue;
+    Q e;
+    e.init(smem);
+    e.setup(a, t, n0);
+    typename Q::Acc acc;
+#pragma unroll
+    for (int i = 0; i < Q::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < Q::FN; ++j) acc[i][j] = v16f{0};
+    e.run(0, nk, nk, a.K, acc);     // starts with a barrier: the ring is free to reuse
+    e.epilogue(a, t, n0, acc);
   }
 }
 
@@ -1142,7 +1086,8 @@ __global__ void __launch_bounds__(256) zero_fill_kernel(v4i* __restrict__ y, int
 
 // kind: 0 = both operands through LDS (one tile per workgroup),
 //       3 = small M: W and X straight to registers, K split across the 4 waves,
-//       4 = kind 0 on a persistent grid with a split last wave (stacked layout).
+//       4 = kind 0 on a persistent grid whose last round may run as quarter tiles
+//           (stacked layout).
 // pre: 1 = W pre-shuffled (the _preshuffle entry points), 0 = plain W.
 //                      BM   BN   BK  WM WN stages kind wdepth twin pre
 const KernelConfig kConfigs[] = {
@@ -1190,15 +1135,14 @@ static hipError_t launch_lds(bool k_tail, const GemmArgs& a, int64_t grid, hipSt
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool PRE = false>
-static hipError_t launch_tail(bool k_tail, const GemmArgs& a, int grid, float* partials, uint32_t* counters,
-                              int force_split, hipStream_t s) {
+static hipError_t launch_persistent(bool k_tail, const GemmArgs& a, int grid, int tail_mode, hipStream_t s) {
   const dim3 block(WM * WN * 64);
   if (k_tail)
-    hipLaunchKernelGGL((gg_tail_kernel<BM, BN, BK, WM, WN, STAGES, true, PRE>), dim3((uint32_t)grid), block, 0, s, a,
-                       partials, counters, force_split);
+    hipLaunchKernelGGL((gg_persistent_kernel<BM, BN, BK, WM, WN, STAGES, true, PRE>), dim3((uint32_t)grid), block, 0,
+                       s, a, tail_mode);
   else
-    hipLaunchKernelGGL((gg_tail_kernel<BM, BN, BK, WM, WN, STAGES, false, PRE>), dim3((uint32_t)grid), block, 0, s,
-                       a, partials, counters, force_split);
+    hipLaunchKernelGGL((gg_persistent_kernel<BM, BN, BK, WM, WN, STAGES, false, PRE>), dim3((uint32_t)grid), block,
+                       0, s, a, tail_mode);
   return hipGetLastError();
 }
 
@@ -1211,8 +1155,8 @@ static hipError_t launch_skinny(bool k_tail, const GemmArgs& a, int64_t grid, hi
   return hipGetLastError();
 }
 
-// One case per row of kConfigs (same order).  Split-tail rows (16, 17) go through
-// launch_gemm_tail; without a workspace the caller launches their twin here.
+// One case per row of kConfigs (same order).  Persistent rows (16, 17, 26) go
+// through launch_gemm_persistent; the padded layout launches their twin here.
 template <int LAYOUT>
 static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
   switch (config_id) {
@@ -1245,12 +1189,12 @@ static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, i
   }
 }
 
-hipError_t launch_gemm_tail(int config_id, bool k_tail, const GemmArgs& a, int grid, float* partials,
-                            uint32_t* counters, int force_split, hipStream_t s) {
+hipError_t launch_gemm_persistent(int config_id, bool k_tail, const GemmArgs& a, int grid, int tail_mode,
+                                  hipStream_t s) {
   switch (config_id) {
-    case 16: return launch_tail<256, 256, 128, 2, 4, 2>(k_tail, a, grid, partials, counters, force_split, s);
-    case 17: return launch_tail<128, 256, 128, 2, 4, 3>(k_tail, a, grid, partials, counters, force_split, s);
-    case 26: return launch_tail<256, 256, 128, 2, 4, 2, true>(k_tail, a, grid, partials, counters, force_split, s);
+    case 16: return launch_persistent<256, 256, 128, 2, 4, 2>(k_tail, a, grid, tail_mode, s);
+    case 17: return launch_persistent<128, 256, 128, 2, 4, 3>(k_tail, a, grid, tail_mode, s);
+    case 26: return launch_persistent<256, 256, 128, 2, 4, 2, true>(k_tail, a, grid, tail_mode, s);
     default: return hipErrorInvalidValue;
   }
 }

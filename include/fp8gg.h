@@ -20,17 +20,13 @@
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is only
  *     enqueued: no entry point copies between host and device or synchronises.
  *     Every call may be captured into a HIP graph.
- *   - Workspace: stacked calls with at least 512 rows per group (on average) run on
- *     a persistent grid, one workgroup per compute unit, whose last partial wave of
- *     output tiles may be split along K; the pieces' fp32 partial sums go through a
- *     workspace.  The library allocates it on the first such call on a given
- *     stream (one partial tile per compute unit plus counters: 64 MB on MI355X)
- *     and keeps it for the life of the process; calls on one stream share it (they
- *     run in order), calls on different streams never do.  A call made while its
- *     stream is being captured never touches the workspace: it runs the equivalent
- *     data-parallel kernel, so a graph holds no library-owned memory and may be
- *     replayed on any stream.  Either way the results are deterministic: the
- *     partial sums of a split tile are added in a fixed order.
+ *   - No workspace: the library allocates no device memory.  Stacked calls with at
+ *     least 512 rows per group (on average) run on a persistent grid, one
+ *     workgroup per compute unit; when the output tiles do not fill a whole number
+ *     of rounds of that grid, the tiles of the last round may be computed as four
+ *     quarter tiles each.  Every output element is still computed by one
+ *     workgroup in one fixed K order, so results are deterministic and equal,
+ *     bit for bit, to those of the one-tile-per-workgroup schedule.
  *   - Device-side metadata (M_sizes, zero_start_index_M) is never read by the host.
  *     The kernels clamp it (negative counts -> 0, cumulative row ends -> total_M,
  *     valid rows -> [0, expected_m]), so inconsistent metadata can never cause an
@@ -163,9 +159,9 @@ typedef struct {
   int64_t grid;       /* workgroups of the data-parallel schedule (one per tile)     */
   int32_t zero_fill;  /* 1 if the call zero-fills Y instead (K == 0)                */
   int32_t lds_bytes;  /* LDS per workgroup                                          */
-  int32_t split_tail; /* 1: persistent grid (one workgroup per compute unit) whose
-                         last partial wave is split along K; the grid above is then
-                         the tile count of the data-parallel schedule               */
+  int32_t persistent; /* 1: persistent grid (one workgroup per compute unit); the
+                         grid above is then the tile count of the data-parallel
+                         schedule                                                   */
 } fp8gg_plan;
 
 enum { FP8GG_LAYOUT_STACKED = 0, FP8GG_LAYOUT_PADDED = 1 };
