@@ -15,8 +15,11 @@ from .grouped_gemm import (  # noqa: F401
     dynamic_entries,
     dynamic_row_classes,
     e4m3fn_table,
+    grouped_batched,
     grouped_dynamic,
+    grouped_offsets,
     grouped_stacked,
+    offsets_row_groups,
     stacked_entries,
     stacked_row_groups,
 )

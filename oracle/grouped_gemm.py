@@ -25,6 +25,13 @@ What is computed, per group g (the plain definition, written out):
     only the first zero_start_index_M[g] are valid; padding rows are zero, the
     part of the contract the zeroing_output_tensor flag controls ([MSLK-471],
     commits adding the padded layout and its test).
+  * Offsets layout (2D-3D): groups packed along M as in the stacked layout, but
+    the boundaries come as an int32 inclusive prefix sum: group g owns rows
+    [offsets[g-1], offsets[g]) with offsets[-1] = 0 ([MSLK-471], commit adding
+    the offsets layout, and the commit mapping the grouped mm op's 2D-3D ranks
+    onto it).
+  * Batched layout (3D-3D): every group owns a full slab of M rows, all valid;
+    there is no row metadata ([MSLK-471], commit adding the batched layout).
   * A contraction over K = 0 returns a zeroed output whatever the layout
     ([MSLK-471], commits on zero-length reductions and on the fakes' contracts).
 
@@ -44,6 +51,9 @@ Readings taken where the pages are silent (also listed in the design notes):
   * M_sizes entries < 0 count as 0; rows past the running sum (or past total_M)
     belong to no group and are left untouched.
   * zero_start_index_M is clamped to [0, expected_m].
+  * offsets: group g ends at min(max(offsets[g], end of group g-1), total_M), so
+    an offset below its predecessor makes an empty group and rows past the last
+    end belong to no group (left untouched).
   * K = 0 zeroes every row of the output, in both layouts.
 
 Row classes returned with every result: ROW_WRITTEN (computed), ROW_ZEROED
@@ -186,15 +196,42 @@ def stacked_row_groups(M_sizes: np.ndarray, total_M: int) -> np.ndarray:
     return owner
 
 
+def offsets_row_groups(offsets: np.ndarray, total_M: int) -> np.ndarray:
+    """Owning group of each row of the offsets layout, or -1 for rows of none.
+
+    Group g owns rows [end_{g-1}, end_g), end_{-1} = 0, with
+    end_g = min(max(offsets[g], end_{g-1}), total_M).
+    """
+    owner = np.full(int(total_M), -1, dtype=np.int64)
+    prev = 0
+    for g, o in enumerate(np.asarray(offsets, dtype=np.int64).tolist()):
+        end = min(max(o, prev), total_M)
+        owner[prev:end] = g
+        prev = end
+    return owner
+
+
 def grouped_stacked(XQ, WQ, x_scale, w_scale, M_sizes) -> OracleResult:
     """Stacked layout: XQ [total_M, K], WQ [G, N, K], x_scale [total_M],
     w_scale [G, N], M_sizes [G] -> Y [total_M, N]."""
+    XQ = np.asarray(XQ, np.uint8)
+    return _grouped_packed(XQ, WQ, x_scale, w_scale, stacked_row_groups(M_sizes, XQ.shape[0]))
+
+
+def grouped_offsets(XQ, WQ, x_scale, w_scale, offsets) -> OracleResult:
+    """Offsets layout: XQ [total_M, K], WQ [G, N, K], x_scale [total_M],
+    w_scale [G, N], offsets [G] int32 inclusive prefix -> Y [total_M, N]."""
+    XQ = np.asarray(XQ, np.uint8)
+    return _grouped_packed(XQ, WQ, x_scale, w_scale, offsets_row_groups(offsets, XQ.shape[0]))
+
+
+def _grouped_packed(XQ, WQ, x_scale, w_scale, owner) -> OracleResult:
+    """Groups packed along M; owner[r] is the group of row r (-1: none)."""
     XQ = np.asarray(XQ, np.uint8)
     WQ = np.asarray(WQ, np.uint8)
     total_M, K = XQ.shape
     G, N, K2 = WQ.shape
     assert K == K2
-    owner = stacked_row_groups(M_sizes, total_M)
     values = np.full((total_M, N), np.nan)
     bits = np.full((total_M, N), UNTOUCHED_SENTINEL, dtype=np.uint16)
     row_class = np.full(total_M, ROW_UNTOUCHED, dtype=np.int8)
@@ -250,6 +287,24 @@ def grouped_dynamic(XQ, WQ, x_scale, w_scale, zero_start_index_M,
         values[g, zeroed] = 0.0
         bits[g, zeroed] = 0
     return OracleResult(values, bits, cls.reshape(-1))
+
+
+def grouped_batched(XQ, WQ, x_scale, w_scale) -> OracleResult:
+    """Batched layout: XQ [G, M, K], WQ [G, N, K], x_scale [G, M], w_scale [G, N]
+    -> Y [G, M, N], every row written (flattened row classes [G*M])."""
+    XQ = np.asarray(XQ, np.uint8)
+    WQ = np.asarray(WQ, np.uint8)
+    G, M, K = XQ.shape
+    G2, N, K2 = WQ.shape
+    assert G == G2 and K == K2
+    if K == 0:
+        return OracleResult(np.zeros((G, M, N)), np.zeros((G, M, N), np.uint16),
+                            np.full(G * M, ROW_ZEROED, np.int8))
+    values = np.empty((G, M, N))
+    for g in range(G):
+        acc = _accumulate(XQ[g], WQ[g])
+        values[g] = _apply_scales(acc, np.asarray(x_scale)[g], np.asarray(w_scale)[g])
+    return OracleResult(values, bf16_rne_from_f64(values), np.full(G * M, ROW_WRITTEN, np.int8))
 
 
 # ---------------------------------------------------------------------------

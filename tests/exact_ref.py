@@ -77,3 +77,21 @@ def stacked_exact(XQ, WQ, x_scale, w_scale, M_sizes):
             out[r] = row
         start += s
     return out
+
+
+def offsets_exact(XQ, WQ, x_scale, w_scale, offsets):
+    """Exact bf16 bits [total_M, N] for well-formed offsets (non-decreasing, at most
+    total_M): group g owns rows offsets[g-1] .. offsets[g]-1, offsets[-1] = 0."""
+    total_M = XQ.shape[0]
+    G, N, _ = WQ.shape
+    out = [None] * total_M
+    for g in range(G):
+        lo = int(offsets[g - 1]) if g > 0 else 0
+        for r in range(lo, int(offsets[g])):
+            row = []
+            for n in range(N):
+                acc = dot_exact(XQ[r], WQ[g, n])
+                v = None if acc is None else acc * Fraction(float(x_scale[r])) * Fraction(float(w_scale[g, n]))
+                row.append(bf16_bits_exact(v))
+            out[r] = row
+    return out

@@ -149,6 +149,96 @@ def test_stacked_equals_exact_bruteforce(seed, sizes, N, K, total_M):
     assert _check_bruteforce(seed, sizes, N, K, total_M)
 
 
+def _rows_match_exact(res, exact):
+    """res (an OracleResult over rows) against exact rows (None: no group)."""
+    for r, row in enumerate(exact):
+        if row is None:
+            if res.row_class[r] != oracle.ROW_UNTOUCHED:
+                return False
+            continue
+        if res.row_class[r] != oracle.ROW_WRITTEN:
+            return False
+        got = res.bits.reshape(len(exact), -1)[r].astype(np.int64)
+        want = np.array(row, np.int64)
+        zero = (want & 0x7FFF) == 0
+        if not np.array_equal(got[~zero], want[~zero]):
+            return False
+        if not np.all((got[zero] & 0x7FFF) == 0):
+            return False
+    return True
+
+
+# (seed, offsets, N, K, total_M): offsets are int32 inclusive prefix sums
+OFFSETS_CASES = [
+    (31, [2, 2, 5], 4, 48, None),      # an empty middle group
+    (32, [0, 3, 3, 7], 3, 32, 9),      # rows 7 and 8 belong to no group
+    (33, [4], 5, 16, None),
+]
+
+
+def _check_offsets(seed, offsets, N, K, total_M):
+    sizes = np.diff([0] + offsets)
+    XQ, WQ, xs, ws, _ = _rand_problem(seed, sizes, N, K, total_M)
+    res = oracle.grouped_offsets(XQ, WQ, xs, ws, np.array(offsets, np.int32))
+    return _rows_match_exact(res, exact_ref.offsets_exact(XQ, WQ, xs, ws, offsets))
+
+
+@pytest.mark.parametrize("seed,offsets,N,K,total_M", OFFSETS_CASES)
+def test_offsets_equals_exact_bruteforce(seed, offsets, N, K, total_M):
+    assert _check_offsets(seed, offsets, N, K, total_M)
+
+
+def test_offsets_reading_of_ill_formed_prefixes():
+    """An offset below its predecessor ends an empty group; offsets past total_M are
+    cut there; rows past the last end belong to no group."""
+    owner = oracle.offsets_row_groups(np.array([3, 1, 6, 20], np.int32), 8)
+    assert owner.tolist() == [0, 0, 0, 2, 2, 2, 3, 3]
+    owner = oracle.offsets_row_groups(np.array([-2, 2], np.int32), 5)
+    assert owner.tolist() == [1, 1, -1, -1, -1]
+
+
+def test_offsets_equals_stacked_with_differenced_sizes():
+    sizes = np.array([5, 0, 9, 1, 7])
+    XQ, WQ, xs, ws, _ = _rand_problem(34, sizes, 6, 64, 25)
+    offs = np.cumsum(sizes).astype(np.int32)
+    a = oracle.grouped_offsets(XQ, WQ, xs, ws, offs)
+    b = oracle.grouped_stacked(XQ, WQ, xs, ws, sizes)
+    assert np.array_equal(a.bits, b.bits) and np.array_equal(a.row_class, b.row_class)
+
+
+def _check_batched(seed, G, M, N, K):
+    XQ, WQ, xs, ws, _ = _rand_problem(seed, [M] * G, N, K)
+    res = oracle.grouped_batched(XQ.reshape(G, M, K), WQ, xs.reshape(G, M), ws)
+    return _rows_match_exact(res, exact_ref.stacked_exact(XQ, WQ, xs, ws, [M] * G))
+
+
+@pytest.mark.parametrize("seed,G,M,N,K", [(41, 3, 2, 4, 48), (42, 1, 5, 3, 32)])
+def test_batched_equals_exact_bruteforce(seed, G, M, N, K):
+    assert _check_batched(seed, G, M, N, K)
+
+
+def test_batched_single_group_is_a_plain_scaled_gemm():
+    """G = 1: the batched layout is one GEMM, (dec(X) @ dec(W)^T) scaled by rows and
+    columns, written here with numpy's matmul on float64 (exact at this size)."""
+    rng = np.random.default_rng(43)
+    XQ = rng.choice(FINITE_CODES, size=(1, 6, 96)).astype(np.uint8)
+    WQ = rng.choice(FINITE_CODES, size=(1, 5, 96)).astype(np.uint8)
+    xs = (2.0 ** rng.uniform(-4, 4, (1, 6))).astype(np.float32)
+    ws = (2.0 ** rng.uniform(-4, 4, (1, 5))).astype(np.float32)
+    x = torch.from_numpy(XQ[0]).view(torch.float8_e4m3fn).double().numpy()
+    w = torch.from_numpy(WQ[0]).view(torch.float8_e4m3fn).double().numpy()
+    ref = (x @ w.T) * xs[0].astype(np.float64)[:, None] * ws[0].astype(np.float64)[None, :]
+    res = oracle.grouped_batched(XQ, WQ, xs, ws)
+    assert np.array_equal(res.values[0], ref)
+    assert np.all(res.row_class == oracle.ROW_WRITTEN)
+
+
+def test_batched_k_zero_is_zero():
+    res = oracle.grouped_batched(np.zeros((2, 3, 0), np.uint8), np.zeros((2, 4, 0), np.uint8),
+                                 np.ones((2, 3), np.float32), np.ones((2, 4), np.float32))
+    assert np.all(res.bits == 0) and np.all(res.row_class == oracle.ROW_ZEROED)
+
+
 def _load_worked():
     with open(os.path.join(GOLDEN, "worked_example.json")) as f:
         ex = json.load(f)
@@ -365,6 +455,8 @@ def test_entries_match_full_result():
 
 def _pins_pass():
     ok = all(_check_bruteforce(*c) for c in BRUTE_CASES)
+    ok = ok and all(_check_offsets(*c) for c in OFFSETS_CASES)
+    ok = ok and _check_batched(41, 3, 2, 4, 48)
     try:
         test_worked_example_stacked()
         test_worked_example_padded()
@@ -389,6 +481,15 @@ def _mut_group_shift(M_sizes, total_M):
     return og.__dict__["_orig_rows"](np.roll(np.asarray(M_sizes), 1), total_M)
 
 
+def _mut_offsets_start(offsets, total_M):
+    """Reads offsets[g] as the start of group g instead of its end."""
+    owner = np.full(int(total_M), -1, dtype=np.int64)
+    o = np.asarray(offsets, np.int64).tolist() + [total_M]
+    for g in range(len(o) - 1):
+        owner[min(o[g], total_M):min(max(o[g + 1], o[g]), total_M)] = g
+    return owner
+
+
 def _mut_sign(codes):
     return np.abs(og._E4M3FN_TABLE[np.asarray(codes, np.uint8)])
 
@@ -408,6 +509,7 @@ def _mut_truncate(v):
     ("dropped K term", "_accumulate", _mut_dropped_term),
     ("x_scale dropped", "_apply_scales", _mut_no_xscale),
     ("wrong group", "stacked_row_groups", _mut_group_shift),
+    ("offsets read as group starts", "offsets_row_groups", _mut_offsets_start),
     ("sign lost in decode", "decode_e4m3fn", _mut_sign),
     ("bf16 rounding truncates", "bf16_rne_from_f64", _mut_truncate),
 ])
