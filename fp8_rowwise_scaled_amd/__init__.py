@@ -3,10 +3,24 @@
 The computation lives in the HIP library libfp8gg.so (C ABI: include/fp8gg.h);
 this package holds its sources (csrc/), the build step and a thin binding.
 """
-from ._lib import LAYOUT_PADDED, LAYOUT_STACKED, SHUFFLE_K, SHUFFLE_N, last_error, load, plan  # noqa: F401
+from ._lib import (  # noqa: F401
+    LAYOUT_BATCHED,
+    LAYOUT_OFFSETS,
+    LAYOUT_PADDED,
+    LAYOUT_STACKED,
+    SHUFFLE_K,
+    SHUFFLE_N,
+    last_error,
+    load,
+    plan,
+)
 from .ops import (  # noqa: F401
+    f8f8bf16_rowwise_grouped_batched,
+    f8f8bf16_rowwise_grouped_batched_preshuffle,
     f8f8bf16_rowwise_grouped_dynamic,
     f8f8bf16_rowwise_grouped_dynamic_preshuffle,
+    f8f8bf16_rowwise_grouped_offsets,
+    f8f8bf16_rowwise_grouped_offsets_preshuffle,
     f8f8bf16_rowwise_grouped_stacked,
     f8f8bf16_rowwise_grouped_stacked_preshuffle,
     f8f8bf16_shuffle_b,

@@ -14,6 +14,8 @@ ERR_HIP = 3
 
 LAYOUT_STACKED = 0
 LAYOUT_PADDED = 1
+LAYOUT_OFFSETS = 2
+LAYOUT_BATCHED = 3
 SHUFFLE_N = 32
 SHUFFLE_K = 64
 
@@ -23,6 +25,10 @@ EXPORTS = (
     "f8f8bf16_rowwise_grouped_dynamic",
     "f8f8bf16_rowwise_grouped_stacked_preshuffle",
     "f8f8bf16_rowwise_grouped_dynamic_preshuffle",
+    "f8f8bf16_rowwise_grouped_offsets",
+    "f8f8bf16_rowwise_grouped_offsets_preshuffle",
+    "f8f8bf16_rowwise_grouped_batched",
+    "f8f8bf16_rowwise_grouped_batched_preshuffle",
     "f8f8bf16_shuffle_b",
     "f8f8bf16_last_error",
     "f8f8bf16_plan",
@@ -71,9 +77,14 @@ def load() -> ctypes.CDLL:
     lib.f8f8bf16_rowwise_grouped_stacked_preshuffle.argtypes = gemm + [P]
     lib.f8f8bf16_rowwise_grouped_dynamic.argtypes = gemm + [I, P]
     lib.f8f8bf16_rowwise_grouped_dynamic_preshuffle.argtypes = gemm + [I, P]
-    for name in ("f8f8bf16_rowwise_grouped_stacked", "f8f8bf16_rowwise_grouped_stacked_preshuffle",
-                 "f8f8bf16_rowwise_grouped_dynamic", "f8f8bf16_rowwise_grouped_dynamic_preshuffle"):
-        getattr(lib, name).restype = I
+    lib.f8f8bf16_rowwise_grouped_offsets.argtypes = gemm + [P]
+    lib.f8f8bf16_rowwise_grouped_offsets_preshuffle.argtypes = gemm + [P]
+    batched = [P, P, P, P, P, I64, I64, I64, I64, P]
+    lib.f8f8bf16_rowwise_grouped_batched.argtypes = batched
+    lib.f8f8bf16_rowwise_grouped_batched_preshuffle.argtypes = batched
+    for name in EXPORTS:
+        if name.startswith("f8f8bf16_rowwise_grouped_"):
+            getattr(lib, name).restype = I
     lib.f8f8bf16_shuffle_b.argtypes = [P, P, I64, I64, I64, P]
     lib.f8f8bf16_shuffle_b.restype = I
     lib.f8f8bf16_last_error.argtypes = []

@@ -60,9 +60,14 @@ int env_int(const char* name, int dflt) {
   return std::atoi(v);
 }
 
+// Packed layouts put the groups one after another along M (total rows M); slab
+// layouts give each group M rows (total rows G * M).
+bool packed(int layout) { return layout == FP8GG_LAYOUT_STACKED || layout == FP8GG_LAYOUT_OFFSETS; }
+int64_t total_rows(int layout, int64_t G, int64_t M) { return packed(layout) ? M : G * M; }
+
 // Shape checks shared by plan() and the entry points.
 fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
-  if (layout != FP8GG_LAYOUT_STACKED && layout != FP8GG_LAYOUT_PADDED)
+  if (layout < FP8GG_LAYOUT_STACKED || layout > FP8GG_LAYOUT_BATCHED)
     return fail(FP8GG_ERR_INVALID_ARGUMENT, "unknown layout %d", layout);
   if (G < 0 || M < 0 || N < 0 || K < 0)
     return fail(FP8GG_ERR_INVALID_ARGUMENT, "negative size (G=%lld M=%lld N=%lld K=%lld)", (long long)G,
@@ -78,11 +83,11 @@ fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int6
   const int64_t lim = (int64_t(1) << 31) - 256;
   if (K > lim || N > lim || M > lim || G > lim)
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "a dimension exceeds 2^31-256");
-  if (layout == FP8GG_LAYOUT_PADDED && G * M > lim)
-    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "G*expected_m exceeds 2^31-256");
+  if (!packed(layout) && G * M > lim)
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "G*M exceeds 2^31-256 (G times the slab height)");
   // Every tensor's byte count (and so every 64-bit offset the kernels form) stays
   // far below overflow; 2^48 bytes is beyond any device memory.
-  const int64_t rows = layout == FP8GG_LAYOUT_STACKED ? M : G * M;
+  const int64_t rows = total_rows(layout, G, M);
   const int64_t cap = int64_t(1) << 48;
   auto too_big = [cap](int64_t a, int64_t b) { return a > 0 && b > cap / a; };
   if (too_big(rows, K) || too_big(G, N) || (G * N > 0 && too_big(G * N, K)) || too_big(rows, 2 * N))
@@ -93,19 +98,21 @@ fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int6
 
 // Fixed selector (measured on MI355X; no benchmarking inside a call).  The key is
 // the rows one group contributes on average -- total_M normalised by G for the
-// stacked layout -- because a tile only ever sees one group.
+// packed layouts, the slab height otherwise -- because a tile only ever sees one
+// group.
 // Compute units the selector plans for (MI355X).  Only a heuristic: the persistent
 // grid itself is sized from the device at launch.
 constexpr int64_t kPlanCus = 256;
 
 int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
   (void)K;
-  const int64_t per_group = layout == FP8GG_LAYOUT_STACKED ? (G > 0 ? (M + G - 1) / G : M) : M;
-  const bool stacked = layout == FP8GG_LAYOUT_STACKED;
-  // Stacked calls with at least 256 rows per group run 256x256 tiles on the
-  // persistent grid (the last round as quarter tiles); with 256 to 511 rows per
-  // group this measured 8% faster than 128x256 tiles (down projection, M = 2048).
-  if (stacked && per_group >= 256) return preshuffled ? 26 : 16;
+  const int64_t per_group = packed(layout) ? (G > 0 ? (M + G - 1) / G : M) : M;
+  const bool slab_with_padding = layout == FP8GG_LAYOUT_PADDED;
+  // Calls with at least 256 rows per group whose tiles are all in use (every
+  // layout but padded) run 256x256 tiles on the persistent grid (the last round as
+  // quarter tiles); with 256 to 511 rows per group this measured 8% faster than
+  // 128x256 tiles (down projection, M = 2048).
+  if (!slab_with_padding && per_group >= 256) return preshuffled ? 26 : 16;
   if (preshuffled) {
     // The same tiles as for plain W, reading pre-shuffled blocks.
     if (per_group >= 512) {
@@ -130,7 +137,7 @@ int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, 
   // rows, so each group's weights are spread over many workgroups (32 columns each,
   // K split over 4 waves, straight to registers).  Otherwise 32-row tiles with a
   // deep LDS pipeline: 32 x 64 for at most two rows per group, 32 x 128 above.
-  const int64_t rows = stacked ? M : G * M;
+  const int64_t rows = total_rows(layout, G, M);
   if (rows < G) return 15;
   if (per_group <= 2) return 21;
   return 18;
@@ -157,13 +164,13 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
   p->config_id = -1;
   fp8gg_status st = check_shape(layout, preshuffled, G, M, N, K);
   if (st != FP8GG_OK) return st;
-  const int64_t rows = layout == FP8GG_LAYOUT_STACKED ? M : G * M;
+  const int64_t rows = total_rows(layout, G, M);
   if (rows == 0 || N == 0) return FP8GG_OK;  // empty output: nothing to launch
   if (K == 0) {
     p->zero_fill = 1;
     return FP8GG_OK;
   }
-  if (G == 0) return FP8GG_OK;  // stacked rows that belong to no group are left untouched
+  if (G == 0) return FP8GG_OK;  // packed rows that belong to no group are left untouched
 
   int cfg = select_config(layout, preshuffled, G, M, N, K);
   if (cfg < 0)
@@ -174,8 +181,8 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
       return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_CONFIG=%d does not name a usable configuration", forced);
     cfg = forced;
   }
-  if (layout != FP8GG_LAYOUT_STACKED && fp8gg::kConfigs[cfg].kind == fp8gg::kKindPersistent)
-    cfg = fp8gg::kConfigs[cfg].twin;   // the persistent schedule covers the stacked layout only
+  if (layout == FP8GG_LAYOUT_PADDED && fp8gg::kConfigs[cfg].kind == fp8gg::kKindPersistent)
+    cfg = fp8gg::kConfigs[cfg].twin;   // the persistent schedule covers the packed and batched layouts
   const fp8gg::KernelConfig& c = fp8gg::kConfigs[cfg];
   p->config_id = cfg;
   p->BM = c.BM;
@@ -186,11 +193,16 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
   p->k_tail = (K % c.BK) != 0;
   p->n_tail = (N % c.BN) != 0;
   p->n_tiles = (N + c.BN - 1) / c.BN;
-  if (layout == FP8GG_LAYOUT_STACKED) {
+  if (packed(layout)) {
     // Sum over groups of ceil(M_g / BM) <= ceil(total_M / BM) + G - 1, and each
     // tile holds at least one row.
     int64_t ub = (M + c.BM - 1) / c.BM + G - 1;
     p->m_tiles = ub < M ? ub : M;
+    p->grid = p->m_tiles * p->n_tiles;
+    p->persistent = c.kind == fp8gg::kKindPersistent ? 1 : 0;
+  } else if (layout == FP8GG_LAYOUT_BATCHED) {
+    // Every group is a full slab: exactly G * ceil(M / BM) tiles.
+    p->m_tiles = G * ((M + c.BM - 1) / c.BM);
     p->grid = p->m_tiles * p->n_tiles;
     p->persistent = c.kind == fp8gg::kKindPersistent ? 1 : 0;
   } else {
@@ -204,13 +216,14 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
   return FP8GG_OK;
 }
 
+// meta: M_sizes or zero_start_index_M (int64), offsets (int32), none (batched).
 fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* WQ, const float* xs,
-                 const float* ws, const int64_t* meta, uint16_t* Y, int64_t G, int64_t M, int64_t N, int64_t K,
+                 const float* ws, const void* meta, uint16_t* Y, int64_t G, int64_t M, int64_t N, int64_t K,
                  int zeroing, void* stream) {
   fp8gg_plan p;
   fp8gg_status st = make_plan(layout, preshuffled, G, M, N, K, &p);
   if (st != FP8GG_OK) return st;
-  const int64_t rows = layout == FP8GG_LAYOUT_STACKED ? M : G * M;
+  const int64_t rows = total_rows(layout, G, M);
   if (rows == 0 || N == 0) return ok();
   if (!Y) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y is null");
   if (!aligned(Y, 16)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y must be 16-byte aligned");
@@ -221,19 +234,22 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
     return ok();
   }
   if (p.config_id < 0) return ok();
-  if (!XQ || !WQ || !xs || !ws || !meta)
+  const bool has_meta = layout != FP8GG_LAYOUT_BATCHED;
+  const int64_t meta_elem = layout == FP8GG_LAYOUT_OFFSETS ? 4 : 8;
+  if (!XQ || !WQ || !xs || !ws || (has_meta && !meta))
     return fail(FP8GG_ERR_INVALID_ARGUMENT, "null input pointer (XQ=%p WQ=%p x_scale=%p w_scale=%p meta=%p)",
-                (const void*)XQ, (const void*)WQ, (const void*)xs, (const void*)ws, (const void*)meta);
+                (const void*)XQ, (const void*)WQ, (const void*)xs, (const void*)ws, meta);
   if (!aligned(XQ, 16) || !aligned(WQ, 16) || !aligned(ws, 16))
     return fail(FP8GG_ERR_INVALID_ARGUMENT, "XQ, WQ and w_scale must be 16-byte aligned");
-  if (!aligned(xs, 4) || !aligned(meta, 8))
-    return fail(FP8GG_ERR_INVALID_ARGUMENT, "x_scale must be 4-byte and the metadata 8-byte aligned");
+  if (!aligned(xs, 4) || (has_meta && !aligned(meta, meta_elem)))
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "x_scale must be 4-byte and the metadata %d-byte aligned",
+                (int)meta_elem);
   const Range out{Y, rows * N * 2, "Y"};
   const Range ins[] = {{XQ, rows * K, "XQ"},
                        {WQ, G * N * K, "WQ"},
                        {xs, rows * 4, "x_scale"},
                        {ws, G * N * 4, "w_scale"},
-                       {meta, G * 8, "metadata"}};
+                       {has_meta ? meta : nullptr, G * meta_elem, "metadata"}};
   for (const Range& r : ins)
     if (overlap(out, r)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y overlaps %s", r.name);
 
@@ -242,7 +258,9 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
   a.W = WQ;
   a.xs = xs;
   a.ws = ws;
-  a.meta = meta;
+  a.meta = layout == FP8GG_LAYOUT_STACKED || layout == FP8GG_LAYOUT_PADDED ? static_cast<const int64_t*>(meta)
+                                                                             : nullptr;
+  a.offs = layout == FP8GG_LAYOUT_OFFSETS ? static_cast<const int32_t*>(meta) : nullptr;
   a.Y = Y;
   a.G = G;
   a.M = M;
@@ -250,7 +268,7 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
   a.K = K;
   a.m_tiles = p.m_tiles;
   a.n_tiles = p.n_tiles;
-  a.zeroing = zeroing ? 1 : 0;
+  a.zeroing = layout == FP8GG_LAYOUT_PADDED && zeroing ? 1 : 0;
   if (env_int("FP8GG_LOG", 0))
     std::fprintf(stderr,
                  "[fp8gg] layout=%d pre=%d G=%lld M=%lld N=%lld K=%lld -> cfg=%d tile=%dx%dx%d thr=%d st=%d "
@@ -269,7 +287,7 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
     const int tail_mode = env_int("FP8GG_TAIL", 0);
     if (tail_mode < 0 || tail_mode > 2) return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_TAIL=%d is not 0, 1 or 2", tail_mode);
     if (env_int("FP8GG_LOG", 0)) std::fprintf(stderr, "[fp8gg] persistent grid %d, tail mode %d\n", P, tail_mode);
-    e = fp8gg::launch_gemm_persistent(p.config_id, p.k_tail != 0, a, P, tail_mode, s);
+    e = fp8gg::launch_gemm_persistent(layout, p.config_id, p.k_tail != 0, a, P, tail_mode, s);
   } else {
     e = fp8gg::launch_gemm(layout, p.config_id, p.k_tail != 0, a, p.grid, s);
   }
@@ -309,6 +327,32 @@ fp8gg_status f8f8bf16_rowwise_grouped_dynamic_preshuffle(const uint8_t* XQ, cons
                                                          int zeroing_output_tensor, void* stream) {
   return run(FP8GG_LAYOUT_PADDED, 1, XQ, WQs, x_scale, w_scale, zero_start_index_M, Y, G, expected_m, N, K,
              zeroing_output_tensor, stream);
+}
+
+fp8gg_status f8f8bf16_rowwise_grouped_offsets(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                              const float* w_scale, const int32_t* offsets, uint16_t* Y,
+                                              int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream) {
+  return run(FP8GG_LAYOUT_OFFSETS, 0, XQ, WQ, x_scale, w_scale, offsets, Y, G, total_M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_rowwise_grouped_offsets_preshuffle(const uint8_t* XQ, const uint8_t* WQs,
+                                                         const float* x_scale, const float* w_scale,
+                                                         const int32_t* offsets, uint16_t* Y, int64_t G,
+                                                         int64_t total_M, int64_t N, int64_t K, void* stream) {
+  return run(FP8GG_LAYOUT_OFFSETS, 1, XQ, WQs, x_scale, w_scale, offsets, Y, G, total_M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_rowwise_grouped_batched(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                              const float* w_scale, uint16_t* Y, int64_t G, int64_t M, int64_t N,
+                                              int64_t K, void* stream) {
+  return run(FP8GG_LAYOUT_BATCHED, 0, XQ, WQ, x_scale, w_scale, nullptr, Y, G, M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_rowwise_grouped_batched_preshuffle(const uint8_t* XQ, const uint8_t* WQs,
+                                                         const float* x_scale, const float* w_scale, uint16_t* Y,
+                                                         int64_t G, int64_t M, int64_t N, int64_t K,
+                                                         void* stream) {
+  return run(FP8GG_LAYOUT_BATCHED, 1, XQ, WQs, x_scale, w_scale, nullptr, Y, G, M, N, K, 0, stream);
 }
 
 fp8gg_status f8f8bf16_shuffle_b(const uint8_t* WQ, uint8_t* WQs, int64_t G, int64_t N, int64_t K,

@@ -8,18 +8,20 @@
 
 namespace fp8gg {
 
-enum Layout : int { kStacked = 0, kPadded = 1 };
+// Values match FP8GG_LAYOUT_* of the public header.
+enum Layout : int { kStacked = 0, kPadded = 1, kOffsets = 2, kBatched = 3 };
 
 // Operands of one grouped GEMM call, as the kernels see them.  Row-major, dense.
 struct GemmArgs {
-  const uint8_t* X;      // stacked: [M, K]; padded: [G * M, K] (M = expected_m)
+  const uint8_t* X;      // stacked, offsets: [M, K]; padded, batched: [G * M, K] (M = slab height)
   const uint8_t* W;      // [G, N, K] (plain) or the pre-shuffled blocks
   const float* xs;       // one scale per row of X
   const float* ws;       // [G, N]
-  const int64_t* meta;   // stacked: M_sizes [G]; padded: zero_start_index_M [G]
+  const int64_t* meta;   // stacked: M_sizes [G]; padded: zero_start_index_M [G]; else unused
+  const int32_t* offs;   // offsets: inclusive row prefix [G]; else unused
   uint16_t* Y;           // bf16 bits, one row per row of X, N columns
   int64_t G, M, N, K;
-  int64_t m_tiles;       // stacked: upper bound of M tiles over all groups; padded: per slab
+  int64_t m_tiles;       // packed: upper bound of M tiles over all groups; padded: per slab
   int64_t n_tiles;
   int32_t zeroing;       // padded: write zeros into padding rows
 };
@@ -33,7 +35,7 @@ struct KernelConfig {
   int stages;   // LDS pipeline depth (X and W; X only when W is pre-shuffled)
   int kind;     // 0: X and W through LDS; 3: small M, W and X straight to registers with
                 // K split across waves; 4: kind 0 on a persistent grid whose last round
-                // may run as quarter tiles (stacked layout)
+                // may run as quarter tiles (packed layouts)
   int wdepth;   // kind 3: K steps of fragments held in flight in registers
   int twin;     // kind 4: the kind-0 configuration with the same tile (used for the padded layout)
   int pre;      // 1: W pre-shuffled by f8f8bf16_shuffle_b (the _preshuffle entry points)
@@ -64,8 +66,8 @@ inline int lds_bytes(const KernelConfig& c) {
 
 hipError_t launch_gemm(int layout, int config_id, bool k_tail, const GemmArgs& args,
                        int64_t grid, hipStream_t stream);
-hipError_t launch_gemm_persistent(int config_id, bool k_tail, const GemmArgs& args, int grid, int tail_mode,
-                                  hipStream_t stream);
+hipError_t launch_gemm_persistent(int layout, int config_id, bool k_tail, const GemmArgs& args, int grid,
+                                  int tail_mode, hipStream_t stream);
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t stream);
 hipError_t launch_shuffle_b(const uint8_t* W, uint8_t* Ws, int64_t G, int64_t N, int64_t K,
                             hipStream_t stream);

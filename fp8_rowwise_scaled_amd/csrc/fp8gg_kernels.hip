@@ -9,8 +9,11 @@
 //     K loop and epilogue are shared (Design notes, "one kernel, not six");
 //   * stacked layout: the host launches an upper bound of M tiles and each tile
 //     finds its group from the device-side row counts or retires (commit on
-//     self-retiring tiles); padded layout: the group is a grid coordinate and the
-//     row base a multiple of expected_m (commit adding the padded layout);
+//     self-retiring tiles); offsets layout: the same walk over an int32 inclusive
+//     prefix (commit adding the offsets layout); padded layout: the group is a grid
+//     coordinate and the row base a multiple of expected_m (commit adding the
+//     padded layout); batched layout: every group a full slab, so the group and
+//     row base are arithmetic (commit adding the batched layout);
 //   * K-tail: K need only be a multiple of 16 bytes; chunks past K read as zero
 //     (commit on the K-tail variant); N-tail: W rows past N are not used and stores
 //     past N are dropped, predicated on the last column of each store (commits on
@@ -144,45 +147,74 @@ struct Tile {
   int64_t zero_end;   // rows [row_end, zero_end) are written as zero
 };
 
-// Counts of groups g0 .. g0+7 (indices past G read group G-1 and are ignored by the
-// callers).  A whole block of eight in bounds is read as one 64-byte struct, which
-// the compiler turns into a single scalar load.
-struct alignas(8) Counts8 {
-  int64_t v[8];
+// Metadata of groups g0 .. g0+7 (indices past G read group G-1 and are ignored by
+// the callers).  A whole block of eight in bounds is read as one struct, which the
+// compiler turns into a single scalar load.
+template <typename T>
+struct alignas(8) Meta8 {
+  T v[8];
 };
-__device__ __forceinline__ void load_counts8(const int64_t* meta, int64_t g0, int64_t G, int64_t (&cnt)[8]) {
+template <typename T>
+__device__ __forceinline__ void load_meta8(const T* meta, int64_t g0, int64_t G, int64_t (&out)[8]) {
   if (g0 + 8 <= G) {
-    const Counts8 c = *reinterpret_cast<const Counts8*>(meta + g0);
+    const Meta8<T> c = *reinterpret_cast<const Meta8<T>*>(meta + g0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) cnt[i] = c.v[i];
+    for (int i = 0; i < 8; ++i) out[i] = c.v[i];
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) cnt[i] = meta[g0 + i < G ? g0 + i : G - 1];
+    for (int i = 0; i < 8; ++i) out[i] = meta[g0 + i < G ? g0 + i : G - 1];
   }
 }
 
-// Stacked: walk the groups with a running row prefix and tile prefix.  Counts are
-// clamped (negative -> 0, cumulative end -> M), so any metadata stays in bounds.
-// Each block of eight counts is fetched, and its row ends and tile counts are
-// computed, before the search looks at any of them: a call pays one memory round
-// trip per eight groups before its first operand load (a search that could stop
-// early would let the compiler fetch the counts one by one, each behind a wait).
-template <int BM>
-__device__ __forceinline__ bool resolve_stacked(const GemmArgs& a, int64_t m_tile, Tile& t) {
+// Row ends of groups g0 .. g0+7 of a packed layout, given the end s0 of group
+// g0 - 1, clamped so that any metadata stays in bounds: stacked, from int64 row
+// counts (negative -> 0, cumulative end -> M); offsets, from the int32 inclusive
+// prefix (an end below the previous one -> empty group, past M -> M).  Groups past
+// G end where the last one did.
+template <int LAYOUT>
+__device__ __forceinline__ void packed_ends8(const GemmArgs& a, int64_t g0, int64_t s0, int64_t (&end)[8]) {
+  int64_t v[8];
+  if constexpr (LAYOUT == kOffsets) load_meta8(a.offs, g0, a.G, v);
+  else load_meta8(a.meta, g0, a.G, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int64_t e;
+    if constexpr (LAYOUT == kOffsets) e = v[i] > s0 ? v[i] : s0;
+    else e = s0 + (v[i] > 0 ? v[i] : 0);
+    e = e > a.M ? a.M : e;
+    e = g0 + i < a.G ? e : s0;
+    end[i] = e;
+    s0 = e;
+  }
+}
+
+// Packed layouts (stacked, offsets): walk the groups with a running row prefix and
+// tile prefix.  Each block of eight groups is fetched, and its row ends and tile
+// counts are computed, before the search looks at any of them: a call pays one
+// memory round trip per eight groups before its first operand load (a search that
+// could stop early would let the compiler fetch the metadata one entry at a time,
+// each behind a wait).  Batched: every group is a full slab of M rows, so the
+// group and row base are arithmetic (no metadata).
+template <int LAYOUT, int BM>
+__device__ __forceinline__ bool resolve_packed(const GemmArgs& a, int64_t m_tile, Tile& t) {
+  if constexpr (LAYOUT == kBatched) {
+    const int64_t per = (a.M + BM - 1) / BM;
+    if (per == 0 || m_tile >= a.G * per) return false;
+    t.g = m_tile / per;
+    t.row_base = t.g * a.M + (m_tile % per) * BM;
+    t.row_end = t.g * a.M + a.M;
+    t.zero_end = t.row_end;
+    return true;
+  }
   int64_t start = 0, tiles_before = 0;
   for (int64_t g0 = 0; g0 < a.G; g0 += 8) {
-    int64_t cnt[8];
-    load_counts8(a.meta, g0, a.G, cnt);
     int64_t end[8], tiles[8];
+    packed_ends8<LAYOUT>(a, g0, start, end);
     int64_t s0 = start;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t c = (g0 + i < a.G && cnt[i] > 0) ? cnt[i] : 0;
-      int64_t e = s0 + c;
-      e = e > a.M ? a.M : e;
-      tiles[i] = (e - s0 + BM - 1) / BM;
-      end[i] = e;
-      s0 = e;
+      tiles[i] = (end[i] - s0 + BM - 1) / BM;
+      s0 = end[i];
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -618,10 +650,10 @@ gg_lds_kernel(GemmArgs a) {
   const int64_t n_tile = bid % a.n_tiles;
   const int64_t rest = bid / a.n_tiles;
   Tile t;
-  if (LAYOUT == kStacked) {
-    if (!resolve_stacked<BM>(a, rest, t)) return;
-  } else {
+  if (LAYOUT == kPadded) {
     if (!resolve_padded<BM>(a, rest / a.m_tiles, rest % a.m_tiles, t)) return;
+  } else {
+    if (!resolve_packed<LAYOUT, BM>(a, rest, t)) return;
   }
   const int64_t n0 = n_tile * BN;
   if (t.row_base >= t.row_end) {
@@ -645,26 +677,24 @@ gg_lds_kernel(GemmArgs a) {
   e.epilogue(a, t, n0, acc);
 }
 
-// Number of M tiles over all groups (stacked layout), with the resolver's clamping.
-template <int BM>
+// Number of M tiles over all groups of a packed layout, with the resolver's clamping.
+template <int LAYOUT, int BM>
 __device__ __forceinline__ int64_t count_m_tiles(const GemmArgs& a) {
+  if constexpr (LAYOUT == kBatched) return a.G * ((a.M + BM - 1) / BM);
   int64_t start = 0, tiles = 0;
   for (int64_t g0 = 0; g0 < a.G; g0 += 8) {
-    int64_t cnt[8];
-    load_counts8(a.meta, g0, a.G, cnt);
+    int64_t end[8];
+    packed_ends8<LAYOUT>(a, g0, start, end);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int64_t c = (g0 + i < a.G && cnt[i] > 0) ? cnt[i] : 0;
-      int64_t end = start + c;
-      end = end > a.M ? a.M : end;
-      tiles += (end - start + BM - 1) / BM;
-      start = end;
+      tiles += (end[i] - start + BM - 1) / BM;
+      start = end[i];
     }
   }
   return tiles;
 }
 
-// Persistent kernel (stacked layout).
+// Persistent kernel (packed layouts: stacked, offsets, batched).
 //
 // Schedule.  A grid of P workgroups, one per compute unit, walks the T output
 // tiles in data-parallel order: workgroup w computes whole tiles w, w + P, ...
@@ -691,7 +721,7 @@ __device__ __forceinline__ int64_t count_m_tiles(const GemmArgs& a) {
 //
 // tail_mode: 0 chooses quarters by the rule above, 1 never uses them, 2 always
 // does when rem > 0.
-template <typename E>
+template <int LAYOUT, typename E>
 __device__ __forceinline__ void persistent_whole_tiles(const GemmArgs& a, int64_t w, int64_t P, int64_t whole,
                                                        int nk, uint8_t* smem, float (*scales)[E::SCALE_FLOATS],
                                                        float* scale_dummy) {
@@ -717,7 +747,7 @@ __device__ __forceinline__ void persistent_whole_tiles(const GemmArgs& a, int64_
     it.tile = next;
     it.seq = seq;
     next += P;
-    resolve_stacked<E::BM_>(a, it.tile / a.n_tiles, it.t);
+    resolve_packed<LAYOUT, E::BM_>(a, it.tile / a.n_tiles, it.t);
     it.n0 = (it.tile % a.n_tiles) * E::BN_;
     return true;
   };
@@ -808,7 +838,7 @@ __device__ __forceinline__ void persistent_whole_tiles(const GemmArgs& a, int64_
   }
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PRE>
+template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PRE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gg_persistent_kernel(GemmArgs a, int tail_mode) {
   typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL, PRE> E;
@@ -824,17 +854,17 @@ gg_persistent_kernel(GemmArgs a, int tail_mode) {
   const int64_t P = gridDim.x;
   const int64_t w = blockIdx.x;
   const int nk = (int)((a.K + BK - 1) / BK);
-  const int64_t T = count_m_tiles<BM>(a) * a.n_tiles;
+  const int64_t T = count_m_tiles<LAYOUT, BM>(a) * a.n_tiles;
   const int64_t rem = tail_quarters(T, P, tail_mode) ? T % P : 0;
   const int64_t whole = T - rem;
 
-  persistent_whole_tiles<E>(a, w, P, whole, nk, smem, scales, scale_dummy);
+  persistent_whole_tiles<LAYOUT, E>(a, w, P, whole, nk, smem, scales, scale_dummy);
 
   for (int64_t qn = w; qn < 4 * rem; qn += P) {
     const int64_t tile = whole + qn / 4;
     const int q = (int)(qn % 4);
     Tile t;
-    resolve_stacked<BM>(a, tile / a.n_tiles, t);
+    resolve_packed<LAYOUT, BM>(a, tile / a.n_tiles, t);
     t.row_base += (q >> 1) * (BM / 2);
     const int64_t n0 = (tile % a.n_tiles) * BN + (q & 1) * (BN / 2);
     if (t.row_base >= t.row_end || n0 >= a.N) continue;
@@ -919,10 +949,10 @@ gg_skinny_kernel(GemmArgs a) {
   const int64_t n_tile = bid % a.n_tiles;
   const int64_t rest = bid / a.n_tiles;
   Tile t;
-  if (LAYOUT == kStacked) {
-    if (!resolve_stacked<BM>(a, rest, t)) return;
-  } else {
+  if (LAYOUT == kPadded) {
     if (!resolve_padded<BM>(a, rest / a.m_tiles, rest % a.m_tiles, t)) return;
+  } else {
+    if (!resolve_packed<LAYOUT, BM>(a, rest, t)) return;
   }
   const int64_t N = a.N;
   const int64_t K = a.K;
@@ -1087,7 +1117,7 @@ __global__ void __launch_bounds__(256) zero_fill_kernel(v4i* __restrict__ y, int
 // kind: 0 = both operands through LDS (one tile per workgroup),
 //       3 = small M: W and X straight to registers, K split across the 4 waves,
 //       4 = kind 0 on a persistent grid whose last round may run as quarter tiles
-//           (stacked layout).
+//           (packed layouts: stacked, offsets, batched).
 // pre: 1 = W pre-shuffled (the _preshuffle entry points), 0 = plain W.
 //                      BM   BN   BK  WM WN stages kind wdepth twin pre
 const KernelConfig kConfigs[] = {
@@ -1134,15 +1164,15 @@ static hipError_t launch_lds(bool k_tail, const GemmArgs& a, int64_t grid, hipSt
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int WM, int WN, int STAGES, bool PRE = false>
+template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool PRE = false>
 static hipError_t launch_persistent(bool k_tail, const GemmArgs& a, int grid, int tail_mode, hipStream_t s) {
   const dim3 block(WM * WN * 64);
   if (k_tail)
-    hipLaunchKernelGGL((gg_persistent_kernel<BM, BN, BK, WM, WN, STAGES, true, PRE>), dim3((uint32_t)grid), block, 0,
-                       s, a, tail_mode);
+    hipLaunchKernelGGL((gg_persistent_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, true, PRE>), dim3((uint32_t)grid),
+                       block, 0, s, a, tail_mode);
   else
-    hipLaunchKernelGGL((gg_persistent_kernel<BM, BN, BK, WM, WN, STAGES, false, PRE>), dim3((uint32_t)grid), block,
-                       0, s, a, tail_mode);
+    hipLaunchKernelGGL((gg_persistent_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, false, PRE>), dim3((uint32_t)grid),
+                       block, 0, s, a, tail_mode);
   return hipGetLastError();
 }
 
@@ -1189,20 +1219,36 @@ static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, i
   }
 }
 
-hipError_t launch_gemm_persistent(int config_id, bool k_tail, const GemmArgs& a, int grid, int tail_mode,
-                                  hipStream_t s) {
+template <int LAYOUT>
+static hipError_t launch_persistent_layout(int config_id, bool k_tail, const GemmArgs& a, int grid, int tail_mode,
+                                           hipStream_t s) {
   switch (config_id) {
-    case 16: return launch_persistent<256, 256, 128, 2, 4, 2>(k_tail, a, grid, tail_mode, s);
-    case 17: return launch_persistent<128, 256, 128, 2, 4, 3>(k_tail, a, grid, tail_mode, s);
-    case 26: return launch_persistent<256, 256, 128, 2, 4, 2, true>(k_tail, a, grid, tail_mode, s);
+    case 16: return launch_persistent<LAYOUT, 256, 256, 128, 2, 4, 2>(k_tail, a, grid, tail_mode, s);
+    case 17: return launch_persistent<LAYOUT, 128, 256, 128, 2, 4, 3>(k_tail, a, grid, tail_mode, s);
+    case 26: return launch_persistent<LAYOUT, 256, 256, 128, 2, 4, 2, true>(k_tail, a, grid, tail_mode, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_persistent(int layout, int config_id, bool k_tail, const GemmArgs& a, int grid,
+                                  int tail_mode, hipStream_t s) {
+  switch (layout) {
+    case kStacked: return launch_persistent_layout<kStacked>(config_id, k_tail, a, grid, tail_mode, s);
+    case kOffsets: return launch_persistent_layout<kOffsets>(config_id, k_tail, a, grid, tail_mode, s);
+    case kBatched: return launch_persistent_layout<kBatched>(config_id, k_tail, a, grid, tail_mode, s);
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gemm(int layout, int config_id, bool k_tail, const GemmArgs& a, int64_t grid,
                        hipStream_t s) {
-  if (layout == kStacked) return launch_layout<kStacked>(config_id, k_tail, a, grid, s);
-  return launch_layout<kPadded>(config_id, k_tail, a, grid, s);
+  switch (layout) {
+    case kStacked: return launch_layout<kStacked>(config_id, k_tail, a, grid, s);
+    case kPadded: return launch_layout<kPadded>(config_id, k_tail, a, grid, s);
+    case kOffsets: return launch_layout<kOffsets>(config_id, k_tail, a, grid, s);
+    case kBatched: return launch_layout<kBatched>(config_id, k_tail, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t s) {

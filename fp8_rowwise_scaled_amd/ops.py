@@ -36,7 +36,7 @@ def _stream(dev: torch.device) -> int:
     return torch.cuda.current_stream(dev).cuda_stream
 
 
-def _stacked(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out):
+def _stacked(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out, meta_name="M_sizes", meta_dtype=torch.int64):
     XQ = _bytes(XQ, "XQ")
     WQ = _bytes(WQ, "WQ")
     if XQ.dim() != 2 or WQ.dim() != 3:
@@ -49,7 +49,7 @@ def _stacked(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out):
     _check(WQ, "WQ", torch.uint8, (G, N, K))
     _check(x_scale, "x_scale", torch.float32, (total_M,))
     _check(w_scale, "w_scale", torch.float32, (G, N))
-    _check(M_sizes, "M_sizes", torch.int64, (G,))
+    _check(M_sizes, meta_name, meta_dtype, (G,))
     if out is None:
         out = torch.empty((total_M, N), dtype=torch.bfloat16, device=XQ.device)
     _check(out, "out", torch.bfloat16, (total_M, N))
@@ -107,6 +107,53 @@ def f8f8bf16_rowwise_grouped_dynamic_preshuffle(XQ, WQs, x_scale, w_scale, zero_
     """As the dynamic op, with WQs produced by f8f8bf16_shuffle_b."""
     return _dynamic("f8f8bf16_rowwise_grouped_dynamic_preshuffle", XQ, WQs, x_scale, w_scale,
                     zero_start_index_M, zeroing_output_tensor, out)
+
+
+def _batched(fn_name, XQ, WQ, x_scale, w_scale, out):
+    XQ = _bytes(XQ, "XQ")
+    WQ = _bytes(WQ, "WQ")
+    if XQ.dim() != 3 or WQ.dim() != 3:
+        raise ValueError("XQ must be [G, M, K] and WQ [G, N, K]")
+    G, M, K = XQ.shape
+    G2, N, K2 = WQ.shape
+    if G2 != G or K2 != K:
+        raise ValueError(f"shape mismatch: XQ {tuple(XQ.shape)} vs WQ {tuple(WQ.shape)}")
+    _check(XQ, "XQ", torch.uint8, (G, M, K))
+    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _check(x_scale, "x_scale", torch.float32, (G, M))
+    _check(w_scale, "w_scale", torch.float32, (G, N))
+    if out is None:
+        out = torch.empty((G, M, N), dtype=torch.bfloat16, device=XQ.device)
+    _check(out, "out", torch.bfloat16, (G, M, N))
+    lib = _lib.load()
+    st = getattr(lib, fn_name)(XQ.data_ptr(), WQ.data_ptr(), x_scale.data_ptr(), w_scale.data_ptr(),
+                               out.data_ptr(), G, M, N, K, _stream(XQ.device))
+    _lib.check(st, fn_name)
+    return out
+
+
+def f8f8bf16_rowwise_grouped_offsets(XQ, WQ, x_scale, w_scale, offsets, out=None):
+    """Y [total_M, N] bf16 for the offsets layout: offsets [G] int32 inclusive
+    prefix sums of the group row counts (see include/fp8gg.h)."""
+    return _stacked("f8f8bf16_rowwise_grouped_offsets", XQ, WQ, x_scale, w_scale, offsets, out,
+                    "offsets", torch.int32)
+
+
+def f8f8bf16_rowwise_grouped_offsets_preshuffle(XQ, WQs, x_scale, w_scale, offsets, out=None):
+    """As the offsets op, with WQs produced by f8f8bf16_shuffle_b."""
+    return _stacked("f8f8bf16_rowwise_grouped_offsets_preshuffle", XQ, WQs, x_scale, w_scale, offsets, out,
+                    "offsets", torch.int32)
+
+
+def f8f8bf16_rowwise_grouped_batched(XQ, WQ, x_scale, w_scale, out=None):
+    """Y [G, M, N] bf16 for the batched layout: every group a full slab of M rows
+    (see include/fp8gg.h)."""
+    return _batched("f8f8bf16_rowwise_grouped_batched", XQ, WQ, x_scale, w_scale, out)
+
+
+def f8f8bf16_rowwise_grouped_batched_preshuffle(XQ, WQs, x_scale, w_scale, out=None):
+    """As the batched op, with WQs produced by f8f8bf16_shuffle_b."""
+    return _batched("f8f8bf16_rowwise_grouped_batched_preshuffle", XQ, WQs, x_scale, w_scale, out)
 
 
 def f8f8bf16_shuffle_b(WQ, out=None):

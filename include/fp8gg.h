@@ -105,6 +105,39 @@ fp8gg_status f8f8bf16_rowwise_grouped_dynamic(
     int zeroing_output_tensor, void* stream);
 
 /*
+ * Offsets layout (MSLK #471: commit adding the offsets layout; commit mapping the
+ * grouped mm op's 2D-3D operand ranks onto it).  Groups are concatenated along M
+ * as in the stacked layout, but their boundaries come as an inclusive prefix
+ * sum: group g owns rows [offsets[g-1], offsets[g]) of XQ / x_scale / Y, with
+ * offsets[-1] = 0.
+ *
+ *   XQ, WQ, x_scale, w_scale, Y   as in the stacked layout
+ *   offsets   [G]   int32 inclusive prefix sums of the group row counts, on the device
+ *
+ * Group g ends at min(max(offsets[g], end of group g-1), total_M): an offset below
+ * its predecessor gives an empty group.  Rows past the last end are not written.
+ */
+fp8gg_status f8f8bf16_rowwise_grouped_offsets(
+    const uint8_t* XQ, const uint8_t* WQ, const float* x_scale, const float* w_scale,
+    const int32_t* offsets, uint16_t* Y,
+    int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
+
+/*
+ * Batched layout (MSLK #471: commit adding the batched layout; the grouped mm
+ * op's 3D-3D ranks).  Every group owns a full slab of M rows, all of them valid;
+ * there is no row metadata.
+ *
+ *   XQ        [G, M, K]   fp8 e4m3fn
+ *   WQ        [G, N, K]   fp8 e4m3fn
+ *   x_scale   [G, M]      fp32
+ *   w_scale   [G, N]      fp32
+ *   Y         [G, M, N]   bf16, every row written
+ */
+fp8gg_status f8f8bf16_rowwise_grouped_batched(
+    const uint8_t* XQ, const uint8_t* WQ, const float* x_scale, const float* w_scale,
+    uint16_t* Y, int64_t G, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Pre-shuffled weights (MSLK #471: commit registering the stacked op and its
  * preshuffle sibling; Design notes on preshuffled B: offered only where each
  * group owns a whole [N, K]).  WQs is WQ rearranged once by f8f8bf16_shuffle_b
@@ -126,6 +159,15 @@ fp8gg_status f8f8bf16_rowwise_grouped_dynamic_preshuffle(
     const int64_t* zero_start_index_M, uint16_t* Y,
     int64_t G, int64_t expected_m, int64_t N, int64_t K,
     int zeroing_output_tensor, void* stream);
+
+fp8gg_status f8f8bf16_rowwise_grouped_offsets_preshuffle(
+    const uint8_t* XQ, const uint8_t* WQs, const float* x_scale, const float* w_scale,
+    const int32_t* offsets, uint16_t* Y,
+    int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
+
+fp8gg_status f8f8bf16_rowwise_grouped_batched_preshuffle(
+    const uint8_t* XQ, const uint8_t* WQs, const float* x_scale, const float* w_scale,
+    uint16_t* Y, int64_t G, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
  * Rearranges WQ [G, N, K] into the pre-shuffled order WQs (same size, must not
@@ -164,9 +206,10 @@ typedef struct {
                          schedule                                                   */
 } fp8gg_plan;
 
-enum { FP8GG_LAYOUT_STACKED = 0, FP8GG_LAYOUT_PADDED = 1 };
+enum { FP8GG_LAYOUT_STACKED = 0, FP8GG_LAYOUT_PADDED = 1, FP8GG_LAYOUT_OFFSETS = 2, FP8GG_LAYOUT_BATCHED = 3 };
 
-/* M is total_M for the stacked layout and expected_m for the padded one.
+/* M is total_M for the stacked and offsets layouts, expected_m for the padded one
+ * and the slab height for the batched one.
  * Performs the same shape checks as the GEMM entry points. */
 fp8gg_status f8f8bf16_plan(int layout, int preshuffled, int64_t G, int64_t M,
                            int64_t N, int64_t K, fp8gg_plan* out);

@@ -22,7 +22,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 8
+    assert len(names) == 12
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -35,6 +35,29 @@ def test_plan_gate_up():
     assert p["m_tiles"] == min(-(-4096 // p["BM"]) + 7, 4096)
     assert p["n_tiles"] == -(-4096 // p["BN"])
     assert p["grid"] == p["m_tiles"] * p["n_tiles"]
+
+
+def test_plan_offsets_matches_stacked():
+    for args in [(8, 4096, 4096, 7168), (8, 2048, 7168, 2048), (8, 32, 7168, 2048), (16, 3, 512, 256)]:
+        for pre in (False, True):
+            assert F.plan(F.LAYOUT_OFFSETS, pre, *args) == F.plan(F.LAYOUT_STACKED, pre, *args)
+
+
+def test_plan_batched_is_exact():
+    G, M, N, K = 4, 512, 8192, 28672
+    p = F.plan(F.LAYOUT_BATCHED, False, G, M, N, K)
+    assert p["persistent"] == 1
+    assert p["m_tiles"] == G * -(-M // p["BM"])
+    assert p["grid"] == p["m_tiles"] * p["n_tiles"]
+    q = F.plan(F.LAYOUT_BATCHED, False, 16, 40, 1024, 512)
+    assert q["persistent"] == 0 and q["m_tiles"] == 16 * -(-40 // q["BM"])
+
+
+def test_plan_refuses_unknown_layout():
+    with pytest.raises(ValueError):
+        F.plan(4, False, 1, 1, 8, 16)
+    with pytest.raises(ValueError):
+        F.plan(-1, False, 1, 1, 8, 16)
 
 
 def test_plan_padded_tails():
