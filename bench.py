@@ -33,8 +33,8 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 MALL_BYTES = 256 * 2 ** 20    # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
-WORKLOADS = ["moe_gate_up", "tiny_stacked", "dense_expert", "dense_expert_preshuffle", "padded_tails"] + [
-    f"moe_down_M{m}" for m in (1, 8, 32, 256, 2048, 8192)]
+WORKLOADS = ["moe_gate_up", "tiny_stacked", "dense_expert", "dense_expert_preshuffle", "padded_tails",
+             "moe_gate_up_offsets", "dense_expert_batched"] + [f"moe_down_M{m}" for m in (1, 8, 32, 256, 2048, 8192)]
 
 
 def log(*a):
@@ -53,6 +53,16 @@ def make_workload(name):
         return wl.dense_expert(), "stacked", True
     if name == "padded_tails":
         return wl.padded_tails(), "padded", False
+    if name == "moe_gate_up_offsets":
+        # the same inputs, group boundaries given as an int32 inclusive prefix sum
+        w = wl.moe_gate_up()
+        w.name += "_offsets"
+        return w, "offsets", False
+    if name == "dense_expert_batched":
+        # every group a full slab of 512 rows: the batched (3D-3D) layout
+        w = wl.dense_expert()
+        w.name += "_batched"
+        return w, "batched", False
     if name.startswith("moe_down_M"):
         return wl.moe_down(int(name[len("moe_down_M"):])), "stacked", False
     raise ValueError(name)
@@ -66,7 +76,7 @@ def algorithmic_work(w, layout):
     padding inputs are not counted."""
     import numpy as np
     G, N, K = w.G, w.N, w.K
-    if layout == "stacked":
+    if layout in ("stacked", "offsets", "batched"):
         sizes = np.clip(w.M_sizes, 0, None)
         R = int(min(sizes.sum(), w.total_M))
         G_ne = int(np.count_nonzero(sizes))
@@ -79,6 +89,12 @@ def algorithmic_work(w, layout):
     flop = 2 * N * K * R
     nbytes = R * K + G_ne * N * K + 4 * R + 4 * G_ne * N + 2 * N * R_out + 8 * G
     return flop, nbytes, R, G_ne
+
+
+def offsets_of(w):
+    """int32 inclusive prefix sums of a stacked workload's group row counts."""
+    import numpy as np
+    return np.cumsum(np.clip(w.M_sizes, 0, None)).astype(np.int32)
 
 
 def kernel_source_hash():
@@ -119,6 +135,11 @@ def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=3):
         t0 = time.perf_counter()
         if layout == "stacked":
             oracle.grouped_stacked(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
+        elif layout == "offsets":
+            oracle.grouped_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, offsets_of(w))
+        elif layout == "batched":
+            M = w.total_M // w.G
+            oracle.grouped_batched(w.XQ.reshape(w.G, M, w.K), w.WQ, w.x_scale.reshape(w.G, M), w.w_scale)
         else:
             oracle.grouped_dynamic(w.XQ, w.WQ, w.x_scale, w.w_scale, w.zero_start_index_M, True)
         times.append(time.perf_counter() - t0)
@@ -225,22 +246,40 @@ def main():
     Wt = torch.from_numpy(w.WQ).to(dev)
     xs = torch.from_numpy(w.x_scale).to(dev)
     ws = torch.from_numpy(w.w_scale).to(dev)
-    meta = torch.from_numpy(w.M_sizes if layout == "stacked" else w.zero_start_index_M).to(dev)
+    if layout == "offsets":
+        meta = torch.from_numpy(offsets_of(w)).to(dev)
+    elif layout == "batched":
+        meta = torch.zeros(1, dtype=torch.int64, device=dev)   # the batched layout has no metadata
+        Gb, Mb = w.G, w.total_M // w.G
+        X = X.view(Gb, Mb, w.K)
+        xs = xs.view(Gb, Mb)
+    else:
+        meta = torch.from_numpy(w.M_sizes if layout == "stacked" else w.zero_start_index_M).to(dev)
     if pre:
         Wt = F.f8f8bf16_shuffle_b(Wt)
     sets = [(X, Wt, xs, ws, meta)]
     for _ in range(rotate - 1):
         sets.append(tuple(t.clone() for t in sets[0]))
-    outs = [torch.empty((w.total_M, w.N) if layout == "stacked" else (w.G, w.expected_m, w.N),
-                        dtype=torch.bfloat16, device=dev) for _ in range(rotate)]
+    out_shape = {"stacked": (w.total_M, w.N), "offsets": (w.total_M, w.N),
+                 "batched": (w.G, w.total_M // w.G, w.N)}.get(layout) or (w.G, w.expected_m, w.N)
+    outs = [torch.empty(out_shape, dtype=torch.bfloat16, device=dev) for _ in range(rotate)]
     log(f"rotating over {rotate} input set(s)")
 
-    if layout == "stacked":
-        fn = F.f8f8bf16_rowwise_grouped_stacked_preshuffle if pre else F.f8f8bf16_rowwise_grouped_stacked
+    if layout in ("stacked", "offsets"):
+        if layout == "stacked":
+            fn = F.f8f8bf16_rowwise_grouped_stacked_preshuffle if pre else F.f8f8bf16_rowwise_grouped_stacked
+        else:
+            fn = F.f8f8bf16_rowwise_grouped_offsets_preshuffle if pre else F.f8f8bf16_rowwise_grouped_offsets
 
         def call(i):
             s = sets[i % rotate]
             fn(s[0], s[1], s[2], s[3], s[4], out=outs[i % rotate])
+    elif layout == "batched":
+        fn = F.f8f8bf16_rowwise_grouped_batched_preshuffle if pre else F.f8f8bf16_rowwise_grouped_batched
+
+        def call(i):
+            s = sets[i % rotate]
+            fn(s[0], s[1], s[2], s[3], out=outs[i % rotate])
     else:
         fn = F.f8f8bf16_rowwise_grouped_dynamic_preshuffle if pre else F.f8f8bf16_rowwise_grouped_dynamic
 
@@ -304,11 +343,11 @@ def main():
             "layout": layout,
             "preshuffled": pre,
             "G": w.G,
-            "rows": int(w.total_M if layout == "stacked" else w.G * w.expected_m),
+            "rows": int(w.G * w.expected_m if layout == "padded" else w.total_M),
             "valid_rows": R,
             "N": w.N,
             "K": w.K,
-            "group_rows": (w.M_sizes if layout == "stacked" else w.zero_start_index_M).tolist(),
+            "group_rows": (w.zero_start_index_M if layout == "padded" else w.M_sizes).tolist(),
             "rotating_input_sets": rotate,
             "us_per_call": round(avg * 1e6, 3),
         },
