@@ -23,3 +23,4 @@ from .grouped_gemm import (  # noqa: F401
     stacked_entries,
     stacked_row_groups,
 )
+from .quantize import e4m3fn_rne, quantize_rowwise  # noqa: F401,E402

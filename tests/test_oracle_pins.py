@@ -525,3 +525,69 @@ def test_planted_double_rounding_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "bf16_rne_from_f64", _mut_fp32_detour)
     with pytest.raises(AssertionError):
         test_bf16_golden_cases()
+
+
+# ---------------------------------------------------------------------------
+# rowwise activation quantisation (amax / 448 scales, e4m3fn RNE codes)
+# ---------------------------------------------------------------------------
+
+def _bf16_bits(v):
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_e4m3fn_rne_matches_torch_cast():
+    """The encoder against torch's own fp32 -> float8_e4m3fn cast (RNE) on random
+    values, every code's value, and every midpoint between neighbouring codes."""
+    rng = np.random.default_rng(50)
+    pos = oracle.e4m3fn_table()[:0x7F]
+    mids = (pos[1:] + pos[:-1]) / 2
+    vals = np.concatenate([rng.uniform(-448, 448, 20000), rng.normal(0, 1, 20000),
+                           2.0 ** rng.uniform(-12, -6, 2000), pos, -pos, mids, -mids,
+                           np.nextafter(mids, 0), np.nextafter(mids, 1000)]).astype(np.float32)
+    vals = vals[np.abs(vals) <= 448]
+    want = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3fn_rne(vals), want)
+
+
+def test_quantize_closed_forms():
+    # the largest magnitude of a row maps to +-448 (code 0x7E / 0xFE); zero rows get scale 1
+    x = np.array([[3.0, -1.5, 0.25, 0.0], [0.0, 0.0, 0.0, 0.0], [-7.0, 7.0, 1.0, -0.0]], np.float32)
+    q, s = oracle.quantize_rowwise(_bf16_bits(x))
+    assert s[1] == 1.0 and np.all(q[1] == 0)
+    assert s[0] == np.float32(3.0) / np.float32(448.0)
+    assert q[0, 0] == 0x7E and q[2, 1] == 0x7E and q[2, 0] == 0xFE
+    assert q[0, 3] == 0x00 and q[2, 3] == 0x80
+    # a row of powers of two with amax 448 has scale 1 and exact codes
+    p2 = np.array([[448.0, 1.0, -0.5, 2.0 ** -9]], np.float32)
+    q2, s2 = oracle.quantize_rowwise(_bf16_bits(p2))
+    assert s2[0] == 1.0
+    assert np.array_equal(oracle.decode_e4m3fn(q2[0]), p2[0].astype(np.float64))
+
+
+def test_quantize_error_within_half_a_code_step():
+    rng = np.random.default_rng(51)
+    x = rng.normal(0, 1, (64, 512)).astype(np.float32) * (2.0 ** rng.uniform(-8, 8, (64, 1))).astype(np.float32)
+    bits = _bf16_bits(x)
+    xb = oracle.bf16_bits_to_f64(bits)
+    q, s = oracle.quantize_rowwise(bits)
+    y = xb / s.astype(np.float64)[:, None]
+    dec = oracle.decode_e4m3fn(q)
+    pos = oracle.e4m3fn_table()[:0x7F]
+    idx = np.clip(np.searchsorted(pos, np.abs(y)), 1, 0x7E)
+    step = pos[idx] - pos[idx - 1]
+    assert np.all(np.abs(dec - y) <= step / 2 * (1 + 1e-6))
+
+
+def test_planted_truncation_in_quantiser_is_caught(monkeypatch):
+    from oracle import quantize as oq
+
+    def truncate(y):
+        y = np.asarray(y, np.float32)
+        a = np.abs(y).astype(np.float64)
+        code = np.clip(np.searchsorted(oq._POS, a, side="right") - 1, 0, 0x7E).astype(np.uint8)
+        return (code | np.where(np.signbit(y), np.uint8(0x80), np.uint8(0))).astype(np.uint8)
+
+    monkeypatch.setattr(oq, "e4m3fn_rne", truncate)
+    monkeypatch.setattr(oracle, "e4m3fn_rne", truncate)
+    with pytest.raises(AssertionError):
+        test_e4m3fn_rne_matches_torch_cast()
