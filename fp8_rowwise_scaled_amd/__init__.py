@@ -22,6 +22,7 @@ from .ops import (  # noqa: F401
     f8f8bf16_rowwise_grouped_offsets,
     f8f8bf16_rowwise_grouped_offsets_preshuffle,
     f8f8bf16_rowwise_grouped_stacked,
+    f8f8bf16_quantize_rowwise,
     f8f8bf16_rowwise_grouped_stacked_preshuffle,
     f8f8bf16_shuffle_b,
 )

@@ -30,6 +30,7 @@ EXPORTS = (
     "f8f8bf16_rowwise_grouped_batched",
     "f8f8bf16_rowwise_grouped_batched_preshuffle",
     "f8f8bf16_shuffle_b",
+    "f8f8bf16_quantize_rowwise",
     "f8f8bf16_last_error",
     "f8f8bf16_plan",
     "f8f8bf16_num_configs",
@@ -87,6 +88,8 @@ def load() -> ctypes.CDLL:
             getattr(lib, name).restype = I
     lib.f8f8bf16_shuffle_b.argtypes = [P, P, I64, I64, I64, P]
     lib.f8f8bf16_shuffle_b.restype = I
+    lib.f8f8bf16_quantize_rowwise.argtypes = [P, P, P, I64, I64, P]
+    lib.f8f8bf16_quantize_rowwise.restype = I
     lib.f8f8bf16_last_error.argtypes = []
     lib.f8f8bf16_last_error.restype = ctypes.c_char_p
     lib.f8f8bf16_plan.argtypes = [I, I, I64, I64, I64, I64, ctypes.POINTER(Plan)]

@@ -355,6 +355,28 @@ fp8gg_status f8f8bf16_rowwise_grouped_batched_preshuffle(const uint8_t* XQ, cons
   return run(FP8GG_LAYOUT_BATCHED, 1, XQ, WQs, x_scale, w_scale, nullptr, Y, G, M, N, K, 0, stream);
 }
 
+fp8gg_status f8f8bf16_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale, int64_t rows, int64_t K,
+                                       void* stream) {
+  if (rows < 0 || K < 0)
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "negative size (rows=%lld K=%lld)", (long long)rows, (long long)K);
+  if (K % 8 != 0) return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "K=%lld must be a multiple of 8", (long long)K);
+  const int64_t lim = (int64_t(1) << 31) - 256;
+  if (rows > lim || K > lim || (rows > 0 && K > (int64_t(1) << 47) / rows))
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "rows=%lld K=%lld is too large", (long long)rows, (long long)K);
+  if (rows == 0) return ok();
+  if (!x_scale || (K > 0 && (!X || !XQ)))
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "null pointer (X=%p XQ=%p x_scale=%p)", (const void*)X, (const void*)XQ,
+                (const void*)x_scale);
+  if (!aligned(X, 16) || !aligned(XQ, 8) || !aligned(x_scale, 4))
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "X must be 16-byte, XQ 8-byte and x_scale 4-byte aligned");
+  const Range x{X, rows * K * 2, "X"}, q{XQ, rows * K, "XQ"}, sc{x_scale, rows * 4, "x_scale"};
+  if (overlap(q, x) || overlap(sc, x) || overlap(q, sc))
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "X, XQ and x_scale must not overlap");
+  hipError_t e = fp8gg::launch_quantize_rowwise(X, XQ, x_scale, rows, K, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "quantize launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 fp8gg_status f8f8bf16_shuffle_b(const uint8_t* WQ, uint8_t* WQs, int64_t G, int64_t N, int64_t K,
                                 void* stream) {
   fp8gg_status st = check_shape(FP8GG_LAYOUT_STACKED, 1, G, 0, N, K);

@@ -69,6 +69,8 @@ hipError_t launch_gemm(int layout, int config_id, bool k_tail, const GemmArgs& a
 hipError_t launch_gemm_persistent(int layout, int config_id, bool k_tail, const GemmArgs& args, int grid,
                                   int tail_mode, hipStream_t stream);
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t stream);
+hipError_t launch_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale, int64_t rows, int64_t K,
+                                   hipStream_t stream);
 hipError_t launch_shuffle_b(const uint8_t* W, uint8_t* Ws, int64_t G, int64_t N, int64_t K,
                             hipStream_t stream);
 

@@ -169,3 +169,23 @@ def f8f8bf16_shuffle_b(WQ, out=None):
     st = _lib.load().f8f8bf16_shuffle_b(WQ.data_ptr(), out.data_ptr(), G, N, K, _stream(WQ.device))
     _lib.check(st, "f8f8bf16_shuffle_b")
     return out
+
+
+def f8f8bf16_quantize_rowwise(X, XQ=None, x_scale=None):
+    """Rowwise fp8 quantisation of bf16 activations X [rows, K]: returns (XQ uint8
+    [rows, K] e4m3fn codes, x_scale float32 [rows]) (see include/fp8gg.h)."""
+    if X.dim() != 2:
+        raise ValueError("X must be [rows, K]")
+    rows, K = X.shape
+    _check(X, "X", torch.bfloat16, (rows, K))
+    if XQ is None:
+        XQ = torch.empty((rows, K), dtype=torch.uint8, device=X.device)
+    if x_scale is None:
+        x_scale = torch.empty((rows,), dtype=torch.float32, device=X.device)
+    XQ = _bytes(XQ, "XQ")
+    _check(XQ, "XQ", torch.uint8, (rows, K))
+    _check(x_scale, "x_scale", torch.float32, (rows,))
+    st = _lib.load().f8f8bf16_quantize_rowwise(X.data_ptr(), XQ.data_ptr(), x_scale.data_ptr(), rows, K,
+                                              _stream(X.device))
+    _lib.check(st, "f8f8bf16_quantize_rowwise")
+    return XQ, x_scale

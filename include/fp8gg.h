@@ -182,6 +182,24 @@ fp8gg_status f8f8bf16_rowwise_grouped_batched_preshuffle(
 fp8gg_status f8f8bf16_shuffle_b(const uint8_t* WQ, uint8_t* WQs,
                                 int64_t G, int64_t N, int64_t K, void* stream);
 
+/*
+ * Rowwise fp8 quantisation of bf16 activations: produces the XQ and x_scale
+ * operands of the GEMMs above (one scale per row, constant along K: MSLK #471,
+ * Design notes, scaling-scheme paragraph; the amax choice of the scale is this
+ * library's).  Per row r of X:
+ *     x_scale[r] = amax_k |X[r, k]| / 448   (fp32, IEEE division; 1 if amax == 0)
+ *     XQ[r, k]   = e4m3fn_rne(clamp(X[r, k] / x_scale[r], -448, 448))   (fp32 quotient)
+ *
+ *   X         [rows, K]   bf16 (raw bits), 16-byte aligned
+ *   XQ        [rows, K]   fp8 e4m3fn output, 8-byte aligned
+ *   x_scale   [rows]      fp32 output
+ *
+ * Shape rule: K % 8 == 0.  Inputs are expected finite: a NaN is ignored by amax
+ * and gives an unspecified code.  The three buffers must not overlap.
+ */
+fp8gg_status f8f8bf16_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale,
+                                       int64_t rows, int64_t K, void* stream);
+
 /* Message describing the last failure on the calling thread ("" if none). */
 const char* f8f8bf16_last_error(void);
 

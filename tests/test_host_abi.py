@@ -22,7 +22,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 12
+    assert len(names) == 13
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -149,3 +149,21 @@ def test_plan_refuses_tensors_past_2_to_48_bytes(G, M, N, K):
 def test_plan_accepts_large_but_sane_shapes():
     p = F.plan(F.LAYOUT_STACKED, False, 256, 1 << 20, 8192, 8192)   # W 16 GiB, X 8 GiB
     assert p["config_id"] >= 0
+
+
+def test_quantize_refuses_bad_shapes_and_overlaps_on_the_host():
+    """Checks run before any launch: fake device addresses never reach a kernel."""
+    lib = _lib.load()
+    base = 0x10000000
+    # K not a multiple of 8
+    assert lib.f8f8bf16_quantize_rowwise(base, base + (1 << 20), base + (2 << 20), 4, 12, None) == _lib.ERR_UNSUPPORTED_SHAPE
+    # negative size
+    assert lib.f8f8bf16_quantize_rowwise(base, base + (1 << 20), base + (2 << 20), -1, 8, None) == _lib.ERR_INVALID_ARGUMENT
+    # XQ overlapping X
+    assert lib.f8f8bf16_quantize_rowwise(base, base + 64, base + (2 << 20), 4, 64, None) == _lib.ERR_INVALID_ARGUMENT
+    # misaligned X
+    assert lib.f8f8bf16_quantize_rowwise(base + 8, base + (1 << 20), base + (2 << 20), 4, 64, None) == _lib.ERR_INVALID_ARGUMENT
+    # null scale pointer
+    assert lib.f8f8bf16_quantize_rowwise(base, base + (1 << 20), None, 4, 64, None) == _lib.ERR_INVALID_ARGUMENT
+    # nothing to do: no launch, success
+    assert lib.f8f8bf16_quantize_rowwise(None, None, None, 0, 64, None) == _lib.OK
