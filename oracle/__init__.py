@@ -15,8 +15,12 @@ from .grouped_gemm import (  # noqa: F401
     dynamic_entries,
     dynamic_row_classes,
     e4m3fn_table,
+    k_offsets_slices,
+    n_offsets_col_groups,
     grouped_batched,
     grouped_dynamic,
+    grouped_k_offsets,
+    grouped_n_offsets,
     grouped_offsets,
     grouped_stacked,
     offsets_row_groups,

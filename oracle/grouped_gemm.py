@@ -32,6 +32,16 @@ What is computed, per group g (the plain definition, written out):
     onto it).
   * Batched layout (3D-3D): every group owns a full slab of M rows, all valid;
     there is no row metadata ([MSLK-471], commit adding the batched layout).
+  * N-offsets layout (3D-2D): the weights are one [total_N, K] matrix whose rows
+    (output columns) the groups partition by an int32 inclusive prefix; group g
+    multiplies its own slab XQ[g] [M, K] against its rows of W, and the results
+    sit side by side in Y [M, total_N] ([MSLK-471], commit adding the 3D-2D form
+    of the grouped mm; commit on store predicates keyed on the last column).
+  * K-offsets layout (2D-2D): both operands are one matrix, XQ [M, total_K] and
+    WQ [N, total_K], whose K columns the groups slice by an int32 inclusive
+    prefix; every group contracts over its own slice only and produces a whole
+    [M, N] output, so Y is [G, M, N] ([MSLK-471], commit adding the 2D-2D form,
+    and the commit keying the K-tail predicate on the group's own slice).
   * A contraction over K = 0 returns a zeroed output whatever the layout
     ([MSLK-471], commits on zero-length reductions and on the fakes' contracts).
 
@@ -54,7 +64,15 @@ Readings taken where the pages are silent (also listed in the design notes):
   * offsets: group g ends at min(max(offsets[g], end of group g-1), total_M), so
     an offset below its predecessor makes an empty group and rows past the last
     end belong to no group (left untouched).
-  * K = 0 zeroes every row of the output, in both layouts.
+  * K = 0 zeroes every row of the output, in every layout.
+  * n_offsets, k_offsets: the boundaries are read like the offsets layout's (an
+    end below its predecessor makes an empty group, ends are cut at total_N or
+    total_K); columns past the last end belong to no group and are untouched.
+    An empty K slice contributes a zero sum, scaled as usual.
+  * Scales of the two new layouts: n_offsets takes x_scale [G, M] (one per row of
+    each slab) and w_scale [total_N] (one per row of W); k_offsets takes x_scale
+    [G, M] and w_scale [G, N], since each group's slice of a row is a separate
+    quantised vector (the pages name no scale shapes for these ranks).
 
 Row classes returned with every result: ROW_WRITTEN (computed), ROW_ZEROED
 (must be +-0), ROW_UNTOUCHED (the caller's buffer is left as it was).
@@ -171,6 +189,7 @@ class OracleResult:
     values: np.ndarray
     bits: np.ndarray
     row_class: np.ndarray
+    col_class: np.ndarray | None = None   # n_offsets: per output column (else None)
 
     def written_values_rounded(self) -> np.ndarray:
         return bf16_bits_to_f64(self.bits[self.row_class == ROW_WRITTEN])
@@ -303,6 +322,86 @@ def grouped_batched(XQ, WQ, x_scale, w_scale) -> OracleResult:
     values = np.empty((G, M, N))
     for g in range(G):
         acc = _accumulate(XQ[g], WQ[g])
+        values[g] = _apply_scales(acc, np.asarray(x_scale)[g], np.asarray(w_scale)[g])
+    return OracleResult(values, bf16_rne_from_f64(values), np.full(G * M, ROW_WRITTEN, np.int8))
+
+
+def n_offsets_col_groups(n_offsets: np.ndarray, total_N: int) -> np.ndarray:
+    """Owning group of each output column of the n_offsets layout, or -1.
+
+    Group g owns columns [end_{g-1}, end_g), end_{-1} = 0, with
+    end_g = min(max(n_offsets[g], end_{g-1}), total_N).
+    """
+    owner = np.full(int(total_N), -1, dtype=np.int64)
+    prev = 0
+    for g, o in enumerate(np.asarray(n_offsets, dtype=np.int64).tolist()):
+        end = min(max(o, prev), total_N)
+        owner[prev:end] = g
+        prev = end
+    return owner
+
+
+def grouped_n_offsets(XQ, WQ, x_scale, w_scale, n_offsets) -> OracleResult:
+    """N-offsets layout (3D-2D): XQ [G, M, K], WQ [total_N, K], x_scale [G, M],
+    w_scale [total_N], n_offsets [G] int32 inclusive prefix over W's rows
+    -> Y [M, total_N].  Column n of group g:
+        Y[m, n] = (sum_k dec(XQ[g, m, k]) dec(WQ[n, k])) * x_scale[g, m] * w_scale[n].
+    Columns of no group are untouched (col_class)."""
+    XQ = np.asarray(XQ, np.uint8)
+    WQ = np.asarray(WQ, np.uint8)
+    G, M, K = XQ.shape
+    total_N, K2 = WQ.shape
+    assert K == K2
+    values = np.full((M, total_N), np.nan)
+    bits = np.full((M, total_N), UNTOUCHED_SENTINEL, dtype=np.uint16)
+    col_class = np.full(total_N, ROW_UNTOUCHED, dtype=np.int8)
+    if K == 0:
+        return OracleResult(np.zeros((M, total_N)), np.zeros((M, total_N), np.uint16),
+                            np.full(M, ROW_ZEROED, np.int8), np.full(total_N, ROW_ZEROED, np.int8))
+    owner = n_offsets_col_groups(n_offsets, total_N)
+    for g in range(G):
+        cols = np.nonzero(owner == g)[0]
+        if cols.size == 0:
+            continue
+        acc = _accumulate(XQ[g], WQ[cols])
+        v = _apply_scales(acc, np.asarray(x_scale)[g], np.asarray(w_scale)[cols])
+        values[:, cols] = v
+        bits[:, cols] = bf16_rne_from_f64(v)
+        col_class[cols] = ROW_WRITTEN
+    row_class = np.full(M, ROW_WRITTEN if np.any(col_class == ROW_WRITTEN) else ROW_UNTOUCHED, np.int8)
+    return OracleResult(values, bits, row_class, col_class)
+
+
+def k_offsets_slices(k_offsets: np.ndarray, total_K: int) -> list:
+    """K slice [start, end) of each group of the k_offsets layout: end_g =
+    min(max(k_offsets[g], end_{g-1}), total_K), start_g = end_{g-1}, end_{-1} = 0."""
+    out = []
+    prev = 0
+    for o in np.asarray(k_offsets, dtype=np.int64).tolist():
+        end = min(max(o, prev), total_K)
+        out.append((prev, end))
+        prev = end
+    return out
+
+
+def grouped_k_offsets(XQ, WQ, x_scale, w_scale, k_offsets) -> OracleResult:
+    """K-offsets layout (2D-2D): XQ [M, total_K], WQ [N, total_K], x_scale [G, M],
+    w_scale [G, N], k_offsets [G] int32 inclusive prefix over K -> Y [G, M, N]:
+        Y[g, m, n] = (sum_{k in slice g} dec(XQ[m, k]) dec(WQ[n, k])) * x_scale[g, m] * w_scale[g, n].
+    Every row of every group is written (flattened row classes [G*M])."""
+    XQ = np.asarray(XQ, np.uint8)
+    WQ = np.asarray(WQ, np.uint8)
+    M, total_K = XQ.shape
+    N, K2 = WQ.shape
+    assert total_K == K2
+    slices = k_offsets_slices(k_offsets, total_K)
+    G = len(slices)
+    if total_K == 0:
+        return OracleResult(np.zeros((G, M, N)), np.zeros((G, M, N), np.uint16),
+                            np.full(G * M, ROW_ZEROED, np.int8))
+    values = np.empty((G, M, N))
+    for g, (ks, ke) in enumerate(slices):
+        acc = _accumulate(XQ[:, ks:ke], WQ[:, ks:ke])
         values[g] = _apply_scales(acc, np.asarray(x_scale)[g], np.asarray(w_scale)[g])
     return OracleResult(values, bf16_rne_from_f64(values), np.full(G * M, ROW_WRITTEN, np.int8))
 

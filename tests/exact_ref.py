@@ -95,3 +95,43 @@ def offsets_exact(XQ, WQ, x_scale, w_scale, offsets):
                 row.append(bf16_bits_exact(v))
             out[r] = row
     return out
+
+
+def n_offsets_exact(XQ, WQ, x_scale, w_scale, n_offsets):
+    """Exact bf16 bits [M][total_N] of the n_offsets (3D-2D) layout for well-formed
+    offsets: group g owns W rows (output columns) n_offsets[g-1] .. n_offsets[g]-1,
+    n_offsets[-1] = 0, and multiplies them against its slab XQ[g].  Columns of no
+    group are None."""
+    G, M, _ = XQ.shape
+    total_N = WQ.shape[0]
+    out = [[None] * total_N for _ in range(M)]
+    for g in range(G):
+        lo = int(n_offsets[g - 1]) if g > 0 else 0
+        for n in range(lo, int(n_offsets[g])):
+            for m in range(M):
+                acc = dot_exact(XQ[g, m], WQ[n])
+                v = None if acc is None else acc * Fraction(float(x_scale[g, m])) * Fraction(float(w_scale[n]))
+                out[m][n] = bf16_bits_exact(v)
+    return out
+
+
+def k_offsets_exact(XQ, WQ, x_scale, w_scale, k_offsets):
+    """Exact bf16 bits [G][M][N] of the k_offsets (2D-2D) layout for well-formed
+    offsets: group g contracts over K columns k_offsets[g-1] .. k_offsets[g]-1 of
+    both operands, k_offsets[-1] = 0."""
+    M = XQ.shape[0]
+    N = WQ.shape[0]
+    out = []
+    for g in range(len(k_offsets)):
+        lo = int(k_offsets[g - 1]) if g > 0 else 0
+        hi = int(k_offsets[g])
+        slab = []
+        for m in range(M):
+            row = []
+            for n in range(N):
+                acc = dot_exact(XQ[m, lo:hi], WQ[n, lo:hi])
+                v = None if acc is None else acc * Fraction(float(x_scale[g, m])) * Fraction(float(w_scale[g, n]))
+                row.append(bf16_bits_exact(v))
+            slab.append(row)
+        out.append(slab)
+    return out

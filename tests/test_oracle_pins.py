@@ -239,6 +239,171 @@ def test_batched_k_zero_is_zero():
     assert np.all(res.bits == 0) and np.all(res.row_class == oracle.ROW_ZEROED)
 
 
+# ---------------------------------------------------------------------------
+# n_offsets (3D-2D) and k_offsets (2D-2D) layouts
+# ---------------------------------------------------------------------------
+
+def _bits_match_exact(got_bits, exact):
+    """bf16 bits against exact ones (None entries must be the untouched sentinel;
+    either sign of zero accepted)."""
+    got = np.asarray(got_bits).astype(np.int64).reshape(-1)
+    flat = [x for row in np.asarray(exact, dtype=object).reshape(-1).tolist() for x in [row]]
+    for gv, want in zip(got.tolist(), flat):
+        if want is None:
+            if gv != int(og.UNTOUCHED_SENTINEL):
+                return False
+        elif (want & 0x7FFF) == 0:
+            if (gv & 0x7FFF) != 0:
+                return False
+        elif gv != want:
+            return False
+    return True
+
+
+def _n_problem(seed, G, M, total_N, K):
+    rng = np.random.default_rng(seed)
+    XQ = rng.choice(FINITE_CODES, size=(G, M, K)).astype(np.uint8)
+    WQ = rng.choice(FINITE_CODES, size=(total_N, K)).astype(np.uint8)
+    xs = (2.0 ** rng.uniform(-12, 4, (G, M))).astype(np.float32)
+    ws = (2.0 ** rng.uniform(-12, 4, total_N)).astype(np.float32)
+    return XQ, WQ, xs, ws
+
+
+def _k_problem(seed, G, M, N, total_K):
+    rng = np.random.default_rng(seed)
+    XQ = rng.choice(FINITE_CODES, size=(M, total_K)).astype(np.uint8)
+    WQ = rng.choice(FINITE_CODES, size=(N, total_K)).astype(np.uint8)
+    xs = (2.0 ** rng.uniform(-12, 4, (G, M))).astype(np.float32)
+    ws = (2.0 ** rng.uniform(-12, 4, (G, N))).astype(np.float32)
+    return XQ, WQ, xs, ws
+
+
+# (seed, n_offsets, M, K, total_N): an empty group, odd widths, unowned trailing columns
+N_OFFSETS_CASES = [
+    (51, [3, 3, 8], 2, 48, 8),
+    (52, [1, 6], 3, 32, 9),
+    (53, [5], 2, 16, 5),
+]
+
+
+def _check_n_offsets(seed, offs, M, K, total_N):
+    XQ, WQ, xs, ws = _n_problem(seed, len(offs), M, total_N, K)
+    res = oracle.grouped_n_offsets(XQ, WQ, xs, ws, np.array(offs, np.int32))
+    ok = _bits_match_exact(res.bits, exact_ref.n_offsets_exact(XQ, WQ, xs, ws, offs))
+    owner = np.full(total_N, -1)
+    prev = 0
+    for g, o in enumerate(offs):
+        owner[prev:o] = g
+        prev = o
+    want_cls = np.where(owner >= 0, oracle.ROW_WRITTEN, oracle.ROW_UNTOUCHED)
+    return ok and np.array_equal(res.col_class, want_cls)
+
+
+@pytest.mark.parametrize("seed,offs,M,K,total_N", N_OFFSETS_CASES)
+def test_n_offsets_equals_exact_bruteforce(seed, offs, M, K, total_N):
+    assert _check_n_offsets(seed, offs, M, K, total_N)
+
+
+# (seed, k_offsets, M, N, total_K): an empty slice, unequal slices, a trailing unread part
+K_OFFSETS_CASES = [
+    (61, [16, 16, 48], 2, 3, 48),
+    (62, [32, 48], 3, 2, 64),
+    (63, [16], 2, 2, 16),
+]
+
+
+def _check_k_offsets(seed, offs, M, N, total_K):
+    XQ, WQ, xs, ws = _k_problem(seed, len(offs), M, N, total_K)
+    res = oracle.grouped_k_offsets(XQ, WQ, xs, ws, np.array(offs, np.int32))
+    return _bits_match_exact(res.bits, exact_ref.k_offsets_exact(XQ, WQ, xs, ws, offs)) and \
+        np.all(res.row_class == oracle.ROW_WRITTEN)
+
+
+@pytest.mark.parametrize("seed,offs,M,N,total_K", K_OFFSETS_CASES)
+def test_k_offsets_equals_exact_bruteforce(seed, offs, M, N, total_K):
+    assert _check_k_offsets(seed, offs, M, N, total_K)
+
+
+def test_n_and_k_offsets_reading_of_ill_formed_prefixes():
+    owner = oracle.n_offsets_col_groups(np.array([4, 2, 7, 30], np.int32), 9)
+    assert owner.tolist() == [0, 0, 0, 0, 2, 2, 2, 3, 3]
+    assert oracle.k_offsets_slices(np.array([32, 16, 64, 999], np.int32), 80) == \
+        [(0, 32), (32, 32), (32, 64), (64, 80)]
+    assert oracle.k_offsets_slices(np.array([-16, 16], np.int32), 32) == [(0, 0), (0, 16)]
+
+
+def test_n_offsets_single_group_is_a_plain_scaled_gemm():
+    """One group owning every column: a plain GEMM of the slab against W, written
+    with numpy's matmul on torch-decoded operands (exact at this size)."""
+    XQ, WQ, xs, ws = _n_problem(54, 1, 5, 7, 96)
+    x = torch.from_numpy(XQ[0]).view(torch.float8_e4m3fn).double().numpy()
+    w = torch.from_numpy(WQ).view(torch.float8_e4m3fn).double().numpy()
+    ref = (x @ w.T) * xs[0].astype(np.float64)[:, None] * ws.astype(np.float64)[None, :]
+    res = oracle.grouped_n_offsets(XQ, WQ, xs, ws, np.array([7], np.int32))
+    assert np.array_equal(res.values, ref)
+
+
+def test_n_offsets_equal_widths_equals_batched():
+    """Groups of equal width N: column block g of the n_offsets result is the
+    batched layout's slab g (W's rows regrouped as [G, N, K])."""
+    G, M, N, K = 3, 4, 5, 64
+    XQ, WQ, xs, ws = _n_problem(55, G, M, G * N, K)
+    a = oracle.grouped_n_offsets(XQ, WQ, xs, ws, np.arange(1, G + 1, dtype=np.int32) * N)
+    b = oracle.grouped_batched(XQ, WQ.reshape(G, N, K), xs, ws.reshape(G, N))
+    for g in range(G):
+        assert np.array_equal(a.bits[:, g * N:(g + 1) * N], b.bits[g])
+
+
+def test_k_offsets_slices_sum_to_the_full_contraction():
+    """With unit scales the unrounded per-group results of a partition of K add up
+    to the full-K product of torch-decoded operands, exactly (every partial sum is
+    exact in fp64)."""
+    G, M, N, total_K = 4, 3, 5, 160
+    XQ, WQ, _, _ = _k_problem(64, G, M, N, total_K)
+    one_x = np.ones((G, M), np.float32)
+    one_w = np.ones((G, N), np.float32)
+    res = oracle.grouped_k_offsets(XQ, WQ, one_x, one_w, np.array([48, 48, 112, 160], np.int32))
+    x = torch.from_numpy(XQ).view(torch.float8_e4m3fn).double().numpy()
+    w = torch.from_numpy(WQ).view(torch.float8_e4m3fn).double().numpy()
+    assert np.array_equal(res.values.sum(axis=0), x @ w.T)
+    assert np.all(res.values[1] == 0)          # the empty slice
+
+
+def test_k_offsets_concatenated_slabs_equal_batched():
+    """Slabs laid side by side along K, each group slicing its own: group g's output
+    is the batched layout's slab g."""
+    G, M, N, K = 3, 4, 5, 48
+    rng = np.random.default_rng(65)
+    Xb = rng.choice(FINITE_CODES, size=(G, M, K)).astype(np.uint8)
+    Wb = rng.choice(FINITE_CODES, size=(G, N, K)).astype(np.uint8)
+    xs = (2.0 ** rng.uniform(-8, 4, (G, M))).astype(np.float32)
+    ws = (2.0 ** rng.uniform(-8, 4, (G, N))).astype(np.float32)
+    a = oracle.grouped_k_offsets(np.concatenate(list(Xb), axis=1), np.concatenate(list(Wb), axis=1), xs, ws,
+                                 np.arange(1, G + 1, dtype=np.int32) * K)
+    b = oracle.grouped_batched(Xb, Wb, xs, ws)
+    assert np.array_equal(a.bits, b.bits)
+
+
+def test_k_offsets_single_signed_neighbours():
+    """Constant single-signed data outside a group's slice: a read past the slice
+    would add terms of one sign and move the result far past any rounding."""
+    M, N = 2, 3
+    XQ = np.full((M, 96), 0x38, np.uint8)      # 1.0 everywhere
+    WQ = np.full((N, 96), 0x38, np.uint8)
+    res = oracle.grouped_k_offsets(XQ, WQ, np.ones((3, M), np.float32), np.ones((3, N), np.float32),
+                                   np.array([16, 48, 96], np.int32))
+    assert res.values[:, 0, 0].tolist() == [16.0, 32.0, 48.0]
+
+
+def test_n_and_k_offsets_k_zero():
+    a = oracle.grouped_n_offsets(np.zeros((2, 3, 0), np.uint8), np.zeros((5, 0), np.uint8),
+                                 np.ones((2, 3), np.float32), np.ones(5, np.float32), np.array([2, 5], np.int32))
+    assert np.all(a.bits == 0) and np.all(a.col_class == oracle.ROW_ZEROED)
+    b = oracle.grouped_k_offsets(np.zeros((3, 0), np.uint8), np.zeros((4, 0), np.uint8),
+                                 np.ones((2, 3), np.float32), np.ones((2, 4), np.float32), np.array([0, 0], np.int32))
+    assert b.bits.shape == (2, 3, 4) and np.all(b.bits == 0)
+
+
 def _load_worked():
     with open(os.path.join(GOLDEN, "worked_example.json")) as f:
         ex = json.load(f)
@@ -457,6 +622,8 @@ def _pins_pass():
     ok = all(_check_bruteforce(*c) for c in BRUTE_CASES)
     ok = ok and all(_check_offsets(*c) for c in OFFSETS_CASES)
     ok = ok and _check_batched(41, 3, 2, 4, 48)
+    ok = ok and all(_check_n_offsets(*c) for c in N_OFFSETS_CASES)
+    ok = ok and all(_check_k_offsets(*c) for c in K_OFFSETS_CASES)
     try:
         test_worked_example_stacked()
         test_worked_example_padded()
@@ -490,6 +657,33 @@ def _mut_offsets_start(offsets, total_M):
     return owner
 
 
+def _mut_n_offsets_start(n_offsets, total_N):
+    """Reads n_offsets[g] as the first column of group g instead of its end."""
+    return _mut_offsets_start(n_offsets, total_N)
+
+
+def _mut_k_slice_to_total(k_offsets, total_K):
+    """Keys the end of every K slice on the total K instead of the group's own end."""
+    out = []
+    prev = 0
+    for o in np.asarray(k_offsets, np.int64).tolist():
+        end = min(max(o, prev), total_K)
+        out.append((prev, total_K))
+        prev = end
+    return out
+
+
+def _mut_k_slice_from_zero(k_offsets, total_K):
+    """Starts every K slice at 0 (offsets read as slice lengths from the origin)."""
+    out = []
+    prev = 0
+    for o in np.asarray(k_offsets, np.int64).tolist():
+        end = min(max(o, prev), total_K)
+        out.append((0, end))
+        prev = end
+    return out
+
+
 def _mut_sign(codes):
     return np.abs(og._E4M3FN_TABLE[np.asarray(codes, np.uint8)])
 
@@ -510,6 +704,9 @@ def _mut_truncate(v):
     ("x_scale dropped", "_apply_scales", _mut_no_xscale),
     ("wrong group", "stacked_row_groups", _mut_group_shift),
     ("offsets read as group starts", "offsets_row_groups", _mut_offsets_start),
+    ("n_offsets read as group starts", "n_offsets_col_groups", _mut_n_offsets_start),
+    ("K slice read to the total K", "k_offsets_slices", _mut_k_slice_to_total),
+    ("K slice read from the origin", "k_offsets_slices", _mut_k_slice_from_zero),
     ("sign lost in decode", "decode_e4m3fn", _mut_sign),
     ("bf16 rounding truncates", "bf16_rne_from_f64", _mut_truncate),
 ])

@@ -254,3 +254,122 @@ def padded_tails() -> Dynamic:
 def gen_rows_from(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
     """Seeded integers in [lo, hi) (helper for randomised edge cases)."""
     return np.random.default_rng(seed).integers(lo, hi, n).astype(np.int64)
+
+
+# ---------------------------------------------------------------------------
+# Layouts whose groups partition N (n_offsets, 3D-2D) or K (k_offsets, 2D-2D).
+# ---------------------------------------------------------------------------
+
+@dataclass
+class NOffsets:
+    """Inputs of the n_offsets layout: one X slab per group, W rows split by group."""
+    XQ: np.ndarray         # [G, M, K] uint8
+    WQ: np.ndarray         # [total_N, K] uint8
+    x_scale: np.ndarray    # [G, M] float32
+    w_scale: np.ndarray    # [total_N] float32
+    n_offsets: np.ndarray  # [G] int32 inclusive prefix of the group widths
+    name: str = ""
+
+    @property
+    def G(self) -> int:
+        return int(self.XQ.shape[0])
+
+    @property
+    def M(self) -> int:
+        return int(self.XQ.shape[1])
+
+    @property
+    def N(self) -> int:
+        return int(self.WQ.shape[0])
+
+    @property
+    def K(self) -> int:
+        return int(self.WQ.shape[1])
+
+
+@dataclass
+class KOffsets:
+    """Inputs of the k_offsets layout: both operands split along K by group; each
+    group's slice of a row is quantised on its own (one scale per group and row)."""
+    XQ: np.ndarray         # [M, total_K] uint8
+    WQ: np.ndarray         # [N, total_K] uint8
+    x_scale: np.ndarray    # [G, M] float32
+    w_scale: np.ndarray    # [G, N] float32
+    k_offsets: np.ndarray  # [G] int32 inclusive prefix of the slice lengths
+    name: str = ""
+
+    @property
+    def G(self) -> int:
+        return int(self.k_offsets.shape[0])
+
+    @property
+    def M(self) -> int:
+        return int(self.XQ.shape[0])
+
+    @property
+    def N(self) -> int:
+        return int(self.WQ.shape[0])
+
+    @property
+    def K(self) -> int:
+        return int(self.XQ.shape[1])
+
+
+def make_n_offsets(widths, M: int, K: int, seed: int, total_N: int | None = None, sigma: float = 1.0,
+                   name: str = "") -> NOffsets:
+    """n_offsets inputs for the given group widths (columns per group); ``total_N``
+    larger than their sum leaves trailing columns that belong to no group."""
+    widths = np.asarray(widths, dtype=np.int64)
+    G = int(widths.shape[0])
+    if total_N is None:
+        total_N = int(widths.sum())
+    XQ, xs = draw_quantized(seed, _TAG_X, G * M, K, sigma)
+    WQ, ws = draw_quantized(seed, _TAG_W, total_N, K, sigma)
+    return NOffsets(XQ.reshape(G, M, K), WQ, xs.reshape(G, M), ws, np.cumsum(widths).astype(np.int32), name)
+
+
+def _quantize_slices(x: np.ndarray, bounds) -> tuple[np.ndarray, np.ndarray]:
+    """Rowwise quantisation of each K slice [ks, ke) of x [rows, K] on its own:
+    codes [rows, K] (columns past the last slice quantised as one more slice)
+    and scales [G, rows]."""
+    rows, K = x.shape
+    q = np.zeros((rows, K), np.uint8)
+    s = np.ones((len(bounds), rows), np.float32)
+    for g, (ks, ke) in enumerate(bounds):
+        q[:, ks:ke], s[g] = quantize_rows(x[:, ks:ke])
+    last = bounds[-1][1] if bounds else 0
+    if last < K:
+        q[:, last:], _ = quantize_rows(x[:, last:])
+    return q, s
+
+
+def make_k_offsets(lengths, M: int, N: int, seed: int, total_K: int | None = None, sigma: float = 1.0,
+                   name: str = "") -> KOffsets:
+    """k_offsets inputs for the given slice lengths (K bytes per group)."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    if total_K is None:
+        total_K = int(lengths.sum())
+    ends = np.cumsum(lengths)
+    bounds = [(int(e - n), int(e)) for e, n in zip(ends, lengths)]
+    rx = np.random.default_rng([seed, _TAG_X])
+    rw = np.random.default_rng([seed, _TAG_W])
+    x = rx.standard_normal((M, total_K), dtype=np.float32) * np.float32(sigma)
+    w = rw.standard_normal((N, total_K), dtype=np.float32) * np.float32(sigma)
+    XQ, xs = _quantize_slices(x, bounds)
+    del x
+    WQ, ws = _quantize_slices(w, bounds)
+    return KOffsets(XQ, WQ, xs, ws, ends.astype(np.int32), name)
+
+
+def moe_n_offsets() -> NOffsets:
+    """G=8 slabs of M=512 rows, K=7168; 16384 weight rows split over the groups by
+    Zipf(1.2) in units of 8 columns, one group empty."""
+    widths = 8 * zipf_sizes(6006, 2048, 8)
+    return make_n_offsets(widths, 512, 7168, seed=6006, name="moe_n_offsets_G8_M512_N16384_K7168")
+
+
+def moe_wgrad_k_offsets() -> KOffsets:
+    """Weight-gradient shape: G=8 groups slicing 4096 tokens of K by Zipf(1.2) in
+    units of 16, one group empty; M=2048, N=7168, Y [8, 2048, 7168]."""
+    lengths = 16 * zipf_sizes(7007, 256, 8)
+    return make_k_offsets(lengths, 2048, 7168, seed=7007, name="moe_wgrad_k_offsets_G8_M2048_N7168_K4096")
