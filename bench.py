@@ -34,7 +34,8 @@ MALL_BYTES = 256 * 2 ** 20    # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = ["moe_gate_up", "tiny_stacked", "dense_expert", "dense_expert_preshuffle", "padded_tails",
-             "moe_gate_up_offsets", "dense_expert_batched"] + [f"moe_down_M{m}" for m in (1, 8, 32, 256, 2048, 8192)]
+             "moe_gate_up_offsets", "dense_expert_batched", "moe_n_offsets", "moe_wgrad_k_offsets"] + \
+    [f"moe_down_M{m}" for m in (1, 8, 32, 256, 2048, 8192)]
 
 
 def log(*a):
@@ -63,6 +64,10 @@ def make_workload(name):
         w = wl.dense_expert()
         w.name += "_batched"
         return w, "batched", False
+    if name == "moe_n_offsets":
+        return wl.moe_n_offsets(), "n_offsets", False
+    if name == "moe_wgrad_k_offsets":
+        return wl.moe_wgrad_k_offsets(), "k_offsets", False
     if name.startswith("moe_down_M"):
         return wl.moe_down(int(name[len("moe_down_M"):])), "stacked", False
     raise ValueError(name)
@@ -76,6 +81,21 @@ def algorithmic_work(w, layout):
     padding inputs are not counted."""
     import numpy as np
     G, N, K = w.G, w.N, w.K
+    if layout == "n_offsets":
+        # groups own W rows: R = M rows per slab, N_valid columns, slabs of groups with columns read
+        ends = np.minimum(np.maximum.accumulate(np.maximum(w.n_offsets.astype(np.int64), 0)), N)
+        widths = np.diff(np.concatenate([[0], ends]))
+        n_valid, g_ne, M = int(widths.sum()), int((widths > 0).sum()), w.M
+        flop = 2 * M * K * n_valid
+        nbytes = g_ne * M * K + n_valid * K + 4 * g_ne * M + 4 * n_valid + 2 * M * n_valid + 4 * G
+        return flop, nbytes, M, g_ne
+    if layout == "k_offsets":
+        # groups slice K: every group writes a whole [M, N] output
+        ends = np.minimum(np.maximum.accumulate(np.maximum(w.k_offsets.astype(np.int64), 0)), K)
+        k_valid, M = int(ends[-1]) if G else 0, w.M
+        flop = 2 * M * N * k_valid
+        nbytes = M * k_valid + N * k_valid + 4 * G * M + 4 * G * N + 2 * G * M * N + 4 * G
+        return flop, nbytes, G * M, G
     if layout in ("stacked", "offsets", "batched"):
         sizes = np.clip(w.M_sizes, 0, None)
         R = int(min(sizes.sum(), w.total_M))
@@ -97,11 +117,27 @@ def offsets_of(w):
     return np.cumsum(np.clip(w.M_sizes, 0, None)).astype(np.int32)
 
 
+# Sources that decide what the GEMM kernels do on a workload (kernels, selector,
+# shared header); the activation quantiser is built from its own file.
+GEMM_SOURCES = ("fp8gg_api.cpp", "fp8gg_internal.h", "fp8gg_kernels.hip")
+
+
+def group_meta(w, layout):
+    """The workload's group metadata as a list (row counts, valid rows or offsets)."""
+    if layout == "padded":
+        return w.zero_start_index_M.tolist()
+    if layout == "n_offsets":
+        return w.n_offsets.tolist()
+    if layout == "k_offsets":
+        return w.k_offsets.tolist()
+    return w.M_sizes.tolist()
+
+
 def kernel_source_hash():
     csrc = os.path.join(ROOT, "fp8_rowwise_scaled_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
-        if f.endswith((".hip", ".cpp", ".h")):
+        if f in GEMM_SOURCES:
             with open(os.path.join(csrc, f), "rb") as fh:
                 h.update(f.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
@@ -140,6 +176,10 @@ def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=3):
         elif layout == "batched":
             M = w.total_M // w.G
             oracle.grouped_batched(w.XQ.reshape(w.G, M, w.K), w.WQ, w.x_scale.reshape(w.G, M), w.w_scale)
+        elif layout == "n_offsets":
+            oracle.grouped_n_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, w.n_offsets)
+        elif layout == "k_offsets":
+            oracle.grouped_k_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, w.k_offsets)
         else:
             oracle.grouped_dynamic(w.XQ, w.WQ, w.x_scale, w.w_scale, w.zero_start_index_M, True)
         times.append(time.perf_counter() - t0)
@@ -189,6 +229,38 @@ def small_m_us_per_call(F, torch, totals=(1, 8, 32), calls_per_graph=64, replays
             f"{rot} input copies)")
         del sets, outs, base, g
     return out
+
+
+def quantize_us_per_call(F, torch, rows=4096, K=7168, calls=200):
+    """The rowwise activation quantiser (bf16 [rows, K] -> e4m3fn codes + fp32 row
+    scales) on the gate_up activations' shape, rotating over enough input copies to
+    defeat the Infinity Cache.  HBM-bound: 2 bytes read and 1 written per element,
+    4 bytes written per row."""
+    dev = torch.device("cuda", 0)
+    nbytes = 3 * rows * K + 4 * rows
+    rot = max(1, min(16, math.ceil(2 * MALL_BYTES / nbytes)))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7001)
+    xs = [torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+          for _ in range(rot)]
+    qs = [torch.empty((rows, K), dtype=torch.uint8, device=dev) for _ in range(rot)]
+    ss = [torch.empty((rows,), dtype=torch.float32, device=dev) for _ in range(rot)]
+    stream = torch.cuda.current_stream(dev)
+    for i in range(20):
+        F.f8f8bf16_quantize_rowwise(xs[i % rot], qs[i % rot], ss[i % rot])
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(calls):
+        F.f8f8bf16_quantize_rowwise(xs[i % rot], qs[i % rot], ss[i % rot])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / calls
+    gbs = nbytes / us / 1e3
+    log(f"quantize: bf16 [{rows}, {K}] -> e4m3fn: {us:.2f} us/call ({gbs:.0f} GB/s, {rot} input copies)")
+    del xs, qs, ss
+    return {"shape": [rows, K], "us_per_call": round(us, 3), "GB_per_s": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "input_copies": rot}
 
 
 def copy_calibration(nbytes):
@@ -246,7 +318,11 @@ def main():
     Wt = torch.from_numpy(w.WQ).to(dev)
     xs = torch.from_numpy(w.x_scale).to(dev)
     ws = torch.from_numpy(w.w_scale).to(dev)
-    if layout == "offsets":
+    if layout == "n_offsets":
+        meta = torch.from_numpy(w.n_offsets).to(dev)
+    elif layout == "k_offsets":
+        meta = torch.from_numpy(w.k_offsets).to(dev)
+    elif layout == "offsets":
         meta = torch.from_numpy(offsets_of(w)).to(dev)
     elif layout == "batched":
         meta = torch.zeros(1, dtype=torch.int64, device=dev)   # the batched layout has no metadata
@@ -260,8 +336,10 @@ def main():
     sets = [(X, Wt, xs, ws, meta)]
     for _ in range(rotate - 1):
         sets.append(tuple(t.clone() for t in sets[0]))
-    out_shape = {"stacked": (w.total_M, w.N), "offsets": (w.total_M, w.N),
-                 "batched": (w.G, w.total_M // w.G, w.N)}.get(layout) or (w.G, w.expected_m, w.N)
+    out_shape = {"stacked": lambda: (w.total_M, w.N), "offsets": lambda: (w.total_M, w.N),
+                 "batched": lambda: (w.G, w.total_M // w.G, w.N), "n_offsets": lambda: (w.M, w.N),
+                 "k_offsets": lambda: (w.G, w.M, w.N),
+                 "padded": lambda: (w.G, w.expected_m, w.N)}[layout]()
     outs = [torch.empty(out_shape, dtype=torch.bfloat16, device=dev) for _ in range(rotate)]
     log(f"rotating over {rotate} input set(s)")
 
@@ -270,6 +348,12 @@ def main():
             fn = F.f8f8bf16_rowwise_grouped_stacked_preshuffle if pre else F.f8f8bf16_rowwise_grouped_stacked
         else:
             fn = F.f8f8bf16_rowwise_grouped_offsets_preshuffle if pre else F.f8f8bf16_rowwise_grouped_offsets
+
+        def call(i):
+            s = sets[i % rotate]
+            fn(s[0], s[1], s[2], s[3], s[4], out=outs[i % rotate])
+    elif layout in ("n_offsets", "k_offsets"):
+        fn = F.f8f8bf16_rowwise_grouped_n_offsets if layout == "n_offsets" else F.f8f8bf16_rowwise_grouped_k_offsets
 
         def call(i):
             s = sets[i % rotate]
@@ -343,11 +427,12 @@ def main():
             "layout": layout,
             "preshuffled": pre,
             "G": w.G,
-            "rows": int(w.G * w.expected_m if layout == "padded" else w.total_M),
+            "rows": int(w.G * w.expected_m if layout == "padded" else
+                        (w.M if layout == "n_offsets" else (w.G * w.M if layout == "k_offsets" else w.total_M))),
             "valid_rows": R,
             "N": w.N,
             "K": w.K,
-            "group_rows": (w.zero_start_index_M if layout == "padded" else w.M_sizes).tolist(),
+            "group_rows": group_meta(w, layout),
             "rotating_input_sets": rotate,
             "us_per_call": round(avg * 1e6, 3),
         },
@@ -355,6 +440,7 @@ def main():
     }
     if not args.no_small_m and args.workload == "moe_gate_up":
         result["small_m"] = small_m_us_per_call(F, torch)
+        result["quantize"] = quantize_us_per_call(F, torch)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
         result["cpu_baseline"] = cpu_baseline(w, layout, flop)

@@ -5,6 +5,8 @@ this package holds its sources (csrc/), the build step and a thin binding.
 """
 from ._lib import (  # noqa: F401
     LAYOUT_BATCHED,
+    LAYOUT_K_OFFSETS,
+    LAYOUT_N_OFFSETS,
     LAYOUT_OFFSETS,
     LAYOUT_PADDED,
     LAYOUT_STACKED,
@@ -19,6 +21,10 @@ from .ops import (  # noqa: F401
     f8f8bf16_rowwise_grouped_batched_preshuffle,
     f8f8bf16_rowwise_grouped_dynamic,
     f8f8bf16_rowwise_grouped_dynamic_preshuffle,
+    f8f8bf16_rowwise_grouped_k_offsets,
+    f8f8bf16_rowwise_grouped_mm,
+    f8f8bf16_rowwise_grouped_mm_preshuffle,
+    f8f8bf16_rowwise_grouped_n_offsets,
     f8f8bf16_rowwise_grouped_offsets,
     f8f8bf16_rowwise_grouped_offsets_preshuffle,
     f8f8bf16_rowwise_grouped_stacked,

@@ -16,6 +16,8 @@ LAYOUT_STACKED = 0
 LAYOUT_PADDED = 1
 LAYOUT_OFFSETS = 2
 LAYOUT_BATCHED = 3
+LAYOUT_N_OFFSETS = 4
+LAYOUT_K_OFFSETS = 5
 SHUFFLE_N = 32
 SHUFFLE_K = 64
 
@@ -29,6 +31,8 @@ EXPORTS = (
     "f8f8bf16_rowwise_grouped_offsets_preshuffle",
     "f8f8bf16_rowwise_grouped_batched",
     "f8f8bf16_rowwise_grouped_batched_preshuffle",
+    "f8f8bf16_rowwise_grouped_n_offsets",
+    "f8f8bf16_rowwise_grouped_k_offsets",
     "f8f8bf16_shuffle_b",
     "f8f8bf16_quantize_rowwise",
     "f8f8bf16_last_error",
@@ -80,6 +84,8 @@ def load() -> ctypes.CDLL:
     lib.f8f8bf16_rowwise_grouped_dynamic_preshuffle.argtypes = gemm + [I, P]
     lib.f8f8bf16_rowwise_grouped_offsets.argtypes = gemm + [P]
     lib.f8f8bf16_rowwise_grouped_offsets_preshuffle.argtypes = gemm + [P]
+    lib.f8f8bf16_rowwise_grouped_n_offsets.argtypes = gemm + [P]
+    lib.f8f8bf16_rowwise_grouped_k_offsets.argtypes = gemm + [P]
     batched = [P, P, P, P, P, I64, I64, I64, I64, P]
     lib.f8f8bf16_rowwise_grouped_batched.argtypes = batched
     lib.f8f8bf16_rowwise_grouped_batched_preshuffle.argtypes = batched

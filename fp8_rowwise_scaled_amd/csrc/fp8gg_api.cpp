@@ -63,12 +63,36 @@ int env_int(const char* name, int dflt) {
 // Packed layouts put the groups one after another along M (total rows M); slab
 // layouts give each group M rows (total rows G * M).
 bool packed(int layout) { return layout == FP8GG_LAYOUT_STACKED || layout == FP8GG_LAYOUT_OFFSETS; }
-int64_t total_rows(int layout, int64_t G, int64_t M) { return packed(layout) ? M : G * M; }
+bool ragged(int layout) { return layout == FP8GG_LAYOUT_N_OFFSETS || layout == FP8GG_LAYOUT_K_OFFSETS; }
+// Rows of Y: the n_offsets layout puts the groups side by side along N.
+int64_t total_rows(int layout, int64_t G, int64_t M) {
+  return packed(layout) || layout == FP8GG_LAYOUT_N_OFFSETS ? M : G * M;
+}
+
+// Element counts of each operand of a call (for size and aliasing checks).
+struct Extents {
+  int64_t x, w, xs, ws, y;
+};
+Extents extents(int layout, int64_t G, int64_t M, int64_t N, int64_t K) {
+  const int64_t rows = total_rows(layout, G, M);
+  switch (layout) {
+    case FP8GG_LAYOUT_N_OFFSETS: return {G * M * K, N * K, G * M, N, rows * N};
+    case FP8GG_LAYOUT_K_OFFSETS: return {M * K, N * K, G * M, G * N, rows * N};
+    default: {
+      const int64_t xrows = packed(layout) ? M : G * M;
+      return {xrows * K, G * N * K, xrows, G * N, rows * N};
+    }
+  }
+}
 
 // Shape checks shared by plan() and the entry points.
 fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
-  if (layout < FP8GG_LAYOUT_STACKED || layout > FP8GG_LAYOUT_BATCHED)
+  if (layout < FP8GG_LAYOUT_STACKED || layout > FP8GG_LAYOUT_K_OFFSETS)
     return fail(FP8GG_ERR_INVALID_ARGUMENT, "unknown layout %d", layout);
+  if (preshuffled && ragged(layout))
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE,
+                "pre-shuffled weights interleave N and K across the whole matrix; the n_offsets and k_offsets "
+                "layouts partition those axes, so they take plain weights only");
   if (G < 0 || M < 0 || N < 0 || K < 0)
     return fail(FP8GG_ERR_INVALID_ARGUMENT, "negative size (G=%lld M=%lld N=%lld K=%lld)", (long long)G,
                 (long long)M, (long long)N, (long long)K);
@@ -89,8 +113,11 @@ fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int6
   // far below overflow; 2^48 bytes is beyond any device memory.
   const int64_t rows = total_rows(layout, G, M);
   const int64_t cap = int64_t(1) << 48;
-  auto too_big = [cap](int64_t a, int64_t b) { return a > 0 && b > cap / a; };
-  if (too_big(rows, K) || too_big(G, N) || (G * N > 0 && too_big(G * N, K)) || too_big(rows, 2 * N))
+  auto too_big = [](int64_t a, int64_t b) { return a > 0 && b > (int64_t(1) << 48) / a; };
+  const int64_t xrows = layout == FP8GG_LAYOUT_K_OFFSETS ? M : (packed(layout) ? M : G * M);
+  const int64_t wrows = ragged(layout) ? N : G * N;
+  if (too_big(xrows, K) || too_big(G, N) || (wrows > 0 && too_big(wrows, K)) || too_big(rows, 2 * N) ||
+      G * M > cap / 4)
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "a tensor would exceed 2^48 bytes (G=%lld M=%lld N=%lld K=%lld)",
                 (long long)G, (long long)M, (long long)N, (long long)K);
   return FP8GG_OK;
@@ -104,8 +131,22 @@ fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int6
 // grid itself is sized from the device at launch.
 constexpr int64_t kPlanCus = 256;
 
+// The ragged layouts (n_offsets, k_offsets) run one tile per workgroup on the
+// configurations compiled for them (2, 7, 9, 18, 21), keyed on the slab height
+// and, for n_offsets, on the columns a group owns on average.
+bool ragged_config(int cfg) { return cfg == 2 || cfg == 7 || cfg == 9 || cfg == 18 || cfg == 21; }
+
+int select_ragged(int layout, int64_t G, int64_t M, int64_t N) {
+  const int64_t cols = layout == FP8GG_LAYOUT_N_OFFSETS && G > 0 ? (N + G - 1) / G : N;
+  if (M >= 256 && cols >= 256) return 7;
+  if (M >= 128) return 9;
+  if (M >= 48) return 2;
+  return cols <= 64 ? 21 : 18;
+}
+
 int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
   (void)K;
+  if (ragged(layout)) return select_ragged(layout, G, M, N);
   const int64_t per_group = packed(layout) ? (G > 0 ? (M + G - 1) / G : M) : M;
   const bool slab_with_padding = layout == FP8GG_LAYOUT_PADDED;
   // Calls with at least 256 rows per group whose tiles are all in use (every
@@ -181,8 +222,10 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
       return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_CONFIG=%d does not name a usable configuration", forced);
     cfg = forced;
   }
-  if (layout == FP8GG_LAYOUT_PADDED && fp8gg::kConfigs[cfg].kind == fp8gg::kKindPersistent)
+  if ((layout == FP8GG_LAYOUT_PADDED || ragged(layout)) && fp8gg::kConfigs[cfg].kind == fp8gg::kKindPersistent)
     cfg = fp8gg::kConfigs[cfg].twin;   // the persistent schedule covers the packed and batched layouts
+  if (ragged(layout) && !ragged_config(cfg))
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "configuration %d is not built for the n_offsets/k_offsets layouts", cfg);
   const fp8gg::KernelConfig& c = fp8gg::kConfigs[cfg];
   p->config_id = cfg;
   p->BM = c.BM;
@@ -200,6 +243,18 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
     p->m_tiles = ub < M ? ub : M;
     p->grid = p->m_tiles * p->n_tiles;
     p->persistent = c.kind == fp8gg::kKindPersistent ? 1 : 0;
+  } else if (layout == FP8GG_LAYOUT_N_OFFSETS) {
+    // Column tiles over the groups' ranges: sum of ceil(N_g / BN) <= ceil(N / BN)
+    // + G - 1, and each tile holds at least one column.
+    const int64_t ub = (N + c.BN - 1) / c.BN + G - 1;
+    p->n_tiles = ub < N ? ub : N;
+    p->m_tiles = (M + c.BM - 1) / c.BM;
+    p->grid = p->m_tiles * p->n_tiles;
+  } else if (layout == FP8GG_LAYOUT_K_OFFSETS) {
+    // Group slices are device-side: the last stage of every slice is masked.
+    p->k_tail = 1;
+    p->m_tiles = (M + c.BM - 1) / c.BM;
+    p->grid = p->m_tiles * p->n_tiles * G;
   } else if (layout == FP8GG_LAYOUT_BATCHED) {
     // Every group is a full slab: exactly G * ceil(M / BM) tiles.
     p->m_tiles = G * ((M + c.BM - 1) / c.BM);
@@ -235,7 +290,8 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
   }
   if (p.config_id < 0) return ok();
   const bool has_meta = layout != FP8GG_LAYOUT_BATCHED;
-  const int64_t meta_elem = layout == FP8GG_LAYOUT_OFFSETS ? 4 : 8;
+  const bool int32_meta = layout == FP8GG_LAYOUT_OFFSETS || ragged(layout);
+  const int64_t meta_elem = int32_meta ? 4 : 8;
   if (!XQ || !WQ || !xs || !ws || (has_meta && !meta))
     return fail(FP8GG_ERR_INVALID_ARGUMENT, "null input pointer (XQ=%p WQ=%p x_scale=%p w_scale=%p meta=%p)",
                 (const void*)XQ, (const void*)WQ, (const void*)xs, (const void*)ws, meta);
@@ -244,11 +300,12 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
   if (!aligned(xs, 4) || (has_meta && !aligned(meta, meta_elem)))
     return fail(FP8GG_ERR_INVALID_ARGUMENT, "x_scale must be 4-byte and the metadata %d-byte aligned",
                 (int)meta_elem);
-  const Range out{Y, rows * N * 2, "Y"};
-  const Range ins[] = {{XQ, rows * K, "XQ"},
-                       {WQ, G * N * K, "WQ"},
-                       {xs, rows * 4, "x_scale"},
-                       {ws, G * N * 4, "w_scale"},
+  const Extents ext = extents(layout, G, M, N, K);
+  const Range out{Y, ext.y * 2, "Y"};
+  const Range ins[] = {{XQ, ext.x, "XQ"},
+                       {WQ, ext.w, "WQ"},
+                       {xs, ext.xs * 4, "x_scale"},
+                       {ws, ext.ws * 4, "w_scale"},
                        {has_meta ? meta : nullptr, G * meta_elem, "metadata"}};
   for (const Range& r : ins)
     if (overlap(out, r)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y overlaps %s", r.name);
@@ -260,7 +317,7 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
   a.ws = ws;
   a.meta = layout == FP8GG_LAYOUT_STACKED || layout == FP8GG_LAYOUT_PADDED ? static_cast<const int64_t*>(meta)
                                                                              : nullptr;
-  a.offs = layout == FP8GG_LAYOUT_OFFSETS ? static_cast<const int32_t*>(meta) : nullptr;
+  a.offs = int32_meta ? static_cast<const int32_t*>(meta) : nullptr;
   a.Y = Y;
   a.G = G;
   a.M = M;
@@ -278,7 +335,9 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
                  (long long)p.n_tiles, p.persistent);
   const fp8gg::KernelConfig& cfg = fp8gg::kConfigs[p.config_id];
   hipError_t e;
-  if (cfg.kind == fp8gg::kKindPersistent) {
+  if (ragged(layout)) {
+    e = fp8gg::launch_gemm_ragged(layout, p.config_id, p.k_tail != 0, a, p.grid, s);
+  } else if (cfg.kind == fp8gg::kKindPersistent) {
     // One persistent workgroup per compute unit.  For tuning and tests,
     // FP8GG_TAIL_GRID overrides the grid and FP8GG_TAIL the remainder mode
     // (0 automatic, 1 whole tiles, 2 quarter tiles).
@@ -353,6 +412,18 @@ fp8gg_status f8f8bf16_rowwise_grouped_batched_preshuffle(const uint8_t* XQ, cons
                                                          int64_t G, int64_t M, int64_t N, int64_t K,
                                                          void* stream) {
   return run(FP8GG_LAYOUT_BATCHED, 1, XQ, WQs, x_scale, w_scale, nullptr, Y, G, M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_rowwise_grouped_n_offsets(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                                const float* w_scale, const int32_t* n_offsets, uint16_t* Y,
+                                                int64_t G, int64_t M, int64_t N, int64_t K, void* stream) {
+  return run(FP8GG_LAYOUT_N_OFFSETS, 0, XQ, WQ, x_scale, w_scale, n_offsets, Y, G, M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_rowwise_grouped_k_offsets(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                                const float* w_scale, const int32_t* k_offsets, uint16_t* Y,
+                                                int64_t G, int64_t M, int64_t N, int64_t K, void* stream) {
+  return run(FP8GG_LAYOUT_K_OFFSETS, 0, XQ, WQ, x_scale, w_scale, k_offsets, Y, G, M, N, K, 0, stream);
 }
 
 fp8gg_status f8f8bf16_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale, int64_t rows, int64_t K,

@@ -9,16 +9,20 @@
 namespace fp8gg {
 
 // Values match FP8GG_LAYOUT_* of the public header.
-enum Layout : int { kStacked = 0, kPadded = 1, kOffsets = 2, kBatched = 3 };
+enum Layout : int { kStacked = 0, kPadded = 1, kOffsets = 2, kBatched = 3, kNOffsets = 4, kKOffsets = 5 };
+
+// Layouts whose groups partition the output columns (n_offsets) or the
+// contraction (k_offsets) instead of the rows.
+inline bool is_ragged_layout(int layout) { return layout == kNOffsets || layout == kKOffsets; }
 
 // Operands of one grouped GEMM call, as the kernels see them.  Row-major, dense.
 struct GemmArgs {
-  const uint8_t* X;      // stacked, offsets: [M, K]; padded, batched: [G * M, K] (M = slab height)
-  const uint8_t* W;      // [G, N, K] (plain) or the pre-shuffled blocks
-  const float* xs;       // one scale per row of X
-  const float* ws;       // [G, N]
+  const uint8_t* X;      // stacked, offsets, k_offsets: [M, K]; padded, batched, n_offsets: [G * M, K]
+  const uint8_t* W;      // [G, N, K] (plain) or the pre-shuffled blocks; n_offsets, k_offsets: [N, K]
+  const float* xs;       // one scale per row of X; k_offsets: [G, M]
+  const float* ws;       // [G, N]; n_offsets: [N]
   const int64_t* meta;   // stacked: M_sizes [G]; padded: zero_start_index_M [G]; else unused
-  const int32_t* offs;   // offsets: inclusive row prefix [G]; else unused
+  const int32_t* offs;   // inclusive int32 prefix [G]: rows (offsets), W rows (n_offsets), K (k_offsets)
   uint16_t* Y;           // bf16 bits, one row per row of X, N columns
   int64_t G, M, N, K;
   int64_t m_tiles;       // packed: upper bound of M tiles over all groups; padded: per slab
@@ -68,6 +72,8 @@ hipError_t launch_gemm(int layout, int config_id, bool k_tail, const GemmArgs& a
                        int64_t grid, hipStream_t stream);
 hipError_t launch_gemm_persistent(int layout, int config_id, bool k_tail, const GemmArgs& args, int grid,
                                   int tail_mode, hipStream_t stream);
+hipError_t launch_gemm_ragged(int layout, int config_id, bool k_tail, const GemmArgs& args, int64_t grid,
+                              hipStream_t stream);
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t stream);
 hipError_t launch_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale, int64_t rows, int64_t K,
                                    hipStream_t stream);

@@ -259,6 +259,146 @@ __device__ __forceinline__ void zero_rect(uint16_t* Y, int64_t N, int64_t r0, in
   }
 }
 
+// Ragged layouts ([MSLK-471] commits adding the 3D-2D and 2D-2D forms of the
+// grouped mm): the groups partition W's rows, i.e. the output columns
+// (n_offsets: X [G, M, K], W [N, K], Y [M, N], w_scale [N]), or slice K
+// (k_offsets: X [M, K], W [N, K], Y [G, M, N], w_scale [G, N]).  Rows are numbered
+// in the [G * M] space of x_scale; X and Y rows are that number minus a
+// per-layout shift.
+struct RaggedTile : Tile {
+  int64_t x_delta;   // X row = row - x_delta
+  int64_t y_delta;   // Y row = row - y_delta
+  int64_t k0;        // first K byte of the group's slice (X and W rows)
+  int64_t klen;      // K bytes of the slice
+  int64_t n0;        // first output column of the tile
+  int64_t col_end;   // columns [n0, col_end) belong to the tile's group
+  int64_t w_off;     // byte offset of the group's first W row
+  int64_t ws_off;    // index of the group's first w_scale entry
+};
+
+// Accessors that give the plain layouts' fixed answers for a Tile and the
+// tile's own for a RaggedTile, so LdsTile serves both with no cost to the former.
+template <typename TT>
+struct IsRagged {
+  static constexpr bool value = false;
+};
+template <>
+struct IsRagged<RaggedTile> {
+  static constexpr bool value = true;
+};
+__device__ __forceinline__ int64_t tile_x_delta(const Tile&) { return 0; }
+__device__ __forceinline__ int64_t tile_x_delta(const RaggedTile& t) { return t.x_delta; }
+__device__ __forceinline__ int64_t tile_y_delta(const Tile&) { return 0; }
+__device__ __forceinline__ int64_t tile_y_delta(const RaggedTile& t) { return t.y_delta; }
+__device__ __forceinline__ int64_t tile_k0(const Tile&) { return 0; }
+__device__ __forceinline__ int64_t tile_k0(const RaggedTile& t) { return t.k0; }
+__device__ __forceinline__ int64_t tile_col_end(const GemmArgs& a, const Tile&) { return a.N; }
+__device__ __forceinline__ int64_t tile_col_end(const GemmArgs&, const RaggedTile& t) { return t.col_end; }
+__device__ __forceinline__ int64_t tile_w_off(const GemmArgs& a, const Tile& t) { return t.g * a.N * a.K; }
+__device__ __forceinline__ int64_t tile_w_off(const GemmArgs&, const RaggedTile& t) { return t.w_off; }
+__device__ __forceinline__ int64_t tile_ws_off(const GemmArgs& a, const Tile& t) { return t.g * a.N; }
+__device__ __forceinline__ int64_t tile_ws_off(const GemmArgs&, const RaggedTile& t) { return t.ws_off; }
+
+// Ends of groups g0 .. g0+7 of an int32 inclusive prefix, given the end s0 of
+// group g0 - 1: an end below its predecessor gives an empty group, ends are cut at
+// `limit`, groups past G end where the last one did.
+__device__ __forceinline__ void prefix_ends8(const int32_t* offs, int64_t G, int64_t g0, int64_t s0,
+                                             int64_t limit, int64_t (&end)[8]) {
+  int64_t v[8];
+  load_meta8(offs, g0, G, v);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int64_t e = v[i] > s0 ? v[i] : s0;
+    e = e > limit ? limit : e;
+    e = g0 + i < G ? e : s0;
+    end[i] = e;
+    s0 = e;
+  }
+}
+
+// n_offsets: workgroup b takes column tile b % n_tiles (counted over the groups'
+// column ranges, BN per tile, an upper bound of them launched) and row tile
+// b / n_tiles of the group's slab.
+template <int BM, int BN>
+__device__ __forceinline__ bool resolve_n_offsets(const GemmArgs& a, int64_t b, RaggedTile& t) {
+  const int64_t n_tile = b % a.n_tiles;
+  const int64_t m_tile = b / a.n_tiles;
+  int64_t start = 0, tiles_before = 0;
+  for (int64_t g0 = 0; g0 < a.G; g0 += 8) {
+    int64_t end[8], tiles[8];
+    prefix_ends8(a.offs, a.G, g0, start, a.N, end);
+    int64_t s0 = start;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      tiles[i] = (end[i] - s0 + BN - 1) / BN;
+      s0 = end[i];
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (n_tile < tiles_before + tiles[i]) {
+        const int64_t g = g0 + i;
+        t.g = g;
+        t.row_base = g * a.M + m_tile * BM;
+        t.row_end = g * a.M + a.M;
+        t.zero_end = t.row_end;
+        t.x_delta = 0;
+        t.y_delta = g * a.M;
+        t.k0 = 0;
+        t.klen = a.K;
+        t.n0 = start + (n_tile - tiles_before) * BN;
+        t.col_end = end[i];
+        t.w_off = 0;
+        t.ws_off = 0;
+        return t.row_base < t.row_end;
+      }
+      tiles_before += tiles[i];
+      start = end[i];
+    }
+  }
+  return false;
+}
+
+// k_offsets: the group is the slowest grid coordinate; its K slice is
+// [end of g - 1, end of g) of the prefix, each end rounded down to a multiple of
+// 16 bytes (the slices must be 16-byte aligned; rounding keeps any other value in
+// bounds).
+template <int BM, int BN>
+__device__ __forceinline__ bool resolve_k_offsets(const GemmArgs& a, int64_t b, RaggedTile& t) {
+  const int64_t n_tile = b % a.n_tiles;
+  const int64_t rest = b / a.n_tiles;
+  const int64_t m_tile = rest % a.m_tiles;
+  const int64_t g = rest / a.m_tiles;
+  if (g >= a.G) return false;
+  int64_t start = 0, ks = 0, ke = 0;
+  for (int64_t g0 = 0; g0 <= g; g0 += 8) {
+    int64_t end[8];
+    prefix_ends8(a.offs, a.G, g0, start, a.K, end);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      if (g0 + i == g) {
+        ks = i == 0 ? start : end[i - 1];
+        ke = end[i];
+      }
+    }
+    start = end[7];
+  }
+  ks &= ~(int64_t)15;
+  ke &= ~(int64_t)15;
+  t.g = g;
+  t.row_base = g * a.M + m_tile * BM;
+  t.row_end = g * a.M + a.M;
+  t.zero_end = t.row_end;
+  t.x_delta = g * a.M;
+  t.y_delta = 0;
+  t.k0 = ks;
+  t.klen = ke - ks;
+  t.n0 = n_tile * BN;
+  t.col_end = a.N;
+  t.w_off = 0;
+  t.ws_off = g * a.N;
+  return t.row_base < t.row_end;
+}
+
 // ---------------------------------------------------------------------------
 // The grouped GEMM with both operands staged through LDS (plain or pre-shuffled W)
 // ---------------------------------------------------------------------------
@@ -340,8 +480,12 @@ struct LdsTile {
   // Copy descriptors (global source at k = 0) for the tile at rows t, columns n0.
   // Chunk q of a stage (16 bytes) lands at LDS byte 16*q: row p = q / CPR, physical
   // chunk q % CPR, which holds logical chunk (q % CPR) ^ lds_swz<BK>(p).
-  __device__ __forceinline__ void setup(const GemmArgs& a, const Tile& t, int64_t n0) {
-    const int64_t N = a.N, K = a.K;
+  template <typename TT>
+  __device__ __forceinline__ void setup(const GemmArgs& a, const TT& t, int64_t n0) {
+    static_assert(!(IsRagged<TT>::value && PRE), "pre-shuffled W only where a group owns a whole [N, K]");
+    const int64_t K = a.K;
+    const int64_t k0 = tile_k0(t);
+    const int64_t xd = tile_x_delta(t);
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int q = i * NT + tid;
@@ -349,13 +493,13 @@ struct LdsTile {
       const int c = (q % CPR) ^ lds_swz<BK>(p);
       int64_t row = t.row_base + p;
       row = row < t.row_end ? row : t.row_end - 1;   // rows past the group: any valid row, result dropped
-      a_src[i] = a.X + row * K + c * 16;
+      a_src[i] = a.X + (row - xd) * K + k0 + c * 16;
       a_kc[i] = c * 16;
     }
     if constexpr (PRE) {
       // A stage is BN/32 N blocks x KS K blocks of 2048 bytes, copied linearly:
       // chunk q is byte 16*(q % 128) of stage block q / 128 = (N block j, K block ks).
-      const int64_t nbn = N / 32, nbk = K / 64;
+      const int64_t nbn = a.N / 32, nbk = K / 64;
 #pragma unroll
       for (int i = 0; i < B_LOADS; ++i) {
         const int q = i * NT + tid;
@@ -368,7 +512,8 @@ struct LdsTile {
       }
       return;
     }
-    const uint8_t* Wg = a.W + t.g * N * K;
+    const uint8_t* Wg = a.W + tile_w_off(a, t) + k0;
+    const int64_t cend = tile_col_end(a, t);
 #pragma unroll
     for (int i = 0; i < B_LOADS; ++i) {
       const int q = i * NT + tid;
@@ -382,7 +527,7 @@ struct LdsTile {
       const int rho = pp & 31;
       const int nl = wn_ * TN + ((rho >> 2) & 1) * 16 * FN + 16 * fn + 4 * (rho >> 3) + (rho & 3);
       int64_t n = n0 + nl;
-      n = n < N ? n : N - 1;                            // columns past N: result dropped
+      n = n < cend ? n : cend - 1;                      // columns past the group: result dropped
       b_src[i] = Wg + n * K + c * 16;
       b_kc[i] = c * 16;
     }
@@ -574,20 +719,27 @@ struct LdsTile {
   // i = 4*j + tt, output row wm*TM + 32*fm + r32 and column col0 + 16*fn + i; pair
   // q of Packed[fm][fn] holds slots 2q and 2q + 1.
 
-  __device__ __forceinline__ void scale(const GemmArgs& a, const Tile& t, int64_t n0, const Acc& acc,
+  template <typename TT>
+  __device__ __forceinline__ void scale(const GemmArgs& a, const TT& t, int64_t n0, const Acc& acc,
                                         Packed& pk) const {
-    const int64_t N = a.N;
-    const float* wsg = a.ws + t.g * N;
+    const int64_t cend = tile_col_end(a, t);
+    const float* wsg = a.ws + tile_ws_off(a, t);
     float wsv[16 * FN];
 #pragma unroll
     for (int v = 0; v < 4 * FN; ++v) {
       const int64_t c = n0 + col_of(v / 4) + 4 * (v % 4);
-      v4f w4 = {0.f, 0.f, 0.f, 0.f};
-      if (c < N) w4 = *(const v4f*)(wsg + c);
-      wsv[4 * v + 0] = w4.x;
-      wsv[4 * v + 1] = w4.y;
-      wsv[4 * v + 2] = w4.z;
-      wsv[4 * v + 3] = w4.w;
+      if constexpr (IsRagged<TT>::value) {
+        // a group's columns may start anywhere: scalar loads, each masked
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wsv[4 * v + e] = c + e < cend ? wsg[c + e] : 0.f;
+      } else {
+        v4f w4 = {0.f, 0.f, 0.f, 0.f};
+        if (c < cend) w4 = *(const v4f*)(wsg + c);
+        wsv[4 * v + 0] = w4.x;
+        wsv[4 * v + 1] = w4.y;
+        wsv[4 * v + 2] = w4.z;
+        wsv[4 * v + 3] = w4.w;
+      }
     }
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
@@ -609,17 +761,32 @@ struct LdsTile {
     }
   }
 
-  __device__ __forceinline__ void store(const GemmArgs& a, const Tile& t, int64_t n0, const Packed& pk) const {
+  template <typename TT>
+  __device__ __forceinline__ void store(const GemmArgs& a, const TT& t, int64_t n0, const Packed& pk) const {
     const int64_t N = a.N;
+    const int64_t cend = tile_col_end(a, t);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       const int64_t m = t.row_base + wm * TM + 32 * fm + r32;
       if (m < t.row_end) {
-        uint16_t* yrow = a.Y + m * N;
+        uint16_t* yrow = a.Y + (m - tile_y_delta(t)) * N;
 #pragma unroll
         for (int s = 0; s < 2 * FN; ++s) {           // 8 columns per 16-byte store
           const int64_t c = n0 + col_of(s >> 1) + 8 * (s & 1);
-          if (c < N) *(v4i*)(yrow + c) = pk[fm][s >> 1][s & 1];
+          if constexpr (IsRagged<TT>::value) {
+            // A group's columns may start or end inside a vector: such vectors are
+            // stored column by column, each column up to the group's end.
+            if ((c & 7) == 0 && c + 8 <= cend) {
+              *(v4i*)(yrow + c) = pk[fm][s >> 1][s & 1];
+            } else if (c < cend) {
+              const v4i v = pk[fm][s >> 1][s & 1];
+#pragma unroll
+              for (int e = 0; e < 8; ++e)
+                if (c + e < cend) yrow[c + e] = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
+            }
+          } else {
+            if (c < cend) *(v4i*)(yrow + c) = pk[fm][s >> 1][s & 1];
+          }
         }
       } else if (m < t.zero_end) {
         uint16_t* yrow = a.Y + m * N;
@@ -632,7 +799,8 @@ struct LdsTile {
     }
   }
 
-  __device__ __forceinline__ void epilogue(const GemmArgs& a, const Tile& t, int64_t n0, const Acc& acc) const {
+  template <typename TT>
+  __device__ __forceinline__ void epilogue(const GemmArgs& a, const TT& t, int64_t n0, const Acc& acc) const {
     Packed pk;
     scale(a, t, n0, acc, pk);
     store(a, t, n0, pk);
@@ -675,6 +843,34 @@ gg_lds_kernel(GemmArgs a) {
   const int nk = (int)((a.K + BK - 1) / BK);
   e.run(0, nk, nk, a.K, acc);
   e.epilogue(a, t, n0, acc);
+}
+
+// Ragged layouts (n_offsets, k_offsets): one tile per workgroup, both operands
+// through LDS, plain W only.  The K loop runs over the tile's group slice, whose
+// length is only known on the device (k_offsets), so the trip count is a runtime
+// value and the tail mask is keyed on the slice's own end.
+template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL>
+__global__ void __launch_bounds__(WM * WN * 64)
+gg_ragged_kernel(GemmArgs a) {
+  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL, false> E;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
+  RaggedTile t;
+  if constexpr (LAYOUT == kNOffsets) {
+    if (!resolve_n_offsets<BM, BN>(a, blockIdx.x, t)) return;
+  } else {
+    if (!resolve_k_offsets<BM, BN>(a, blockIdx.x, t)) return;
+  }
+  E e;
+  e.init(smem);
+  e.setup(a, t, t.n0);
+  typename E::Acc acc;
+#pragma unroll
+  for (int i = 0; i < E::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < E::FN; ++j) acc[i][j] = v16f{0};
+  const int nk = (int)((t.klen + BK - 1) / BK);
+  e.run(0, nk, nk, t.klen, acc);
+  e.epilogue(a, t, t.n0, acc);
 }
 
 // Number of M tiles over all groups of a packed layout, with the resolver's clamping.
@@ -1247,6 +1443,42 @@ hipError_t launch_gemm(int layout, int config_id, bool k_tail, const GemmArgs& a
     case kPadded: return launch_layout<kPadded>(config_id, k_tail, a, grid, s);
     case kOffsets: return launch_layout<kOffsets>(config_id, k_tail, a, grid, s);
     case kBatched: return launch_layout<kBatched>(config_id, k_tail, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES>
+static hipError_t launch_ragged(bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
+  const dim3 block(WM * WN * 64);
+  // k_offsets: the slices' lengths are device-side, so the tail mask is always in
+  if (k_tail || LAYOUT == kKOffsets)
+    hipLaunchKernelGGL((gg_ragged_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, true>), dim3((uint32_t)grid), block, 0,
+                       s, a);
+  else
+    hipLaunchKernelGGL((gg_ragged_kernel<LAYOUT, BM, BN, BK, WM, WN, STAGES, false>), dim3((uint32_t)grid), block,
+                       0, s, a);
+  return hipGetLastError();
+}
+
+// The configurations the ragged layouts are built for (a subset of kConfigs with
+// plain W and one tile per workgroup).
+template <int LAYOUT>
+static hipError_t launch_ragged_layout(int config_id, bool k_tail, const GemmArgs& a, int64_t grid, hipStream_t s) {
+  switch (config_id) {
+    case 2: return launch_ragged<LAYOUT, 64, 256, 64, 1, 4, 2>(k_tail, a, grid, s);
+    case 7: return launch_ragged<LAYOUT, 256, 256, 128, 2, 4, 2>(k_tail, a, grid, s);
+    case 9: return launch_ragged<LAYOUT, 128, 256, 128, 2, 4, 3>(k_tail, a, grid, s);
+    case 18: return launch_ragged<LAYOUT, 32, 128, 128, 1, 4, 3>(k_tail, a, grid, s);
+    case 21: return launch_ragged<LAYOUT, 32, 64, 128, 1, 2, 4>(k_tail, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_gemm_ragged(int layout, int config_id, bool k_tail, const GemmArgs& a, int64_t grid,
+                              hipStream_t s) {
+  switch (layout) {
+    case kNOffsets: return launch_ragged_layout<kNOffsets>(config_id, k_tail, a, grid, s);
+    case kKOffsets: return launch_ragged_layout<kKOffsets>(config_id, k_tail, a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

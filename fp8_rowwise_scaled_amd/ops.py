@@ -156,6 +156,93 @@ def f8f8bf16_rowwise_grouped_batched_preshuffle(XQ, WQs, x_scale, w_scale, out=N
     return _batched("f8f8bf16_rowwise_grouped_batched_preshuffle", XQ, WQs, x_scale, w_scale, out)
 
 
+def f8f8bf16_rowwise_grouped_n_offsets(XQ, WQ, x_scale, w_scale, n_offsets, out=None):
+    """Y [M, total_N] bf16 for the n_offsets (3D-2D) layout: XQ [G, M, K], WQ
+    [total_N, K], x_scale [G, M], w_scale [total_N], n_offsets [G] int32 inclusive
+    prefix over W's rows (see include/fp8gg.h)."""
+    XQ = _bytes(XQ, "XQ")
+    WQ = _bytes(WQ, "WQ")
+    if XQ.dim() != 3 or WQ.dim() != 2:
+        raise ValueError("XQ must be [G, M, K] and WQ [total_N, K]")
+    G, M, K = XQ.shape
+    N, K2 = WQ.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: XQ has {K}, WQ has {K2}")
+    _check(XQ, "XQ", torch.uint8, (G, M, K))
+    _check(WQ, "WQ", torch.uint8, (N, K))
+    _check(x_scale, "x_scale", torch.float32, (G, M))
+    _check(w_scale, "w_scale", torch.float32, (N,))
+    _check(n_offsets, "n_offsets", torch.int32, (G,))
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=XQ.device)
+    _check(out, "out", torch.bfloat16, (M, N))
+    st = _lib.load().f8f8bf16_rowwise_grouped_n_offsets(XQ.data_ptr(), WQ.data_ptr(), x_scale.data_ptr(),
+                                                        w_scale.data_ptr(), n_offsets.data_ptr(), out.data_ptr(),
+                                                        G, M, N, K, _stream(XQ.device))
+    _lib.check(st, "f8f8bf16_rowwise_grouped_n_offsets")
+    return out
+
+
+def f8f8bf16_rowwise_grouped_k_offsets(XQ, WQ, x_scale, w_scale, k_offsets, out=None):
+    """Y [G, M, N] bf16 for the k_offsets (2D-2D) layout: XQ [M, total_K], WQ
+    [N, total_K], x_scale [G, M], w_scale [G, N], k_offsets [G] int32 inclusive
+    prefix over K, multiples of 16 (see include/fp8gg.h)."""
+    XQ = _bytes(XQ, "XQ")
+    WQ = _bytes(WQ, "WQ")
+    if XQ.dim() != 2 or WQ.dim() != 2:
+        raise ValueError("XQ must be [M, total_K] and WQ [N, total_K]")
+    M, K = XQ.shape
+    N, K2 = WQ.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: XQ has {K}, WQ has {K2}")
+    if k_offsets.dim() != 1:
+        raise ValueError("k_offsets must be [G]")
+    G = k_offsets.shape[0]
+    _check(XQ, "XQ", torch.uint8, (M, K))
+    _check(WQ, "WQ", torch.uint8, (N, K))
+    _check(x_scale, "x_scale", torch.float32, (G, M))
+    _check(w_scale, "w_scale", torch.float32, (G, N))
+    _check(k_offsets, "k_offsets", torch.int32, (G,))
+    if out is None:
+        out = torch.empty((G, M, N), dtype=torch.bfloat16, device=XQ.device)
+    _check(out, "out", torch.bfloat16, (G, M, N))
+    st = _lib.load().f8f8bf16_rowwise_grouped_k_offsets(XQ.data_ptr(), WQ.data_ptr(), x_scale.data_ptr(),
+                                                        w_scale.data_ptr(), k_offsets.data_ptr(), out.data_ptr(),
+                                                        G, M, N, K, _stream(XQ.device))
+    _lib.check(st, "f8f8bf16_rowwise_grouped_k_offsets")
+    return out
+
+
+def f8f8bf16_rowwise_grouped_mm(XQ, WQ, x_scale, w_scale, offs=None, out=None):
+    """The grouped mm: picks the grouped axis from the operand ranks ([MSLK-471],
+    commit mapping the four rank combinations onto the kernel's layouts):
+    2D-3D -> offsets (groups along M), 3D-3D -> batched (offs unused),
+    3D-2D -> n_offsets (groups along N), 2D-2D -> k_offsets (groups along K)."""
+    ra, rb = XQ.dim(), WQ.dim()
+    if (ra, rb) == (2, 3):
+        return f8f8bf16_rowwise_grouped_offsets(XQ, WQ, x_scale, w_scale, offs, out=out)
+    if (ra, rb) == (3, 3):
+        return f8f8bf16_rowwise_grouped_batched(XQ, WQ, x_scale, w_scale, out=out)
+    if (ra, rb) == (3, 2):
+        return f8f8bf16_rowwise_grouped_n_offsets(XQ, WQ, x_scale, w_scale, offs, out=out)
+    if (ra, rb) == (2, 2):
+        return f8f8bf16_rowwise_grouped_k_offsets(XQ, WQ, x_scale, w_scale, offs, out=out)
+    raise ValueError(f"no grouped layout for operand ranks {ra}D-{rb}D")
+
+
+def f8f8bf16_rowwise_grouped_mm_preshuffle(XQ, WQs, x_scale, w_scale, offs=None, out=None):
+    """The grouped mm on pre-shuffled weights: only the ranks where every group
+    owns a whole [N, K] (2D-3D, 3D-3D); the others raise rather than read shuffled
+    weights as plain ones."""
+    ra, rb = XQ.dim(), WQs.dim()
+    if (ra, rb) == (2, 3):
+        return f8f8bf16_rowwise_grouped_offsets_preshuffle(XQ, WQs, x_scale, w_scale, offs, out=out)
+    if (ra, rb) == (3, 3):
+        return f8f8bf16_rowwise_grouped_batched_preshuffle(XQ, WQs, x_scale, w_scale, out=out)
+    raise ValueError(f"pre-shuffled weights are not accepted for operand ranks {ra}D-{rb}D "
+                     "(the groups would split the shuffled blocks)")
+
+
 def f8f8bf16_shuffle_b(WQ, out=None):
     """Rearranges WQ [G, N, K] into the pre-shuffled layout (same shape and bytes)."""
     WQ = _bytes(WQ, "WQ")

@@ -170,6 +170,61 @@ fp8gg_status f8f8bf16_rowwise_grouped_batched_preshuffle(
     uint16_t* Y, int64_t G, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * N-offsets layout (the 3D-2D ranks of the grouped mm: MSLK #471, commit adding
+ * that form, and the commit that predicates stores on their last column): the
+ * weights are one matrix whose rows (the output columns) the groups partition;
+ * group g multiplies its own slab of XQ against its rows of WQ, and the results
+ * sit side by side in Y.
+ *
+ *   XQ        [G, M, K]     fp8 e4m3fn, one slab of M rows per group
+ *   WQ        [N, K]        fp8 e4m3fn, N = total_N over all groups
+ *   x_scale   [G, M]        fp32
+ *   w_scale   [N]           fp32, one per row of WQ
+ *   n_offsets [G]           int32 inclusive prefix: group g owns W rows / output
+ *                           columns [n_offsets[g-1], n_offsets[g]) (n_offsets[-1] = 0)
+ *   Y         [M, N]        bf16:  Y[m, n] = (sum_k XQ[g, m, k] WQ[n, k]) x_scale[g, m] w_scale[n]
+ *
+ * The offsets are clamped in-kernel like those of the offsets layout (an end below
+ * its predecessor gives an empty group, ends are cut at N); columns past the last
+ * end are left untouched.  A group's columns may start and end anywhere: every
+ * column of every group is written (vectors that straddle a group boundary are
+ * stored column by column).  Plain WQ only: pre-shuffled weights interleave N
+ * across group boundaries (MSLK #471, commit adding the mm preshuffle entry
+ * point), so this layout has no _preshuffle sibling.  Shape rules as above
+ * (K % 16 == 0, N % 8 == 0).
+ */
+fp8gg_status f8f8bf16_rowwise_grouped_n_offsets(
+    const uint8_t* XQ, const uint8_t* WQ, const float* x_scale, const float* w_scale,
+    const int32_t* n_offsets, uint16_t* Y,
+    int64_t G, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
+ * K-offsets layout (the 2D-2D ranks of the grouped mm: MSLK #471, commit adding
+ * that form, and the commit keying the K-tail predicate on the group's own slice):
+ * both operands are one matrix whose K columns the groups slice; every group
+ * contracts over its own slice and produces a whole [M, N] output.
+ *
+ *   XQ        [M, K]        fp8 e4m3fn, K = total_K over all groups
+ *   WQ        [N, K]        fp8 e4m3fn
+ *   x_scale   [G, M]        fp32, one per row of each group's slice of XQ
+ *   w_scale   [G, N]        fp32, one per row of each group's slice of WQ
+ *   k_offsets [G]           int32 inclusive prefix: group g contracts over
+ *                           [k_offsets[g-1], k_offsets[g]) (k_offsets[-1] = 0)
+ *   Y         [G, M, N]     bf16:  Y[g, m, n] = (sum_{k in slice g} XQ[m, k] WQ[n, k]) x_scale[g, m] w_scale[g, n]
+ *
+ * Every element of Y is written; an empty slice gives (0 * x_scale) * w_scale.
+ * The offsets must be multiples of 16 (the load granule); in-kernel they are
+ * clamped like the offsets layout's (ends cut at K, an end below its predecessor
+ * gives an empty slice) and rounded down to a multiple of 16, so other values
+ * never cause an out-of-bounds access but give unspecified results.  Plain WQ
+ * only (no _preshuffle sibling).  Shape rules as above.
+ */
+fp8gg_status f8f8bf16_rowwise_grouped_k_offsets(
+    const uint8_t* XQ, const uint8_t* WQ, const float* x_scale, const float* w_scale,
+    const int32_t* k_offsets, uint16_t* Y,
+    int64_t G, int64_t M, int64_t N, int64_t K, void* stream);
+
+/*
  * Rearranges WQ [G, N, K] into the pre-shuffled order WQs (same size, must not
  * overlap WQ).  Byte layout: for group g, N-block nb (FP8GG_SHUFFLE_N rows) and
  * K-block kb (FP8GG_SHUFFLE_K bytes), the 2048-byte block at
@@ -224,10 +279,18 @@ typedef struct {
                          schedule                                                   */
 } fp8gg_plan;
 
-enum { FP8GG_LAYOUT_STACKED = 0, FP8GG_LAYOUT_PADDED = 1, FP8GG_LAYOUT_OFFSETS = 2, FP8GG_LAYOUT_BATCHED = 3 };
+enum {
+  FP8GG_LAYOUT_STACKED = 0,
+  FP8GG_LAYOUT_PADDED = 1,
+  FP8GG_LAYOUT_OFFSETS = 2,
+  FP8GG_LAYOUT_BATCHED = 3,
+  FP8GG_LAYOUT_N_OFFSETS = 4,
+  FP8GG_LAYOUT_K_OFFSETS = 5
+};
 
 /* M is total_M for the stacked and offsets layouts, expected_m for the padded one
- * and the slab height for the batched one.
+ * and the slab height for the batched, n_offsets and k_offsets ones; N is total_N
+ * for n_offsets and K is total_K for k_offsets.
  * Performs the same shape checks as the GEMM entry points. */
 fp8gg_status f8f8bf16_plan(int layout, int preshuffled, int64_t G, int64_t M,
                            int64_t N, int64_t K, fp8gg_plan* out);

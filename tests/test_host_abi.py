@@ -22,7 +22,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     lib = _lib.load()
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 15
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(_lib.EXPORTS)
@@ -55,7 +55,7 @@ def test_plan_batched_is_exact():
 
 def test_plan_refuses_unknown_layout():
     with pytest.raises(ValueError):
-        F.plan(4, False, 1, 1, 8, 16)
+        F.plan(6, False, 1, 1, 8, 16)
     with pytest.raises(ValueError):
         F.plan(-1, False, 1, 1, 8, 16)
 
@@ -118,6 +118,53 @@ def test_entry_points_refuse_before_any_gpu_call():
     # empty output: nothing to do, even with null pointers
     st = lib.f8f8bf16_rowwise_grouped_stacked(None, None, None, None, None, None, 4, 0, 16, 32, None)
     assert st == _lib.OK and F.last_error() == ""
+
+
+def test_plan_n_offsets_bounds_column_tiles():
+    """n_offsets: column tiles over the groups' ranges are at most ceil(N/BN) + G - 1
+    (each holds a column), row tiles cover one slab."""
+    for G, M, N, K in [(8, 512, 16384, 7168), (5, 40, 1000, 208), (64, 3, 64, 32)]:
+        p = F.plan(F.LAYOUT_N_OFFSETS, False, G, M, N, K)
+        assert p["n_tiles"] == min(-(-N // p["BN"]) + G - 1, N)
+        assert p["m_tiles"] == -(-M // p["BM"])
+        assert p["grid"] == p["m_tiles"] * p["n_tiles"]
+        assert p["persistent"] == 0 and p["k_tail"] == (K % p["BK"] != 0)
+
+
+def test_plan_k_offsets_always_masks_the_tail():
+    p = F.plan(F.LAYOUT_K_OFFSETS, False, 8, 2048, 7168, 4096)
+    assert p["k_tail"] == 1 and p["persistent"] == 0
+    assert p["grid"] == 8 * p["m_tiles"] * p["n_tiles"]
+
+
+def test_ragged_layouts_refuse_preshuffled_weights():
+    for layout in (F.LAYOUT_N_OFFSETS, F.LAYOUT_K_OFFSETS):
+        with pytest.raises(ValueError, match="plain weights only"):
+            F.plan(layout, True, 2, 64, 256, 256)
+
+
+def test_ragged_layouts_refuse_configurations_not_built_for_them(monkeypatch):
+    monkeypatch.setenv("FP8GG_CONFIG", "0")
+    with pytest.raises(ValueError, match="not built"):
+        F.plan(F.LAYOUT_N_OFFSETS, False, 2, 64, 256, 256)
+    monkeypatch.setenv("FP8GG_CONFIG", "16")     # persistent: runs its one-tile twin
+    assert F.plan(F.LAYOUT_K_OFFSETS, False, 2, 64, 256, 256)["config_id"] == 7
+
+
+def test_ragged_entry_points_refuse_on_the_host():
+    lib = _lib.load()
+    a = 0x10000000
+    st = lib.f8f8bf16_rowwise_grouped_n_offsets(a, a, a, a, a, a + 0x1000000, 2, 8, 12, 32, None)
+    assert st == _lib.ERR_UNSUPPORTED_SHAPE and "multiple of 8" in F.last_error()
+    # Y [G, M, N] = 2*8*16 bf16 = 512 bytes from a + 0x100: overlaps WQ at a + 0x200
+    st = lib.f8f8bf16_rowwise_grouped_k_offsets(a + 0x10000, a + 0x200, a + 0x20000, a + 0x30000, a + 0x40000,
+                                                a + 0x100, 2, 8, 16, 32, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT and "overlaps WQ" in F.last_error()
+    st = lib.f8f8bf16_rowwise_grouped_k_offsets(a, a, a, a, a + 2, a + 0x1000000, 2, 8, 16, 32, None)
+    assert st == _lib.ERR_INVALID_ARGUMENT and "aligned" in F.last_error()
+    # no groups, no elements: nothing to do
+    st = lib.f8f8bf16_rowwise_grouped_k_offsets(None, None, None, None, None, None, 0, 8, 16, 32, None)
+    assert st == _lib.OK
 
 
 def test_num_configs():
