@@ -10,7 +10,19 @@
 // One workgroup of 256 threads per row (grid-stride over rows).  A row of up to
 // 8192 values is read once into registers (16 bytes = 8 values per load, four
 // loads per thread); longer rows are read twice, the second time from L2.  The
-// call moves 3 bytes per element (2 read, 1 written) and is bound by HBM.
+// call moves 3 bytes per element (2 read, 1 written) and is bound by HBM, so the
+// per-element arithmetic is kept short:
+//   * the quotient x / s is formed from the row's reciprocal r = 1 / s (one IEEE
+//     division per row) and two FMA correction steps per element,
+//         q = x r;  q += (x - q s) r;  q += (x - q s) r,
+//     which is the correctly rounded quotient by Markstein's theorem (r correctly
+//     rounded, the first corrected q faithful, each residual x - q s exact).  The
+//     residuals are exact as long as nothing underflows, which holds for
+//     s >= 2^-64; rows with a smaller scale use the IEEE division itself;
+//   * the code comes from the hardware fp8 convert (v_cvt_pk_fp8_f32: OCP e4m3fn,
+//     round to nearest even), two values per instruction, on the clamped quotient,
+//     with the input's sign bit copied into each code (the convert returns +0 for
+//     a zero result, the encoding keeps -0 as 0x80).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -26,26 +38,6 @@ typedef int v2i_q __attribute__((ext_vector_type(2)));
 constexpr int kQThreads = 256;
 constexpr int kQRegVecs = 4;      // 16-byte vectors per thread held across the two passes
 constexpr float kE4M3Max = 448.0f;
-
-// e4m3fn code of an fp32 value with |v| <= 448, round to nearest, ties to even.
-// Below 2^-6 the format is subnormal with a fixed step of 2^-9, so the code is the
-// rounded multiple of that step (8 rounds up into the smallest normal, code 8).
-// Above, rounding the fp32 pattern's exponent and top three mantissa bits as one
-// integer (ties to even) carries into the exponent by itself; rebasing the
-// exponent from bias 127 to bias 7 gives the code.  The sign bit is copied.
-__device__ __forceinline__ uint32_t e4m3fn_rne(float v) {
-  const uint32_t b = __float_as_uint(v);
-  const uint32_t sign = (b >> 24) & 0x80u;
-  const uint32_t mag = b & 0x7FFFFFFFu;
-  uint32_t code;
-  if (mag < 0x3C800000u) {
-    code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
-  } else {
-    const uint32_t r = (mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20;
-    code = r - ((127u - 7u) << 3);
-  }
-  return sign | code;
-}
 
 __device__ __forceinline__ float bf16_lo(int w) { return __uint_as_float((uint32_t)w << 16); }
 __device__ __forceinline__ float bf16_hi(int w) { return __uint_as_float((uint32_t)w & 0xFFFF0000u); }
@@ -64,16 +56,39 @@ __device__ __forceinline__ float clamp448(float y) {
   return y > kE4M3Max ? kE4M3Max : (y < -kE4M3Max ? -kE4M3Max : y);
 }
 
+// Rows whose scale is at least this use the reciprocal-and-correction quotient.
+constexpr float kFastScaleMin = 0x1p-64f;
+
+// RN(x / s) from r = RN(1 / s): see the file header.
+__device__ __forceinline__ float quotient(float x, float s, float r) {
+  float q = x * r;
+  q = __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+  return __builtin_fmaf(__builtin_fmaf(-q, s, x), r, q);
+}
+
 // Eight bf16 values -> eight e4m3fn codes (little-endian bytes in two words).
-__device__ __forceinline__ v2i_q quantize8(const v4i_q& v, float s) {
-  uint32_t w[2] = {0u, 0u};
+// FAST: the row's scale admits the reciprocal quotient (else IEEE division).
+template <bool FAST>
+__device__ __forceinline__ v2i_q quantize8(const v4i_q& v, float s, float r) {
+  int w[2] = {0, 0};
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const uint32_t lo = e4m3fn_rne(clamp448(bf16_lo(v[j]) / s));
-    const uint32_t hi = e4m3fn_rne(clamp448(bf16_hi(v[j]) / s));
-    w[j >> 1] |= (lo | (hi << 8)) << (16 * (j & 1));
+    const float a = FAST ? quotient(bf16_lo(v[j]), s, r) : bf16_lo(v[j]) / s;
+    const float b = FAST ? quotient(bf16_hi(v[j]), s, r) : bf16_hi(v[j]) / s;
+    // elements 2j and 2j + 1 to bytes 2j and 2j + 1: half j & 1 of word j >> 1
+    if (j & 1) w[j >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), w[j >> 1], true);
+    else w[j >> 1] = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), w[j >> 1], false);
   }
-  return v2i_q{(int)w[0], (int)w[1]};
+  // The convert writes a zero result as +0 (code 0x00); the code keeps the
+  // quotient's sign, which is the input's (s > 0): OR each input's sign bit into
+  // its byte (a no-op for non-zero codes, which carry it already).
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t lo = (uint32_t)v[2 * h], hi = (uint32_t)v[2 * h + 1];
+    const uint32_t sign = ((lo >> 8) & 0x80u) | ((lo >> 16) & 0x8000u) | ((hi << 8) & 0x800000u) | (hi & 0x80000000u);
+    w[h] = (int)((uint32_t)w[h] | sign);
+  }
+  return v2i_q{w[0], w[1]};
 }
 
 __global__ void __launch_bounds__(kQThreads) quantize_rowwise_kernel(const v4i_q* __restrict__ X,
@@ -109,14 +124,27 @@ __global__ void __launch_bounds__(kQThreads) quantize_rowwise_kernel(const v4i_q
     __syncthreads();   // wave_max is rewritten by the next row
     const float s = amax > 0.f ? amax / kE4M3Max : 1.f;
     v2i_q* qr = XQ + row * nvec;
-    if (in_regs) {
+    if (s >= kFastScaleMin) {
+      const float r = 1.f / s;
+      if (in_regs) {
 #pragma unroll
-      for (int i = 0; i < kQRegVecs; ++i) {
-        const int64_t j = (int64_t)i * kQThreads + tid;
-        if (j < nvec) qr[j] = quantize8(held[i], s);
+        for (int i = 0; i < kQRegVecs; ++i) {
+          const int64_t j = (int64_t)i * kQThreads + tid;
+          if (j < nvec) qr[j] = quantize8<true>(held[i], s, r);
+        }
+      } else {
+        for (int64_t j = tid; j < nvec; j += kQThreads) qr[j] = quantize8<true>(xr[j], s, r);
       }
     } else {
-      for (int64_t j = tid; j < nvec; j += kQThreads) qr[j] = quantize8(xr[j], s);
+      if (in_regs) {
+#pragma unroll
+        for (int i = 0; i < kQRegVecs; ++i) {
+          const int64_t j = (int64_t)i * kQThreads + tid;
+          if (j < nvec) qr[j] = quantize8<false>(held[i], s, 0.f);
+        }
+      } else {
+        for (int64_t j = tid; j < nvec; j += kQThreads) qr[j] = quantize8<false>(xr[j], s, 0.f);
+      }
     }
     if (tid == 0) xs[row] = s;
   }

@@ -32,6 +32,9 @@ def bf16_rows(rows, K, seed):
     if rows > 2:
         x[1] = 0.0                                   # a zero row: scale 1, codes 0
         x[2] *= np.float32(2.0 ** -30)               # tiny values
+    if rows > 3:
+        # amax near 2^-119: the scale is an fp32 subnormal (the IEEE-division rows)
+        x[3] = rng.normal(0, 1, K).astype(np.float32) * np.float32(2.0 ** -120)
     t = torch.from_numpy(x).to(torch.bfloat16)
     return t.view(torch.int16).numpy().view(np.uint16)
 
@@ -72,6 +75,35 @@ def test_quantize_exact_ties_and_boundaries(F):
     q_ref, s_ref = oracle.quantize_rowwise(bits)
     assert np.all(s == 1.0) and np.array_equal(s, s_ref)
     assert np.array_equal(q, q_ref)
+
+
+def _bf16_bits_of(v):
+    return torch.from_numpy(np.asarray(v, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+def test_quantize_quotients_next_to_code_midpoints(F):
+    """Non-power-of-two scales, each row holding the two bf16 neighbours of every
+    midpoint between two codes times its scale: the code then hangs on the last
+    bits of the fp32 quotient x / s, which must be the correctly rounded one."""
+    rng = np.random.default_rng(91)
+    pos = oracle.e4m3fn_table()[:0x7F]
+    mids = (pos[1:] + pos[:-1]) / 2
+    rows = []
+    for _ in range(64):
+        amax_bits = int(_bf16_bits_of(rng.uniform(1, 2) * 2.0 ** int(rng.integers(-40, 40)))[()])
+        amax = np.array([amax_bits << 16], np.uint32).view(np.float32)[0]
+        s = np.float32(amax) / np.float32(448.0)
+        t = (mids * np.float64(s)).astype(np.float32)
+        lo = (t.view(np.uint32) >> np.uint32(16)).astype(np.uint16)        # bf16 toward zero
+        row = np.concatenate([[amax_bits], lo, lo + np.uint16(1)]).astype(np.uint16)
+        row = np.concatenate([row, np.zeros((-row.size) % 8, np.uint16)])
+        rows += [row, row | np.uint16(0x8000)]
+    bits = np.stack(rows)
+    q, s_gpu = run(F, bits)
+    q_ref, s_ref = oracle.quantize_rowwise(bits)
+    assert np.array_equal(s_gpu.view(np.uint32), s_ref.view(np.uint32))
+    mism = np.argwhere(q != q_ref)
+    assert mism.size == 0, f"{len(mism)} codes differ, first at {mism[:5].tolist()}"
 
 
 def test_quantize_k_zero_gives_unit_scales(F):
