@@ -135,3 +135,27 @@ def k_offsets_exact(XQ, WQ, x_scale, w_scale, k_offsets):
             slab.append(row)
         out.append(slab)
     return out
+
+
+def blockscale_exact(XQ, WQ, x_scale, w_scale, M_sizes, block_k, block_n):
+    """Exact bf16 bits [total_M][N] of the stacked layout with block scales: group
+    g's row r, column n is sum over K blocks kb of (exact block dot product) *
+    x_scale[r, kb] * w_scale[g, n // block_n, kb], rounded once.  Rows of no group
+    are None."""
+    total_M, K = XQ.shape
+    G, N, _ = WQ.shape
+    out = [None] * total_M
+    start = 0
+    for g in range(G):
+        s = max(int(M_sizes[g]), 0)
+        for r in range(start, min(start + s, total_M)):
+            row = []
+            for n in range(N):
+                acc = Fraction(0)
+                for kb in range(K // block_k):
+                    d = dot_exact(XQ[r, kb * block_k:(kb + 1) * block_k], WQ[g, n, kb * block_k:(kb + 1) * block_k])
+                    acc += d * Fraction(float(x_scale[r, kb])) * Fraction(float(w_scale[g, n // block_n, kb]))
+                row.append(bf16_bits_exact(acc))
+            out[r] = row
+        start += s
+    return out

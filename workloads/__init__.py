@@ -373,3 +373,79 @@ def moe_wgrad_k_offsets() -> KOffsets:
     units of 16, one group empty; M=2048, N=7168, Y [8, 2048, 7168]."""
     lengths = 16 * zipf_sizes(7007, 256, 8)
     return make_k_offsets(lengths, 2048, 7168, seed=7007, name="moe_wgrad_k_offsets_G8_M2048_N7168_K4096")
+
+
+# ---------------------------------------------------------------------------
+# Block (groupwise) scales: one scale per (row, K block) of X and per
+# (block_n rows, K block) block of each W[g].
+# ---------------------------------------------------------------------------
+
+@dataclass
+class StackedBlockscale:
+    XQ: np.ndarray        # [total_M, K] uint8
+    WQ: np.ndarray        # [G, N, K] uint8
+    x_scale: np.ndarray   # [total_M, K / block_k] float32
+    w_scale: np.ndarray   # [G, N / block_n, K / block_k] float32
+    M_sizes: np.ndarray   # [G] int64
+    block_k: int = 128
+    block_n: int = 128
+    name: str = ""
+
+    @property
+    def G(self) -> int:
+        return int(self.WQ.shape[0])
+
+    @property
+    def N(self) -> int:
+        return int(self.WQ.shape[1])
+
+    @property
+    def K(self) -> int:
+        return int(self.WQ.shape[2])
+
+    @property
+    def total_M(self) -> int:
+        return int(self.XQ.shape[0])
+
+
+def quantize_blocks(x: np.ndarray, rows_per_block: int, block_k: int) -> tuple[np.ndarray, np.ndarray]:
+    """Blockwise fp8 quantisation of a float32 [R, K] array: one scale per
+    (rows_per_block x block_k) block (amax / 448, 1 for an all-zero block), the
+    same clamp-then-cast as quantize_rows.  Returns (codes [R, K], scales
+    [R / rows_per_block, K / block_k])."""
+    x = np.asarray(x, dtype=np.float32)
+    R, K = x.shape
+    xb = x.reshape(R // rows_per_block, rows_per_block, K // block_k, block_k)
+    amax = np.max(np.abs(xb), axis=(1, 3))
+    s = (amax / np.float32(E4M3_MAX)).astype(np.float32)
+    s[s == 0] = np.float32(1.0)
+    y = np.clip(xb / s[:, None, :, None], -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    return _cast_e4m3fn(y.reshape(R, K)), s
+
+
+def make_stacked_blockscale(M_sizes, N: int, K: int, seed: int, sigma: float = 1.0, block_k: int = 128,
+                            block_n: int = 128, total_M: int | None = None, name: str = "") -> StackedBlockscale:
+    """Stacked inputs with block scales; values drawn as for make_stacked (row chunks
+    per operand), then quantised per block."""
+    M_sizes = np.asarray(M_sizes, dtype=np.int64)
+    G = int(M_sizes.shape[0])
+    if total_M is None:
+        total_M = int(np.clip(M_sizes, 0, None).sum())
+    rx = np.random.default_rng([seed, _TAG_X])
+    x = rx.standard_normal((total_M, K), dtype=np.float32) * np.float32(sigma)
+    XQ, xs = quantize_blocks(x, 1, block_k)
+    del x
+    WQ = np.empty((G, N, K), np.uint8)
+    ws = np.empty((G, N // block_n, K // block_k), np.float32)
+    for g in range(G):
+        rw = np.random.default_rng([seed, _TAG_W, g])
+        w = rw.standard_normal((N, K), dtype=np.float32) * np.float32(sigma)
+        WQ[g], ws[g] = quantize_blocks(w, block_n, block_k)
+    return StackedBlockscale(XQ, WQ, xs, ws, M_sizes, block_k, block_n, name)
+
+
+def moe_gate_up_blockscale() -> StackedBlockscale:
+    """The gate_up shape (G=8, Zipf(1.2) split of 4096 rows, N=4096, K=7168) with
+    128 x 128 weight blocks and 1 x 128 activation blocks."""
+    sizes = zipf_sizes(2002, 4096, 8)
+    return make_stacked_blockscale(sizes, 4096, 7168, seed=8008, name="moe_gate_up_blockscale_G8_M4096_N4096_K7168")
