@@ -34,7 +34,7 @@ MALL_BYTES = 256 * 2 ** 20    # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = ["moe_gate_up", "tiny_stacked", "dense_expert", "dense_expert_preshuffle", "padded_tails",
-             "moe_gate_up_offsets", "dense_expert_batched", "moe_n_offsets", "moe_wgrad_k_offsets"] + \
+             "moe_gate_up_offsets", "dense_expert_batched", "moe_n_offsets", "moe_wgrad_k_offsets", "moe_gate_up_blockscale"] + \
     [f"moe_down_M{m}" for m in (1, 8, 32, 256, 2048, 8192)]
 
 
@@ -64,6 +64,8 @@ def make_workload(name):
         w = wl.dense_expert()
         w.name += "_batched"
         return w, "batched", False
+    if name == "moe_gate_up_blockscale":
+        return wl.moe_gate_up_blockscale(), "blockscale", False
     if name == "moe_n_offsets":
         return wl.moe_n_offsets(), "n_offsets", False
     if name == "moe_wgrad_k_offsets":
@@ -96,6 +98,13 @@ def algorithmic_work(w, layout):
         flop = 2 * M * N * k_valid
         nbytes = M * k_valid + N * k_valid + 4 * G * M + 4 * G * N + 2 * G * M * N + 4 * G
         return flop, nbytes, G * M, G
+    if layout == "blockscale":
+        # stacked rows; one scale per (row, K block) and per (128 x 128) W block
+        sizes = np.clip(w.M_sizes, 0, None)
+        R, g_ne, nkb = int(sizes.sum()), int((sizes > 0).sum()), K // w.block_k
+        flop = 2 * N * K * R
+        nbytes = R * K + g_ne * N * K + 4 * R * nkb + 4 * g_ne * (N // w.block_n) * nkb + 2 * N * R + 8 * G
+        return flop, nbytes, R, g_ne
     if layout in ("stacked", "offsets", "batched"):
         sizes = np.clip(w.M_sizes, 0, None)
         R = int(min(sizes.sum(), w.total_M))
@@ -176,6 +185,8 @@ def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=3):
         elif layout == "batched":
             M = w.total_M // w.G
             oracle.grouped_batched(w.XQ.reshape(w.G, M, w.K), w.WQ, w.x_scale.reshape(w.G, M), w.w_scale)
+        elif layout == "blockscale":
+            oracle.grouped_stacked_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
         elif layout == "n_offsets":
             oracle.grouped_n_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, w.n_offsets)
         elif layout == "k_offsets":
@@ -324,6 +335,8 @@ def main():
         meta = torch.from_numpy(w.k_offsets).to(dev)
     elif layout == "offsets":
         meta = torch.from_numpy(offsets_of(w)).to(dev)
+    elif layout == "blockscale":
+        meta = torch.from_numpy(w.M_sizes).to(dev)
     elif layout == "batched":
         meta = torch.zeros(1, dtype=torch.int64, device=dev)   # the batched layout has no metadata
         Gb, Mb = w.G, w.total_M // w.G
@@ -337,6 +350,7 @@ def main():
     for _ in range(rotate - 1):
         sets.append(tuple(t.clone() for t in sets[0]))
     out_shape = {"stacked": lambda: (w.total_M, w.N), "offsets": lambda: (w.total_M, w.N),
+                 "blockscale": lambda: (w.total_M, w.N),
                  "batched": lambda: (w.G, w.total_M // w.G, w.N), "n_offsets": lambda: (w.M, w.N),
                  "k_offsets": lambda: (w.G, w.M, w.N),
                  "padded": lambda: (w.G, w.expected_m, w.N)}[layout]()
@@ -348,6 +362,12 @@ def main():
             fn = F.f8f8bf16_rowwise_grouped_stacked_preshuffle if pre else F.f8f8bf16_rowwise_grouped_stacked
         else:
             fn = F.f8f8bf16_rowwise_grouped_offsets_preshuffle if pre else F.f8f8bf16_rowwise_grouped_offsets
+
+        def call(i):
+            s = sets[i % rotate]
+            fn(s[0], s[1], s[2], s[3], s[4], out=outs[i % rotate])
+    elif layout == "blockscale":
+        fn = F.f8f8bf16_groupwise_grouped_stacked
 
         def call(i):
             s = sets[i % rotate]

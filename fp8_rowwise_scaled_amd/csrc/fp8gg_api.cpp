@@ -426,6 +426,78 @@ fp8gg_status f8f8bf16_rowwise_grouped_k_offsets(const uint8_t* XQ, const uint8_t
   return run(FP8GG_LAYOUT_K_OFFSETS, 0, XQ, WQ, x_scale, w_scale, k_offsets, Y, G, M, N, K, 0, stream);
 }
 
+fp8gg_status f8f8bf16_groupwise_grouped_stacked(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                                const float* w_scale, const int64_t* M_sizes, uint16_t* Y, int64_t G,
+                                                int64_t total_M, int64_t N, int64_t K, void* stream) {
+  constexpr int64_t B = 128;   // scale block along K and along N
+  fp8gg_status st = check_shape(FP8GG_LAYOUT_STACKED, 0, G, total_M, N, K);
+  if (st != FP8GG_OK) return st;
+  if (K % B != 0 || N % B != 0)
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE,
+                "block scaling needs K and N to be whole numbers of %lld-wide scale blocks (N=%lld K=%lld)",
+                (long long)B, (long long)N, (long long)K);
+  if (total_M == 0 || N == 0) return ok();
+  if (!Y) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y is null");
+  if (!aligned(Y, 16)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y must be 16-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (K == 0) {
+    hipError_t e = fp8gg::launch_zero_fill(Y, total_M * N, s);
+    if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "zero fill launch failed: %s", hipGetErrorString(e));
+    return ok();
+  }
+  if (G == 0) return ok();
+  if (!XQ || !WQ || !x_scale || !w_scale || !M_sizes)
+    return fail(FP8GG_ERR_INVALID_ARGUMENT, "null input pointer");
+  if (!aligned(XQ, 16) || !aligned(WQ, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(M_sizes, 8))
+    return fail(FP8GG_ERR_INVALID_ARGUMENT,
+                "XQ and WQ must be 16-byte, x_scale and w_scale 4-byte and M_sizes 8-byte aligned");
+  const Range out{Y, total_M * N * 2, "Y"};
+  const Range ins[] = {{XQ, total_M * K, "XQ"},
+                       {WQ, G * N * K, "WQ"},
+                       {x_scale, total_M * (K / B) * 4, "x_scale"},
+                       {w_scale, G * (N / B) * (K / B) * 4, "w_scale"},
+                       {M_sizes, G * 8, "M_sizes"}};
+  for (const Range& r : ins)
+    if (overlap(out, r)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y overlaps %s", r.name);
+
+  // 128 x 256 tiles unless groups hold fewer than 64 rows on average; FP8GG_BS_CONFIG
+  // (0 or 1) forces one for tests and tuning.
+  const int64_t per_group = (total_M + G - 1) / G;
+  int cfg = per_group >= 64 ? 0 : 1;
+  const int forced = env_int("FP8GG_BS_CONFIG", -1);
+  if (forced >= 0) {
+    if (forced > 1) return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_BS_CONFIG=%d is not 0 or 1", forced);
+    cfg = forced;
+  }
+  const int64_t BM = fp8gg::kBlockscaleTileM[cfg], BN = fp8gg::kBlockscaleTileN[cfg];
+  fp8gg::GemmArgs a;
+  a.X = XQ;
+  a.W = WQ;
+  a.xs = x_scale;
+  a.ws = w_scale;
+  a.meta = M_sizes;
+  a.offs = nullptr;
+  a.Y = Y;
+  a.G = G;
+  a.M = total_M;
+  a.N = N;
+  a.K = K;
+  const int64_t ub = (total_M + BM - 1) / BM + G - 1;
+  a.m_tiles = ub < total_M ? ub : total_M;
+  a.n_tiles = (N + BN - 1) / BN;
+  a.zeroing = 0;
+  const int64_t grid = a.m_tiles * a.n_tiles;
+  if (grid > 0x7FFFFFFFLL)
+    return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "grid of %lld workgroups exceeds the launch limit", (long long)grid);
+  if (env_int("FP8GG_LOG", 0))
+    std::fprintf(stderr, "[fp8gg] groupwise G=%lld M=%lld N=%lld K=%lld -> cfg=%d tile=%lldx%lld grid=%lld\n",
+                 (long long)G, (long long)total_M, (long long)N, (long long)K, cfg, (long long)BM, (long long)BN,
+                 (long long)grid);
+  hipError_t e = fp8gg::launch_gemm_blockscale(cfg, a, grid, s);
+  if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 fp8gg_status f8f8bf16_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale, int64_t rows, int64_t K,
                                        void* stream) {
   if (rows < 0 || K < 0)

@@ -19,8 +19,8 @@ inline bool is_ragged_layout(int layout) { return layout == kNOffsets || layout 
 struct GemmArgs {
   const uint8_t* X;      // stacked, offsets, k_offsets: [M, K]; padded, batched, n_offsets: [G * M, K]
   const uint8_t* W;      // [G, N, K] (plain) or the pre-shuffled blocks; n_offsets, k_offsets: [N, K]
-  const float* xs;       // one scale per row of X; k_offsets: [G, M]
-  const float* ws;       // [G, N]; n_offsets: [N]
+  const float* xs;       // one scale per row of X; k_offsets: [G, M]; block scales: [rows, K / 128]
+  const float* ws;       // [G, N]; n_offsets: [N]; block scales: [G, N / 128, K / 128]
   const int64_t* meta;   // stacked: M_sizes [G]; padded: zero_start_index_M [G]; else unused
   const int32_t* offs;   // inclusive int32 prefix [G]: rows (offsets), W rows (n_offsets), K (k_offsets)
   uint16_t* Y;           // bf16 bits, one row per row of X, N columns
@@ -74,6 +74,10 @@ hipError_t launch_gemm_persistent(int layout, int config_id, bool k_tail, const 
                                   int tail_mode, hipStream_t stream);
 hipError_t launch_gemm_ragged(int layout, int config_id, bool k_tail, const GemmArgs& args, int64_t grid,
                               hipStream_t stream);
+// Block-scaled stacked GEMM: config 0 tiles 128 x 256, config 1 tiles 32 x 128.
+constexpr int kBlockscaleTileM[2] = {128, 32};
+constexpr int kBlockscaleTileN[2] = {256, 128};
+hipError_t launch_gemm_blockscale(int config, const GemmArgs& args, int64_t grid, hipStream_t stream);
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t stream);
 hipError_t launch_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale, int64_t rows, int64_t K,
                                    hipStream_t stream);

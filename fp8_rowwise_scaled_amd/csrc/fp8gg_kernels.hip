@@ -1078,6 +1078,132 @@ gg_persistent_kernel(GemmArgs a, int tail_mode) {
 }
 
 // ---------------------------------------------------------------------------
+// Block (groupwise) scaling, stacked layout
+// ---------------------------------------------------------------------------
+//
+// One scale per (128 x 128) block of W[g] and per (row, 128-byte K block) of X
+// ([MSLK-471], first commit of the list: block scaling scales each block's partial
+// sum inside the K loop).  The K stage is one scale block (BK = 128): the stage's
+// MFMAs accumulate into a zeroed partial tile, which is then added to the running
+// accumulator as acc += partial * (x_scale[m, kb] * w_scale[g, n / 128, kb]).
+// The stage's scales travel with its operand copies: x_scale of the tile's rows
+// and w_scale of its column blocks are copied into an LDS slot of the same ring
+// index (one 4-byte copy per lane, one per wave, the waves past the block into a
+// dummy word), so the stage's wait and barrier cover them too.  The epilogue only
+// rounds and stores.  K and N are whole numbers of blocks (checked on the host).
+template <int BM, int BN, int WM, int WN, int STAGES>
+__global__ void __launch_bounds__(WM * WN * 64)
+gg_blockscale_kernel(GemmArgs a) {
+  constexpr int BK = 128;
+  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, false, false> E;
+  constexpr int SCX = BM > 64 ? BM : 64;   // x_scale floats per slot (slack past BM)
+  constexpr int SC = SCX + 64;             // then the W block scales (BN / 128 used)
+  constexpr int L = E::LOADS_PER_STAGE + 1;
+  static_assert(E::EVEN_LOADS, "the stage wait counts assume equal copies per wave");
+  static_assert(SCX / 64 + 1 <= WM * WN, "one scale copy per wave");
+  static_assert(BN % 128 == 0 && E::TN % 16 == 0, "a lane's 16 columns lie in one block");
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) float sc[STAGES][SC];
+  __shared__ __attribute__((aligned(16))) float sc_dummy[64];
+
+  const int64_t bid = blockIdx.x;
+  const int64_t n_tile = bid % a.n_tiles;
+  Tile t;
+  if (!resolve_packed<kStacked, BM>(a, bid / a.n_tiles, t)) return;
+  const int64_t n0 = n_tile * BN;
+  E e;
+  e.init(smem);
+  e.setup(a, t, n0);
+  const int nkb = (int)(a.K / BK);
+  const int64_t nbn = a.N / 128;
+
+  // This thread's scale source at K block 0 (one float further per block).
+  const float* ssrc;
+  int sdst;                                // 0..: offset in the slot; -1: the dummy word
+  if (e.wave < SCX / 64) {
+    int r = e.wave * 64 + e.lane;
+    r = r < BM ? r : BM - 1;
+    int64_t row = t.row_base + r;
+    row = row < t.row_end ? row : t.row_end - 1;   // rows past the group: any valid row
+    ssrc = a.xs + row * nkb;
+    sdst = e.wave * 64;
+  } else if (e.wave == SCX / 64) {
+    int64_t j = n0 / 128 + (e.lane < BN / 128 ? e.lane : BN / 128 - 1);
+    j = j < nbn ? j : nbn - 1;                     // blocks past N: never used
+    ssrc = a.ws + (t.g * nbn + j) * nkb;
+    sdst = SCX;
+  } else {
+    ssrc = a.xs + t.row_base * nkb;
+    sdst = -1;
+  }
+  auto issue = [&](int kt) {
+    const int slot = kt % STAGES;
+    e.issue(kt, slot, nkb, a.K);
+    copy4_to_lds(ssrc + kt, lds_addr(sdst >= 0 ? &sc[slot][sdst] : sc_dummy));
+  };
+
+  typename E::Acc acc;
+#pragma unroll
+  for (int i = 0; i < E::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < E::FN; ++j) acc[i][j] = v16f{0};
+
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s)
+    if (s < nkb) issue(s);
+  for (int kt = 0; kt < nkb; ++kt) {
+    // stage kt (operands and scales) has landed once only the younger stages'
+    // copies are outstanding; the barrier publishes it and frees the slot reused below
+    if (nkb - 1 - kt >= STAGES - 2) wait_vmcnt_le((STAGES - 2) * L);
+    else wait_vmcnt_le(0);
+    block_barrier();
+    if (kt + STAGES - 1 < nkb) issue(kt + STAGES - 1);
+    const int slot = kt % STAGES;
+    v8i xf[E::KS][E::FM], wf[E::KS][E::FN];
+    e.read_frags(slot, xf, wf);
+    typename E::Acc part;
+#pragma unroll
+    for (int fm = 0; fm < E::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < E::FN; ++fn) {
+        part[fm][fn] = mfma_32x32x64_fp8(wf[0][fn], xf[0][fm], v16f{0});
+#pragma unroll
+        for (int ks = 1; ks < E::KS; ++ks) part[fm][fn] = mfma_32x32x64_fp8(wf[ks][fn], xf[ks][fm], part[fm][fn]);
+      }
+    float xsv[E::FM], wsv[E::FN];
+#pragma unroll
+    for (int fm = 0; fm < E::FM; ++fm) xsv[fm] = sc[slot][e.wm * E::TM + 32 * fm + e.r32];
+#pragma unroll
+    for (int fn = 0; fn < E::FN; ++fn) wsv[fn] = sc[slot][SCX + e.col_of(fn) / 128];
+#pragma unroll
+    for (int fm = 0; fm < E::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < E::FN; ++fn) {
+        const float f = xsv[fm] * wsv[fn];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[fm][fn][i] = __builtin_fmaf(part[fm][fn][i], f, acc[fm][fn][i]);
+      }
+  }
+
+  typename E::Packed pk;
+#pragma unroll
+  for (int fm = 0; fm < E::FM; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < E::FN; ++fn)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        uint32_t q[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = 8 * half + 2 * j;
+          q[j] = pack_bf16x2(acc[fm][fn][i], acc[fm][fn][i + 1]);
+        }
+        pk[fm][fn][half] = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
+      }
+  e.store(a, t, n0, pk);
+}
+
+// ---------------------------------------------------------------------------
 // Pre-shuffled W
 // ---------------------------------------------------------------------------
 //
@@ -1479,6 +1605,20 @@ hipError_t launch_gemm_ragged(int layout, int config_id, bool k_tail, const Gemm
   switch (layout) {
     case kNOffsets: return launch_ragged_layout<kNOffsets>(config_id, k_tail, a, grid, s);
     case kKOffsets: return launch_ragged_layout<kKOffsets>(config_id, k_tail, a, grid, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Block-scaled configurations: 0 = 128 x 256 tiles (2 x 4 waves, 3 stages),
+// 1 = 32 x 128 tiles (1 x 4 waves, 3 stages) for few rows per group.
+hipError_t launch_gemm_blockscale(int config, const GemmArgs& a, int64_t grid, hipStream_t s) {
+  switch (config) {
+    case 0:
+      hipLaunchKernelGGL((gg_blockscale_kernel<128, 256, 2, 4, 3>), dim3((uint32_t)grid), dim3(512), 0, s, a);
+      return hipGetLastError();
+    case 1:
+      hipLaunchKernelGGL((gg_blockscale_kernel<32, 128, 1, 4, 3>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+      return hipGetLastError();
     default: return hipErrorInvalidValue;
   }
 }

@@ -243,6 +243,34 @@ def f8f8bf16_rowwise_grouped_mm_preshuffle(XQ, WQs, x_scale, w_scale, offs=None,
                      "(the groups would split the shuffled blocks)")
 
 
+def f8f8bf16_groupwise_grouped_stacked(XQ, WQ, x_scale, w_scale, M_sizes, out=None):
+    """Y [total_M, N] bf16 for the stacked layout with block scales: x_scale
+    [total_M, K/128], w_scale [G, N/128, K/128] (see include/fp8gg.h)."""
+    XQ = _bytes(XQ, "XQ")
+    WQ = _bytes(WQ, "WQ")
+    if XQ.dim() != 2 or WQ.dim() != 3:
+        raise ValueError("XQ must be [total_M, K] and WQ [G, N, K]")
+    total_M, K = XQ.shape
+    G, N, K2 = WQ.shape
+    if K2 != K:
+        raise ValueError(f"K mismatch: XQ has {K}, WQ has {K2}")
+    if K % 128 or N % 128:
+        raise ValueError(f"block scaling needs K and N to be multiples of 128 (N={N}, K={K})")
+    _check(XQ, "XQ", torch.uint8, (total_M, K))
+    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _check(x_scale, "x_scale", torch.float32, (total_M, K // 128))
+    _check(w_scale, "w_scale", torch.float32, (G, N // 128, K // 128))
+    _check(M_sizes, "M_sizes", torch.int64, (G,))
+    if out is None:
+        out = torch.empty((total_M, N), dtype=torch.bfloat16, device=XQ.device)
+    _check(out, "out", torch.bfloat16, (total_M, N))
+    st = _lib.load().f8f8bf16_groupwise_grouped_stacked(XQ.data_ptr(), WQ.data_ptr(), x_scale.data_ptr(),
+                                                        w_scale.data_ptr(), M_sizes.data_ptr(), out.data_ptr(),
+                                                        G, total_M, N, K, _stream(XQ.device))
+    _lib.check(st, "f8f8bf16_groupwise_grouped_stacked")
+    return out
+
+
 def f8f8bf16_shuffle_b(WQ, out=None):
     """Rearranges WQ [G, N, K] into the pre-shuffled layout (same shape and bytes)."""
     WQ = _bytes(WQ, "WQ")

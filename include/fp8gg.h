@@ -225,6 +225,30 @@ fp8gg_status f8f8bf16_rowwise_grouped_k_offsets(
     int64_t G, int64_t M, int64_t N, int64_t K, void* stream);
 
 /*
+ * Block (groupwise) scaling, stacked layout (MSLK #471, first commit of the list:
+ * block scaling carries one scale per (scale_block_k x scale_block_n) block of B
+ * and scales each block's partial sum inside the K loop; the A-side granularity,
+ * one scale per row and K block, is this library's reading).  Blocks are 128 x 128:
+ *
+ *   XQ        [total_M, K]             fp8 e4m3fn
+ *   WQ        [G, N, K]                fp8 e4m3fn
+ *   x_scale   [total_M, K / 128]       fp32, 4-byte aligned
+ *   w_scale   [G, N / 128, K / 128]    fp32, 4-byte aligned
+ *   M_sizes   [G]                      int64 row counts (as the stacked op)
+ *   Y         [total_M, N]             bf16:
+ *       Y[m, n] = sum_kb (sum_{k in block kb} XQ[m, k] WQ[g, n, k]) x_scale[m, kb] w_scale[g, n / 128, kb]
+ *
+ * Shape rule: K % 128 == 0 and N % 128 == 0 (whole scale blocks; the pages require
+ * the block bound under block scaling), else FP8GG_ERR_UNSUPPORTED_SHAPE.  Each
+ * block's products accumulate in fp32 and are scaled in fp32 before they join the
+ * running sum.  Row classes, clamping and K == 0 as for the stacked op.
+ */
+fp8gg_status f8f8bf16_groupwise_grouped_stacked(
+    const uint8_t* XQ, const uint8_t* WQ, const float* x_scale, const float* w_scale,
+    const int64_t* M_sizes, uint16_t* Y,
+    int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
+
+/*
  * Rearranges WQ [G, N, K] into the pre-shuffled order WQs (same size, must not
  * overlap WQ).  Byte layout: for group g, N-block nb (FP8GG_SHUFFLE_N rows) and
  * K-block kb (FP8GG_SHUFFLE_K bytes), the 2048-byte block at

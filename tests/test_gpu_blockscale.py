@@ -1,0 +1,110 @@
+"""GPU parity for the block-scaled (groupwise) stacked GEMM.
+
+Both kernel configurations are forced in turn on edge shapes (empty groups,
+groups of 1 row, tile - 1 / tile + 1 rows, rows of no group, one and several
+N and K blocks) and compared with the block-scaled oracle element by element;
+the full-size workload is checked on sampled rows; shapes that are not whole
+scale blocks are refused on the host.
+"""
+import os
+from contextlib import contextmanager
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import fp8_rowwise_scaled_amd as F
+    F.load()
+    return F
+
+
+@contextmanager
+def forced(cfg):
+    old = os.environ.get("FP8GG_BS_CONFIG")
+    if cfg is None:
+        os.environ.pop("FP8GG_BS_CONFIG", None)
+    else:
+        os.environ["FP8GG_BS_CONFIG"] = str(cfg)
+    try:
+        yield
+    finally:
+        if old is None:
+            os.environ.pop("FP8GG_BS_CONFIG", None)
+        else:
+            os.environ["FP8GG_BS_CONFIG"] = old
+
+
+def run(F, w, total_M):
+    whole, y = P.guarded_output((total_M, w.N))
+    F.f8f8bf16_groupwise_grouped_stacked(P.dev(w.XQ), P.dev(w.WQ), P.dev(w.x_scale), P.dev(w.w_scale),
+                                         P.dev(w.M_sizes), out=y)
+    torch.cuda.synchronize()
+    P.check_guards(whole)
+    return P.bits_of(y)
+
+
+# (sizes, N, K, total_M): empty and 1-row groups, 127/129/257 rows, trailing rows of no group
+CASES = [
+    ([0, 3, 130, 257], 384, 640, None),
+    ([1, 0, 127], 128, 128, 140),
+    ([33, 31, 129], 256, 1152, None),
+]
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+@pytest.mark.parametrize("case", range(len(CASES)))
+def test_blockscale_matches_oracle(F, cfg, case):
+    sizes, N, K, total_M = CASES[case]
+    w = wl.make_stacked_blockscale(sizes, N, K, seed=900 + case, total_M=total_M)
+    print(f"case blockscale cfg={cfg} sizes={sizes} N={N} K={K}", flush=True)
+    with forced(cfg):
+        got = run(F, w, w.total_M)
+    res = oracle.grouped_stacked_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
+    P.assert_rows_match(got, res, label=f"blockscale cfg {cfg} case {case}")
+
+
+def test_blockscale_refuses_partial_blocks_and_zero_fills_k_zero(F):
+    w = wl.make_stacked_blockscale([4], 128, 128, seed=950)
+    with pytest.raises(ValueError, match="multiples of 128"):
+        F.f8f8bf16_groupwise_grouped_stacked(P.dev(w.XQ[:, :64].copy()), P.dev(w.WQ[:, :, :64].copy()),
+                                             P.dev(w.x_scale), P.dev(w.w_scale), P.dev(w.M_sizes))
+    from fp8_rowwise_scaled_amd import _lib
+    a = 0x10000000
+    st = _lib.load().f8f8bf16_groupwise_grouped_stacked(a, a, a, a, a, a + 0x1000000, 1, 4, 136, 128, None)
+    assert st == _lib.ERR_UNSUPPORTED_SHAPE
+    whole, y = P.guarded_output((3, 128))
+    F.f8f8bf16_groupwise_grouped_stacked(torch.empty((3, 0), dtype=torch.uint8, device="cuda"),
+                                         torch.empty((1, 128, 0), dtype=torch.uint8, device="cuda"),
+                                         torch.empty((3, 0), dtype=torch.float32, device="cuda"),
+                                         torch.empty((1, 1, 0), dtype=torch.float32, device="cuda"),
+                                         P.dev(np.array([3], np.int64)), out=y)
+    torch.cuda.synchronize()
+    P.check_guards(whole)
+    assert np.all(P.bits_of(y) == 0)
+
+
+def test_full_size_blockscale_workload(F):
+    """The block-scaled gate_up workload at full size (the configuration the bench
+    times), checked on every column of 48 sampled rows."""
+    w = wl.moe_gate_up_blockscale()
+    with forced(None):
+        got = run(F, w, w.total_M)
+    rows = np.sort(np.random.default_rng(951).choice(w.total_M, 48, replace=False))
+    owner = oracle.stacked_row_groups(w.M_sizes, w.total_M)[rows]
+    for g in np.unique(owner):
+        sel = rows[owner == g]
+        sizes = np.zeros(w.G, np.int64)
+        sizes[g] = sel.size
+        res = oracle.grouped_stacked_blockscale(w.XQ[sel], w.WQ, w.x_scale[sel], w.w_scale, sizes)
+        P.assert_rows_match(got[sel], res, rms=P.rms_of(res.bits), label=f"moe_gate_up_blockscale group {g}")
