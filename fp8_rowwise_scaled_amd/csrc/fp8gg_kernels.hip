@@ -799,6 +799,65 @@ struct LdsTile {
     }
   }
 
+  // The same stores through LDS, for kernels whose LDS ring is idle after the K
+  // loop (one tile per workgroup).  The packed tile is written to LDS in its MFMA
+  // layout (row r at a stride of BN bf16, 16-byte chunk c stored at c ^ (r mod 16),
+  // which keeps the column-wise writes and the row-wise reads free of bank
+  // conflicts) and read back row by row, so that each global store instruction
+  // covers whole rows of the tile (consecutive lanes, consecutive 16 bytes) instead
+  // of 16-byte pieces of 32 rows: HBM sees whole cache lines.  Row and column masks
+  // as in store().
+  static constexpr int CHUNKS_PER_ROW = BN / 8;
+  static constexpr int SHUF_MASK = (CHUNKS_PER_ROW < 16 ? CHUNKS_PER_ROW : 16) - 1;
+  template <typename TT>
+  __device__ __forceinline__ void store_shuffled(const GemmArgs& a, const TT& t, int64_t n0,
+                                                 const Packed& pk) const {
+    static_assert(BM * BN * 2 <= SMEM_BYTES, "the output tile fits the LDS ring");
+    block_barrier();   // every wave is done reading the ring's last stage
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      const int r = wm * TM + 32 * fm + r32;
+#pragma unroll
+      for (int s = 0; s < 2 * FN; ++s) {
+        const int chunk = (col_of(s >> 1) + 8 * (s & 1)) / 8;
+        *(v4i*)(smem + (r * CHUNKS_PER_ROW + (chunk ^ (r & SHUF_MASK))) * 16) = pk[fm][s >> 1][s & 1];
+      }
+    }
+    block_barrier();
+    const int64_t N = a.N;
+    const int64_t cend = tile_col_end(a, t);
+#pragma unroll 4
+    for (int q = tid; q < BM * CHUNKS_PER_ROW; q += NT) {
+      const int r = q / CHUNKS_PER_ROW;
+      const int chunk = q % CHUNKS_PER_ROW;
+      const int64_t m = t.row_base + r;
+      const int64_t c = n0 + 8 * chunk;
+      if (m >= t.zero_end) continue;
+      v4i v = {0, 0, 0, 0};
+      if (m < t.row_end) v = *(const v4i*)(smem + (r * CHUNKS_PER_ROW + (chunk ^ (r & SHUF_MASK))) * 16);
+      uint16_t* yrow = a.Y + (m - tile_y_delta(t)) * N;
+      if constexpr (IsRagged<TT>::value) {
+        if ((c & 7) == 0 && c + 8 <= cend) {
+          *(v4i*)(yrow + c) = v;
+        } else if (c < cend) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            if (c + e < cend) yrow[c + e] = (uint16_t)((uint32_t)v[e >> 1] >> (16 * (e & 1)));
+        }
+      } else {
+        if (c < cend) *(v4i*)(yrow + c) = v;
+      }
+    }
+  }
+
+  template <typename TT>
+  __device__ __forceinline__ void epilogue_shuffled(const GemmArgs& a, const TT& t, int64_t n0,
+                                                    const Acc& acc) const {
+    Packed pk;
+    scale(a, t, n0, acc, pk);
+    store_shuffled(a, t, n0, pk);
+  }
+
   template <typename TT>
   __device__ __forceinline__ void epilogue(const GemmArgs& a, const TT& t, int64_t n0, const Acc& acc) const {
     Packed pk;
@@ -842,7 +901,7 @@ gg_lds_kernel(GemmArgs a) {
     for (int j = 0; j < E::FN; ++j) acc[i][j] = v16f{0};
   const int nk = (int)((a.K + BK - 1) / BK);
   e.run(0, nk, nk, a.K, acc);
-  e.epilogue(a, t, n0, acc);
+  e.epilogue_shuffled(a, t, n0, acc);
 }
 
 // Ragged layouts (n_offsets, k_offsets): one tile per workgroup, both operands
@@ -870,7 +929,7 @@ gg_ragged_kernel(GemmArgs a) {
     for (int j = 0; j < E::FN; ++j) acc[i][j] = v16f{0};
   const int nk = (int)((t.klen + BK - 1) / BK);
   e.run(0, nk, nk, t.klen, acc);
-  e.epilogue(a, t, t.n0, acc);
+  e.epilogue_shuffled(a, t, t.n0, acc);
 }
 
 // Number of M tiles over all groups of a packed layout, with the resolver's clamping.
@@ -1200,7 +1259,7 @@ gg_blockscale_kernel(GemmArgs a) {
         }
         pk[fm][fn][half] = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
       }
-  e.store(a, t, n0, pk);
+  e.store_shuffled(a, t, n0, pk);
 }
 
 // ---------------------------------------------------------------------------
