@@ -1,0 +1,74 @@
+"""Graph capture of the entry points beyond the persistent kernel.
+
+Every call only enqueues kernels on the caller's stream (no allocation, copy,
+memset or synchronisation), so a sequence of calls can be captured into one HIP
+graph.  The graph here holds an n_offsets, a k_offsets, a block-scaled and a
+quantiser call; it is replayed several times with eager work on other buffers
+in between, and every replay must reproduce the eager results bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def F():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    import fp8_rowwise_scaled_amd as F
+    F.load()
+    return F
+
+
+def test_new_entry_points_under_graph_replay(F):
+    n = wl.make_n_offsets([40, 0, 200, 17], 70, 336, seed=1401, total_N=264)
+    k = wl.make_k_offsets([48, 0, 400, 16], 45, 136, seed=1402)
+    b = wl.make_stacked_blockscale([3, 0, 130], 256, 384, seed=1403)
+    rng = np.random.default_rng(1404)
+    xb = torch.from_numpy(rng.normal(0, 1, (37, 1040)).astype(np.float32)).to(torch.bfloat16).cuda()
+
+    nin = [P.dev(a) for a in (n.XQ, n.WQ, n.x_scale, n.w_scale, n.n_offsets)]
+    kin = [P.dev(a) for a in (k.XQ, k.WQ, k.x_scale, k.w_scale, k.k_offsets)]
+    bin_ = [P.dev(a) for a in (b.XQ, b.WQ, b.x_scale, b.w_scale, b.M_sizes)]
+    yn = torch.empty((n.M, n.N), dtype=torch.bfloat16, device="cuda")
+    yk = torch.empty((k.G, k.M, k.N), dtype=torch.bfloat16, device="cuda")
+    yb = torch.empty((b.total_M, b.N), dtype=torch.bfloat16, device="cuda")
+    q = torch.empty((37, 1040), dtype=torch.uint8, device="cuda")
+    s = torch.empty((37,), dtype=torch.float32, device="cuda")
+    outs = (yn, yk, yb, q, s)
+
+    def calls():
+        F.f8f8bf16_rowwise_grouped_n_offsets(*nin, out=yn)
+        F.f8f8bf16_rowwise_grouped_k_offsets(*kin, out=yk)
+        F.f8f8bf16_groupwise_grouped_stacked(*bin_, out=yb)
+        F.f8f8bf16_quantize_rowwise(xb, q, s)
+
+    calls()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        calls()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        calls()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for rep in range(3):
+        for o in outs:
+            o.zero_()                             # eager work between replays
+        scratch.add_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, o, e in zip(("n_offsets", "k_offsets", "blockscale", "codes", "scales"), outs, eager):
+            assert torch.equal(o.view(torch.uint8), e.view(torch.uint8)), \
+                f"replay {rep}: {name} differs from the eager result"

@@ -214,3 +214,11 @@ def test_quantize_refuses_bad_shapes_and_overlaps_on_the_host():
     assert lib.f8f8bf16_quantize_rowwise(base, base + (1 << 20), None, 4, 64, None) == _lib.ERR_INVALID_ARGUMENT
     # nothing to do: no launch, success
     assert lib.f8f8bf16_quantize_rowwise(None, None, None, 0, 64, None) == _lib.OK
+
+
+def test_missing_library_raises(monkeypatch, tmp_path):
+    """The product path has no fallback: without libfp8gg.so, loading raises."""
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libfp8gg.so"))
+    with pytest.raises(RuntimeError, match="no fallback"):
+        _lib.load()
