@@ -219,6 +219,8 @@ def f8f8bf16_rowwise_grouped_mm(XQ, WQ, x_scale, w_scale, offs=None, out=None):
     2D-3D -> offsets (groups along M), 3D-3D -> batched (offs unused),
     3D-2D -> n_offsets (groups along N), 2D-2D -> k_offsets (groups along K)."""
     ra, rb = XQ.dim(), WQ.dim()
+    if offs is None and (ra, rb) != (3, 3):
+        raise ValueError(f"operand ranks {ra}D-{rb}D group along an axis given by offs, which is missing")
     if (ra, rb) == (2, 3):
         return f8f8bf16_rowwise_grouped_offsets(XQ, WQ, x_scale, w_scale, offs, out=out)
     if (ra, rb) == (3, 3):
@@ -235,6 +237,8 @@ def f8f8bf16_rowwise_grouped_mm_preshuffle(XQ, WQs, x_scale, w_scale, offs=None,
     owns a whole [N, K] (2D-3D, 3D-3D); the others raise rather than read shuffled
     weights as plain ones."""
     ra, rb = XQ.dim(), WQs.dim()
+    if offs is None and (ra, rb) == (2, 3):
+        raise ValueError("operand ranks 2D-3D group along M by offs, which is missing")
     if (ra, rb) == (2, 3):
         return f8f8bf16_rowwise_grouped_offsets_preshuffle(XQ, WQs, x_scale, w_scale, offs, out=out)
     if (ra, rb) == (3, 3):

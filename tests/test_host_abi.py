@@ -222,3 +222,14 @@ def test_missing_library_raises(monkeypatch, tmp_path):
     monkeypatch.setattr(_lib, "LIB_PATH", str(tmp_path / "libfp8gg.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         _lib.load()
+
+
+def test_grouped_mm_needs_offsets_where_the_ranks_group_an_axis():
+    import torch
+    x2, w3 = torch.zeros((4, 32), dtype=torch.uint8), torch.zeros((2, 8, 32), dtype=torch.uint8)
+    x3, w2 = torch.zeros((2, 4, 32), dtype=torch.uint8), torch.zeros((8, 32), dtype=torch.uint8)
+    for a, b in ((x2, w3), (x3, w2), (x2, w2)):
+        with pytest.raises(ValueError, match="offs"):
+            F.f8f8bf16_rowwise_grouped_mm(a, b, None, None, None)
+    with pytest.raises(ValueError, match="no grouped layout"):
+        F.f8f8bf16_rowwise_grouped_mm(torch.zeros(4, dtype=torch.uint8), w3, None, None, torch.zeros(2))
