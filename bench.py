@@ -166,8 +166,9 @@ def measured_traffic(workload, src_hash):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=3):
-    """The oracle as it stands, on the full workload, on this host's cores."""
+def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=50):
+    """The oracle as it stands, on the full workload, on this host's cores: whole
+    calls repeated until about min_seconds of CPU work (at most max_runs calls)."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -196,7 +197,8 @@ def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=3):
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     return {"value": round(flop / med / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the full workload, {len(times)} run(s), median {med:.3f} s per call "
+            "sample": f"the full workload, {len(times)} whole call(s) over {sum(times):.1f} s, "
+                      f"median {med:.3f} s per call "
                       "(e4m3fn table decode, fp64 matmul per group, fp64 scales, bf16 RNE)"}
 
 
