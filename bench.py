@@ -34,7 +34,8 @@ MALL_BYTES = 256 * 2 ** 20    # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = ["moe_gate_up", "tiny_stacked", "dense_expert", "dense_expert_preshuffle", "padded_tails",
-             "moe_gate_up_offsets", "dense_expert_batched", "moe_n_offsets", "moe_wgrad_k_offsets", "moe_gate_up_blockscale"] + \
+             "moe_gate_up_offsets", "dense_expert_batched", "moe_n_offsets", "moe_wgrad_k_offsets", "moe_gate_up_blockscale",
+             "moe_gate_up_blockscale_preshuffle"] + \
     [f"moe_down_M{m}" for m in (1, 8, 32, 256, 2048, 8192)]
 
 
@@ -66,6 +67,8 @@ def make_workload(name):
         return w, "batched", False
     if name == "moe_gate_up_blockscale":
         return wl.moe_gate_up_blockscale(), "blockscale", False
+    if name == "moe_gate_up_blockscale_preshuffle":
+        return wl.moe_gate_up_blockscale(), "blockscale", True
     if name == "moe_n_offsets":
         return wl.moe_n_offsets(), "n_offsets", False
     if name == "moe_wgrad_k_offsets":
@@ -369,7 +372,7 @@ def main():
             s = sets[i % rotate]
             fn(s[0], s[1], s[2], s[3], s[4], out=outs[i % rotate])
     elif layout == "blockscale":
-        fn = F.f8f8bf16_groupwise_grouped_stacked
+        fn = F.f8f8bf16_groupwise_grouped_stacked_preshuffle if pre else F.f8f8bf16_groupwise_grouped_stacked
 
         def call(i):
             s = sets[i % rotate]

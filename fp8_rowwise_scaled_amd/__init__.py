@@ -18,6 +18,7 @@ from ._lib import (  # noqa: F401
 )
 from .ops import (  # noqa: F401
     f8f8bf16_groupwise_grouped_stacked,
+    f8f8bf16_groupwise_grouped_stacked_preshuffle,
     f8f8bf16_rowwise_grouped_batched,
     f8f8bf16_rowwise_grouped_batched_preshuffle,
     f8f8bf16_rowwise_grouped_dynamic,

@@ -426,11 +426,11 @@ fp8gg_status f8f8bf16_rowwise_grouped_k_offsets(const uint8_t* XQ, const uint8_t
   return run(FP8GG_LAYOUT_K_OFFSETS, 0, XQ, WQ, x_scale, w_scale, k_offsets, Y, G, M, N, K, 0, stream);
 }
 
-fp8gg_status f8f8bf16_groupwise_grouped_stacked(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
-                                                const float* w_scale, const int64_t* M_sizes, uint16_t* Y, int64_t G,
-                                                int64_t total_M, int64_t N, int64_t K, void* stream) {
-  constexpr int64_t B = 128;   // scale block along K and along N
-  fp8gg_status st = check_shape(FP8GG_LAYOUT_STACKED, 0, G, total_M, N, K);
+static fp8gg_status groupwise_stacked(int preshuffled, const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                      const float* w_scale, const int64_t* M_sizes, uint16_t* Y, int64_t G,
+                                      int64_t total_M, int64_t N, int64_t K, void* stream) {
+  constexpr int64_t B = 128;   // scale block along K and along N (whole pre-shuffle blocks too)
+  fp8gg_status st = check_shape(FP8GG_LAYOUT_STACKED, preshuffled, G, total_M, N, K);
   if (st != FP8GG_OK) return st;
   if (K % B != 0 || N % B != 0)
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE,
@@ -493,9 +493,22 @@ fp8gg_status f8f8bf16_groupwise_grouped_stacked(const uint8_t* XQ, const uint8_t
     std::fprintf(stderr, "[fp8gg] groupwise G=%lld M=%lld N=%lld K=%lld -> cfg=%d tile=%lldx%lld grid=%lld\n",
                  (long long)G, (long long)total_M, (long long)N, (long long)K, cfg, (long long)BM, (long long)BN,
                  (long long)grid);
-  hipError_t e = fp8gg::launch_gemm_blockscale(cfg, a, grid, s);
+  hipError_t e = fp8gg::launch_gemm_blockscale(cfg, preshuffled != 0, a, grid, s);
   if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+fp8gg_status f8f8bf16_groupwise_grouped_stacked(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                                const float* w_scale, const int64_t* M_sizes, uint16_t* Y, int64_t G,
+                                                int64_t total_M, int64_t N, int64_t K, void* stream) {
+  return groupwise_stacked(0, XQ, WQ, x_scale, w_scale, M_sizes, Y, G, total_M, N, K, stream);
+}
+
+fp8gg_status f8f8bf16_groupwise_grouped_stacked_preshuffle(const uint8_t* XQ, const uint8_t* WQs, const float* x_scale,
+                                                           const float* w_scale, const int64_t* M_sizes, uint16_t* Y,
+                                                           int64_t G, int64_t total_M, int64_t N, int64_t K,
+                                                           void* stream) {
+  return groupwise_stacked(1, XQ, WQs, x_scale, w_scale, M_sizes, Y, G, total_M, N, K, stream);
 }
 
 fp8gg_status f8f8bf16_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale, int64_t rows, int64_t K,

@@ -77,7 +77,8 @@ hipError_t launch_gemm_ragged(int layout, int config_id, bool k_tail, const Gemm
 // Block-scaled stacked GEMM: config 0 tiles 128 x 256, config 1 tiles 32 x 128.
 constexpr int kBlockscaleTileM[2] = {128, 32};
 constexpr int kBlockscaleTileN[2] = {256, 128};
-hipError_t launch_gemm_blockscale(int config, const GemmArgs& args, int64_t grid, hipStream_t stream);
+hipError_t launch_gemm_blockscale(int config, bool preshuffled, const GemmArgs& args, int64_t grid,
+                                  hipStream_t stream);
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t stream);
 hipError_t launch_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale, int64_t rows, int64_t K,
                                    hipStream_t stream);

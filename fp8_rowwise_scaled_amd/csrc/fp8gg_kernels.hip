@@ -1150,11 +1150,13 @@ gg_persistent_kernel(GemmArgs a, int tail_mode) {
 // index (one 4-byte copy per lane, one per wave, the waves past the block into a
 // dummy word), so the stage's wait and barrier cover them too.  The epilogue only
 // rounds and stores.  K and N are whole numbers of blocks (checked on the host).
-template <int BM, int BN, int WM, int WN, int STAGES>
+// PRE: W comes pre-shuffled (f8f8bf16_shuffle_b) and is read through the same tile
+// as in the rowwise kernels; a lane's 16 columns still lie in one 128-column block.
+template <int BM, int BN, int WM, int WN, int STAGES, bool PRE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gg_blockscale_kernel(GemmArgs a) {
   constexpr int BK = 128;
-  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, false, false> E;
+  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, false, PRE> E;
   constexpr int SCX = BM > 64 ? BM : 64;   // x_scale floats per slot (slack past BM)
   constexpr int SC = SCX + 64;             // then the W block scales (BN / 128 used)
   constexpr int L = E::LOADS_PER_STAGE + 1;
@@ -1670,16 +1672,21 @@ hipError_t launch_gemm_ragged(int layout, int config_id, bool k_tail, const Gemm
 
 // Block-scaled configurations: 0 = 128 x 256 tiles (2 x 4 waves, 3 stages),
 // 1 = 32 x 128 tiles (1 x 4 waves, 3 stages) for few rows per group.
-hipError_t launch_gemm_blockscale(int config, const GemmArgs& a, int64_t grid, hipStream_t s) {
+template <bool PRE>
+static hipError_t launch_blockscale(int config, const GemmArgs& a, int64_t grid, hipStream_t s) {
   switch (config) {
     case 0:
-      hipLaunchKernelGGL((gg_blockscale_kernel<128, 256, 2, 4, 3>), dim3((uint32_t)grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gg_blockscale_kernel<128, 256, 2, 4, 3, PRE>), dim3((uint32_t)grid), dim3(512), 0, s, a);
       return hipGetLastError();
     case 1:
-      hipLaunchKernelGGL((gg_blockscale_kernel<32, 128, 1, 4, 3>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gg_blockscale_kernel<32, 128, 1, 4, 3, PRE>), dim3((uint32_t)grid), dim3(256), 0, s, a);
       return hipGetLastError();
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gemm_blockscale(int config, bool preshuffled, const GemmArgs& a, int64_t grid, hipStream_t s) {
+  return preshuffled ? launch_blockscale<true>(config, a, grid, s) : launch_blockscale<false>(config, a, grid, s);
 }
 
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t s) {

@@ -250,6 +250,15 @@ def f8f8bf16_rowwise_grouped_mm_preshuffle(XQ, WQs, x_scale, w_scale, offs=None,
 def f8f8bf16_groupwise_grouped_stacked(XQ, WQ, x_scale, w_scale, M_sizes, out=None):
     """Y [total_M, N] bf16 for the stacked layout with block scales: x_scale
     [total_M, K/128], w_scale [G, N/128, K/128] (see include/fp8gg.h)."""
+    return _groupwise("f8f8bf16_groupwise_grouped_stacked", XQ, WQ, x_scale, w_scale, M_sizes, out)
+
+
+def f8f8bf16_groupwise_grouped_stacked_preshuffle(XQ, WQs, x_scale, w_scale, M_sizes, out=None):
+    """As the block-scaled stacked op, with WQs produced by f8f8bf16_shuffle_b."""
+    return _groupwise("f8f8bf16_groupwise_grouped_stacked_preshuffle", XQ, WQs, x_scale, w_scale, M_sizes, out)
+
+
+def _groupwise(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out):
     XQ = _bytes(XQ, "XQ")
     WQ = _bytes(WQ, "WQ")
     if XQ.dim() != 2 or WQ.dim() != 3:
@@ -268,10 +277,9 @@ def f8f8bf16_groupwise_grouped_stacked(XQ, WQ, x_scale, w_scale, M_sizes, out=No
     if out is None:
         out = torch.empty((total_M, N), dtype=torch.bfloat16, device=XQ.device)
     _check(out, "out", torch.bfloat16, (total_M, N))
-    st = _lib.load().f8f8bf16_groupwise_grouped_stacked(XQ.data_ptr(), WQ.data_ptr(), x_scale.data_ptr(),
-                                                        w_scale.data_ptr(), M_sizes.data_ptr(), out.data_ptr(),
-                                                        G, total_M, N, K, _stream(XQ.device))
-    _lib.check(st, "f8f8bf16_groupwise_grouped_stacked")
+    st = getattr(_lib.load(), fn_name)(XQ.data_ptr(), WQ.data_ptr(), x_scale.data_ptr(), w_scale.data_ptr(),
+                                       M_sizes.data_ptr(), out.data_ptr(), G, total_M, N, K, _stream(XQ.device))
+    _lib.check(st, fn_name)
     return out
 
 

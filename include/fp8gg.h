@@ -248,6 +248,15 @@ fp8gg_status f8f8bf16_groupwise_grouped_stacked(
     const int64_t* M_sizes, uint16_t* Y,
     int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
 
+/* As f8f8bf16_groupwise_grouped_stacked, with WQs produced by f8f8bf16_shuffle_b
+ * (one kernel serves both B layouts under either scaling scheme: MSLK #471, commit
+ * moving the host-side work into the shared grouped dispatch).  The 128-wide
+ * scale blocks are whole pre-shuffle blocks, so the shape rule is unchanged. */
+fp8gg_status f8f8bf16_groupwise_grouped_stacked_preshuffle(
+    const uint8_t* XQ, const uint8_t* WQs, const float* x_scale, const float* w_scale,
+    const int64_t* M_sizes, uint16_t* Y,
+    int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
+
 /*
  * Rearranges WQ [G, N, K] into the pre-shuffled order WQs (same size, must not
  * overlap WQ).  Byte layout: for group g, N-block nb (FP8GG_SHUFFLE_N rows) and

@@ -108,3 +108,18 @@ def test_full_size_blockscale_workload(F):
         sizes[g] = sel.size
         res = oracle.grouped_stacked_blockscale(w.XQ[sel], w.WQ, w.x_scale[sel], w.w_scale, sizes)
         P.assert_rows_match(got[sel], res, rms=P.rms_of(res.bits), label=f"moe_gate_up_blockscale group {g}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_blockscale_preshuffled_weights_bitwise_equal_plain(F, cfg):
+    """Pre-shuffled W through the same tile and K order: bit-identical to plain W."""
+    w = wl.make_stacked_blockscale([0, 3, 130, 257], 384, 640, seed=960)
+    WQs = F.f8f8bf16_shuffle_b(P.dev(w.WQ))
+    with forced(cfg):
+        plain = run(F, w, w.total_M)
+        whole, y = P.guarded_output((w.total_M, w.N))
+        F.f8f8bf16_groupwise_grouped_stacked_preshuffle(P.dev(w.XQ), WQs, P.dev(w.x_scale), P.dev(w.w_scale),
+                                                        P.dev(w.M_sizes), out=y)
+        torch.cuda.synchronize()
+    P.check_guards(whole)
+    assert np.array_equal(P.bits_of(y), plain)
