@@ -91,7 +91,9 @@ __device__ __forceinline__ v2i_q quantize8(const v4i_q& v, float s, float r) {
   return v2i_q{w[0], w[1]};
 }
 
-__global__ void __launch_bounds__(kQThreads) quantize_rowwise_kernel(const v4i_q* __restrict__ X,
+// At least six waves per SIMD (76 VGPRs, no spills): more rows in flight per CU;
+// measured 5% faster than the compiler's own choice (91 VGPRs, five waves).
+__global__ void __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(6))) quantize_rowwise_kernel(const v4i_q* __restrict__ X,
                                                                      v2i_q* __restrict__ XQ,
                                                                      float* __restrict__ xs, int64_t rows,
                                                                      int64_t K) {
