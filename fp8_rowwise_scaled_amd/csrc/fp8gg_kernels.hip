@@ -1220,30 +1220,33 @@ gg_blockscale_kernel(GemmArgs a) {
     block_barrier();
     if (kt + STAGES - 1 < nkb) issue(kt + STAGES - 1);
     const int slot = kt % STAGES;
-    v8i xf[E::KS][E::FM], wf[E::KS][E::FN];
-    e.read_frags(slot, xf, wf);
-    typename E::Acc part;
-#pragma unroll
-    for (int fm = 0; fm < E::FM; ++fm)
-#pragma unroll
-      for (int fn = 0; fn < E::FN; ++fn) {
-        part[fm][fn] = mfma_32x32x64_fp8(wf[0][fn], xf[0][fm], v16f{0});
-#pragma unroll
-        for (int ks = 1; ks < E::KS; ++ks) part[fm][fn] = mfma_32x32x64_fp8(wf[ks][fn], xf[ks][fm], part[fm][fn]);
-      }
+    // the stage's block scales first: their LDS latency hides under the fragment reads
     float xsv[E::FM], wsv[E::FN];
 #pragma unroll
     for (int fm = 0; fm < E::FM; ++fm) xsv[fm] = sc[slot][e.wm * E::TM + 32 * fm + e.r32];
 #pragma unroll
     for (int fn = 0; fn < E::FN; ++fn) wsv[fn] = sc[slot][SCX + e.col_of(fn) / 128];
+    v8i xf[E::KS][E::FM], wf[E::KS][E::FN];
+    e.read_frags(slot, xf, wf);
+    // block b's MFMAs, then block b - 1's scaling, so that the vector unit works on
+    // one partial while the matrix unit fills the next
+    constexpr int NB = E::FM * E::FN;
+    v16f part[NB];
 #pragma unroll
-    for (int fm = 0; fm < E::FM; ++fm)
+    for (int b = 0; b <= NB; ++b) {
+      if (b < NB) {
+        const int fm = b / E::FN, fn = b % E::FN;
+        part[b] = mfma_32x32x64_fp8(wf[0][fn], xf[0][fm], v16f{0});
 #pragma unroll
-      for (int fn = 0; fn < E::FN; ++fn) {
+        for (int ks = 1; ks < E::KS; ++ks) part[b] = mfma_32x32x64_fp8(wf[ks][fn], xf[ks][fm], part[b]);
+      }
+      if (b > 0) {
+        const int fm = (b - 1) / E::FN, fn = (b - 1) % E::FN;
         const float f = xsv[fm] * wsv[fn];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) acc[fm][fn][i] = __builtin_fmaf(part[fm][fn][i], f, acc[fm][fn][i]);
+        for (int i = 0; i < 16; ++i) acc[fm][fn][i] = __builtin_fmaf(part[b - 1][i], f, acc[fm][fn][i]);
       }
+    }
   }
 
   typename E::Packed pk;
