@@ -6,14 +6,20 @@
 //     products and one epilogue applies x_scale[m] * w_scale[g, n] (Design notes,
 //     scaling-scheme paragraph);
 //   * only the step that finds a tile's group differs between layouts; loads,
-//     K loop and epilogue are shared (Design notes, "one kernel, not six");
+//     K loop and epilogue are shared (Design notes, the paragraph on serving every
+//     layout from one kernel);
 //   * stacked layout: the host launches an upper bound of M tiles and each tile
 //     finds its group from the device-side row counts or retires (commit on
 //     self-retiring tiles); offsets layout: the same walk over an int32 inclusive
 //     prefix (commit adding the offsets layout); padded layout: the group is a grid
 //     coordinate and the row base a multiple of expected_m (commit adding the
 //     padded layout); batched layout: every group a full slab, so the group and
-//     row base are arithmetic (commit adding the batched layout);
+//     row base are arithmetic (commit adding the batched layout); n_offsets: the
+//     groups partition W's rows, found from the N-tile index; k_offsets: the groups
+//     slice K, the group is a grid coordinate and the trip count a run-time value
+//     (commits adding the 3D-2D and 2D-2D forms);
+//   * block scaling: each K block's partial sum is scaled inside the K loop (first
+//     commit of the list, on the two scaling schemes);
 //   * K-tail: K need only be a multiple of 16 bytes; chunks past K read as zero
 //     (commit on the K-tail variant); N-tail: W rows past N are not used and stores
 //     past N are dropped, predicated on the last column of each store (commits on
@@ -33,8 +39,11 @@
 //     slice holds the output column that MFMA row rho of block fn produces in the
 //     chosen lane -> column map, so the loads do the permutation for free.
 //   * Large stacked calls run on a persistent grid whose LDS ring continues from
-//     one tile to the next (gg_tail_kernel); small-M calls use 32-row tiles with a
-//     deep ring, or stream W straight into registers (gg_skinny_kernel).
+//     one tile to the next (gg_persistent_kernel); small-M calls use 32-row tiles
+//     with a deep ring, or stream W straight into registers (gg_skinny_kernel).
+//   * Kernels that run one tile per workgroup (gg_lds_kernel, gg_ragged_kernel,
+//     gg_blockscale_kernel) store the output tile through their idle LDS ring, so
+//     each store instruction covers whole rows (LdsTile::store_shuffled).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
