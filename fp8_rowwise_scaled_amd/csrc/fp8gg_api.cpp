@@ -460,13 +460,14 @@ static fp8gg_status groupwise_stacked(int preshuffled, const uint8_t* XQ, const 
   for (const Range& r : ins)
     if (overlap(out, r)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y overlaps %s", r.name);
 
-  // 128 x 256 tiles unless groups hold fewer than 64 rows on average; FP8GG_BS_CONFIG
-  // (0 or 1) forces one for tests and tuning.
+  // 128 x 256 tiles, on the persistent grid from 256 rows per group on average (as
+  // for rowwise scaling), one per workgroup from 64; 32 x 128 tiles below.
+  // FP8GG_BS_CONFIG (0, 1 or 2) forces one for tests and tuning.
   const int64_t per_group = (total_M + G - 1) / G;
-  int cfg = per_group >= 64 ? 0 : 1;
+  int cfg = per_group >= 256 ? fp8gg::kBlockscalePersistent : (per_group >= 64 ? 0 : 1);
   const int forced = env_int("FP8GG_BS_CONFIG", -1);
   if (forced >= 0) {
-    if (forced > 1) return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_BS_CONFIG=%d is not 0 or 1", forced);
+    if (forced > 2) return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_BS_CONFIG=%d is not 0, 1 or 2", forced);
     cfg = forced;
   }
   const int64_t BM = fp8gg::kBlockscaleTileM[cfg], BN = fp8gg::kBlockscaleTileN[cfg];
@@ -486,7 +487,10 @@ static fp8gg_status groupwise_stacked(int preshuffled, const uint8_t* XQ, const 
   a.m_tiles = ub < total_M ? ub : total_M;
   a.n_tiles = (N + BN - 1) / BN;
   a.zeroing = 0;
-  const int64_t grid = a.m_tiles * a.n_tiles;
+  // persistent: one workgroup per compute unit (FP8GG_TAIL_GRID overrides it for tests)
+  const int forced_grid = env_int("FP8GG_TAIL_GRID", 0);
+  const int64_t grid = cfg == fp8gg::kBlockscalePersistent ? (forced_grid > 0 ? forced_grid : device_cus())
+                                                           : a.m_tiles * a.n_tiles;
   if (grid > 0x7FFFFFFFLL)
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "grid of %lld workgroups exceeds the launch limit", (long long)grid);
   if (env_int("FP8GG_LOG", 0))

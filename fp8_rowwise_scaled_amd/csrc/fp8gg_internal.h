@@ -74,9 +74,11 @@ hipError_t launch_gemm_persistent(int layout, int config_id, bool k_tail, const 
                                   int tail_mode, hipStream_t stream);
 hipError_t launch_gemm_ragged(int layout, int config_id, bool k_tail, const GemmArgs& args, int64_t grid,
                               hipStream_t stream);
-// Block-scaled stacked GEMM: config 0 tiles 128 x 256, config 1 tiles 32 x 128.
-constexpr int kBlockscaleTileM[2] = {128, 32};
-constexpr int kBlockscaleTileN[2] = {256, 128};
+// Block-scaled stacked GEMM: config 0 tiles 128 x 256, config 1 tiles 32 x 128,
+// config 2 the 128 x 256 tiles on a persistent grid (one workgroup per CU).
+constexpr int kBlockscaleTileM[3] = {128, 32, 128};
+constexpr int kBlockscaleTileN[3] = {256, 128, 256};
+constexpr int kBlockscalePersistent = 2;
 hipError_t launch_gemm_blockscale(int config, bool preshuffled, const GemmArgs& args, int64_t grid,
                                   hipStream_t stream);
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t stream);

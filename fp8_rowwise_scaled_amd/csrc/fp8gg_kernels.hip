@@ -1161,28 +1161,28 @@ gg_persistent_kernel(GemmArgs a, int tail_mode) {
 // rounds and stores.  K and N are whole numbers of blocks (checked on the host).
 // PRE: W comes pre-shuffled (f8f8bf16_shuffle_b) and is read through the same tile
 // as in the rowwise kernels; a lane's 16 columns still lie in one 128-column block.
-template <int BM, int BN, int WM, int WN, int STAGES, bool PRE>
-__global__ void __launch_bounds__(WM * WN * 64)
-gg_blockscale_kernel(GemmArgs a) {
-  constexpr int BK = 128;
-  typedef LdsTile<BM, BN, BK, WM, WN, STAGES, false, PRE> E;
-  constexpr int SCX = BM > 64 ? BM : 64;   // x_scale floats per slot (slack past BM)
-  constexpr int SC = SCX + 64;             // then the W block scales (BN / 128 used)
+// Floats per LDS scale slot for a block-scaled tile of BM rows: the tile's x_scale
+// column (slack past BM) and then its W block scales.
+template <int BM>
+struct BlockscaleSlots {
+  static constexpr int SCX = BM > 64 ? BM : 64;
+  static constexpr int SC = SCX + 64;
+};
+
+// One block-scaled output tile (rows of t, columns n0 .. n0 + BN): the K loop over
+// 128-byte scale blocks and the coalesced store.  sc holds E::STAGES_ scale slots
+// of BlockscaleSlots<BM>::SC floats.  Starts with a workgroup barrier, so that a
+// workgroup can run tile after tile over the same LDS.
+template <typename E>
+__device__ __forceinline__ void blockscale_tile(E& e, const GemmArgs& a, const Tile& t, int64_t n0, float* sc,
+                                                float* sc_dummy) {
+  constexpr int BK = 128, BM = E::BM_, BN = E::BN_, STAGES = E::STAGES_;
+  constexpr int SCX = BlockscaleSlots<BM>::SCX, SC = BlockscaleSlots<BM>::SC;
   constexpr int L = E::LOADS_PER_STAGE + 1;
   static_assert(E::EVEN_LOADS, "the stage wait counts assume equal copies per wave");
-  static_assert(SCX / 64 + 1 <= WM * WN, "one scale copy per wave");
+  static_assert(SCX / 64 + 1 <= E::NT / 64, "one scale copy per wave");
   static_assert(BN % 128 == 0 && E::TN % 16 == 0, "a lane's 16 columns lie in one block");
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
-  __shared__ __attribute__((aligned(16))) float sc[STAGES][SC];
-  __shared__ __attribute__((aligned(16))) float sc_dummy[64];
-
-  const int64_t bid = blockIdx.x;
-  const int64_t n_tile = bid % a.n_tiles;
-  Tile t;
-  if (!resolve_packed<kStacked, BM>(a, bid / a.n_tiles, t)) return;
-  const int64_t n0 = n_tile * BN;
-  E e;
-  e.init(smem);
+  block_barrier();   // the previous tile of this workgroup may still read the ring
   e.setup(a, t, n0);
   const int nkb = (int)(a.K / BK);
   const int64_t nbn = a.N / 128;
@@ -1209,7 +1209,7 @@ gg_blockscale_kernel(GemmArgs a) {
   auto issue = [&](int kt) {
     const int slot = kt % STAGES;
     e.issue(kt, slot, nkb, a.K);
-    copy4_to_lds(ssrc + kt, lds_addr(sdst >= 0 ? &sc[slot][sdst] : sc_dummy));
+    copy4_to_lds(ssrc + kt, lds_addr(sdst >= 0 ? sc + slot * SC + sdst : sc_dummy));
   };
 
   typename E::Acc acc;
@@ -1232,9 +1232,9 @@ gg_blockscale_kernel(GemmArgs a) {
     // the stage's block scales first: their LDS latency hides under the fragment reads
     float xsv[E::FM], wsv[E::FN];
 #pragma unroll
-    for (int fm = 0; fm < E::FM; ++fm) xsv[fm] = sc[slot][e.wm * E::TM + 32 * fm + e.r32];
+    for (int fm = 0; fm < E::FM; ++fm) xsv[fm] = sc[slot * SC + e.wm * E::TM + 32 * fm + e.r32];
 #pragma unroll
-    for (int fn = 0; fn < E::FN; ++fn) wsv[fn] = sc[slot][SCX + e.col_of(fn) / 128];
+    for (int fn = 0; fn < E::FN; ++fn) wsv[fn] = sc[slot * SC + SCX + e.col_of(fn) / 128];
     v8i xf[E::KS][E::FM], wf[E::KS][E::FN];
     e.read_frags(slot, xf, wf);
     // block b's MFMAs, then block b - 1's scaling, so that the vector unit works on
@@ -1274,6 +1274,66 @@ gg_blockscale_kernel(GemmArgs a) {
         pk[fm][fn][half] = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
       }
   e.store_shuffled(a, t, n0, pk);
+}
+
+template <int BM, int BN, int WM, int WN, int STAGES, bool PRE>
+__global__ void __launch_bounds__(WM * WN * 64)
+gg_blockscale_kernel(GemmArgs a) {
+  typedef LdsTile<BM, BN, 128, WM, WN, STAGES, false, PRE> E;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) float sc[STAGES * BlockscaleSlots<BM>::SC];
+  __shared__ __attribute__((aligned(16))) float sc_dummy[64];
+  const int64_t bid = blockIdx.x;
+  Tile t;
+  if (!resolve_packed<kStacked, BM>(a, bid / a.n_tiles, t)) return;
+  E e;
+  e.init(smem);
+  blockscale_tile(e, a, t, (bid % a.n_tiles) * BN, sc, sc_dummy);
+}
+
+// The same on a persistent grid (one workgroup per compute unit): whole tiles w,
+// w + P, ..., then, when the last round is partial, its tiles as (BM/2) x (BN/2)
+// quarter tiles by the rule of the rowwise persistent kernel (tail_quarters), so a
+// partial round costs a fraction of a tile.  No pipelining across tiles.
+template <int BM, int BN, int WM, int WN, int STAGES, bool PRE>
+__global__ void __launch_bounds__(WM * WN * 64)
+gg_blockscale_persistent_kernel(GemmArgs a) {
+  typedef LdsTile<BM, BN, 128, WM, WN, STAGES, false, PRE> E;
+  constexpr int Q_STAGE_BYTES = (BM + BN) / 2 * 128;
+  constexpr int Q_STAGES = E::SMEM_BYTES / Q_STAGE_BYTES < 8 ? E::SMEM_BYTES / Q_STAGE_BYTES : 8;
+  typedef LdsTile<BM / 2, BN / 2, 128, WM, WN, Q_STAGES, false, PRE> Q;
+  static_assert(Q::SMEM_BYTES <= E::SMEM_BYTES, "quarter tiles reuse the LDS ring");
+  constexpr int SC_FLOATS = STAGES * BlockscaleSlots<BM>::SC > Q_STAGES * BlockscaleSlots<BM / 2>::SC
+                                ? STAGES * BlockscaleSlots<BM>::SC
+                                : Q_STAGES * BlockscaleSlots<BM / 2>::SC;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
+  __shared__ __attribute__((aligned(16))) float sc[SC_FLOATS];
+  __shared__ __attribute__((aligned(16))) float sc_dummy[64];
+
+  const int64_t P = gridDim.x;
+  const int64_t w = blockIdx.x;
+  const int64_t T = count_m_tiles<kStacked, BM>(a) * a.n_tiles;
+  const int64_t rem = tail_quarters(T, P, 0) ? T % P : 0;
+  const int64_t whole = T - rem;
+  for (int64_t tile = w; tile < whole; tile += P) {
+    Tile t;
+    resolve_packed<kStacked, BM>(a, tile / a.n_tiles, t);
+    E e;
+    e.init(smem);
+    blockscale_tile(e, a, t, (tile % a.n_tiles) * BN, sc, sc_dummy);
+  }
+  for (int64_t qn = w; qn < 4 * rem; qn += P) {
+    const int64_t tile = whole + qn / 4;
+    const int q = (int)(qn % 4);
+    Tile t;
+    resolve_packed<kStacked, BM>(a, tile / a.n_tiles, t);
+    t.row_base += (q >> 1) * (BM / 2);
+    const int64_t n0 = (tile % a.n_tiles) * BN + (q & 1) * (BN / 2);
+    if (t.row_base >= t.row_end || n0 >= a.N) continue;
+    Q e;
+    e.init(smem);
+    blockscale_tile(e, a, t, n0, sc, sc_dummy);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1683,7 +1743,8 @@ hipError_t launch_gemm_ragged(int layout, int config_id, bool k_tail, const Gemm
 }
 
 // Block-scaled configurations: 0 = 128 x 256 tiles (2 x 4 waves, 3 stages),
-// 1 = 32 x 128 tiles (1 x 4 waves, 3 stages) for few rows per group.
+// 1 = 32 x 128 tiles (1 x 4 waves, 3 stages) for few rows per group, 2 = the
+// 128 x 256 tiles on a persistent grid (grid = compute units).
 template <bool PRE>
 static hipError_t launch_blockscale(int config, const GemmArgs& a, int64_t grid, hipStream_t s) {
   switch (config) {
@@ -1692,6 +1753,10 @@ static hipError_t launch_blockscale(int config, const GemmArgs& a, int64_t grid,
       return hipGetLastError();
     case 1:
       hipLaunchKernelGGL((gg_blockscale_kernel<32, 128, 1, 4, 3, PRE>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+      return hipGetLastError();
+    case 2:
+      hipLaunchKernelGGL((gg_blockscale_persistent_kernel<128, 256, 2, 4, 3, PRE>), dim3((uint32_t)grid), dim3(512),
+                         0, s, a);
       return hipGetLastError();
     default: return hipErrorInvalidValue;
   }

@@ -62,7 +62,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("cfg", [0, 1])
+@pytest.mark.parametrize("cfg", [0, 1, 2])
 @pytest.mark.parametrize("case", range(len(CASES)))
 def test_blockscale_matches_oracle(F, cfg, case):
     sizes, N, K, total_M = CASES[case]
@@ -110,7 +110,7 @@ def test_full_size_blockscale_workload(F):
         P.assert_rows_match(got[sel], res, rms=P.rms_of(res.bits), label=f"moe_gate_up_blockscale group {g}")
 
 
-@pytest.mark.parametrize("cfg", [0, 1])
+@pytest.mark.parametrize("cfg", [0, 1, 2])
 def test_blockscale_preshuffled_weights_bitwise_equal_plain(F, cfg):
     """Pre-shuffled W through the same tile and K order: bit-identical to plain W."""
     w = wl.make_stacked_blockscale([0, 3, 130, 257], 384, 640, seed=960)
@@ -123,3 +123,29 @@ def test_blockscale_preshuffled_weights_bitwise_equal_plain(F, cfg):
         torch.cuda.synchronize()
     P.check_guards(whole)
     assert np.array_equal(P.bits_of(y), plain)
+
+
+@pytest.mark.parametrize("grid", [5, 7, 9])
+def test_blockscale_persistent_grid_bitwise_equal_one_tile_schedule(F, grid):
+    """The persistent schedule (config 2) on small grids: whole tiles plus quarter
+    tiles (12 tiles on 5 workgroups), whole tiles only (7), two rounds of quarter
+    tiles after the whole ones (9; the default grid of 256 runs only quarters):
+    each output element is computed by one workgroup in the same K
+    order, so the result equals the one-tile-per-workgroup schedule (config 0)
+    bit for bit, and the oracle within the tolerance."""
+    w = wl.make_stacked_blockscale([0, 3, 130, 257], 384, 640, seed=970)
+    with forced(0):
+        ref = run(F, w, w.total_M)
+    old = os.environ.get("FP8GG_TAIL_GRID")
+    os.environ["FP8GG_TAIL_GRID"] = str(grid)
+    try:
+        with forced(2):
+            got = run(F, w, w.total_M)
+    finally:
+        if old is None:
+            os.environ.pop("FP8GG_TAIL_GRID", None)
+        else:
+            os.environ["FP8GG_TAIL_GRID"] = old
+    assert np.array_equal(got, ref)
+    res = oracle.grouped_stacked_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
+    P.assert_rows_match(got, res, label=f"blockscale persistent grid {grid}")
