@@ -149,3 +149,21 @@ def test_blockscale_persistent_grid_bitwise_equal_one_tile_schedule(F, grid):
     assert np.array_equal(got, ref)
     res = oracle.grouped_stacked_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
     P.assert_rows_match(got, res, label=f"blockscale persistent grid {grid}")
+
+
+def test_blockscale_long_k(F):
+    """K = 28672 (224 scale blocks, the dense-expert depth): 224 scaled partial sums
+    per output; both the persistent and the one-tile schedules against the oracle
+    on every column of sampled rows."""
+    w = wl.make_stacked_blockscale([300, 0, 212], 512, 28672, seed=980)
+    rows = np.sort(np.random.default_rng(981).choice(w.total_M, 24, replace=False))
+    owner = oracle.stacked_row_groups(w.M_sizes, w.total_M)[rows]
+    for cfg in (2, 0):
+        with forced(cfg):
+            got = run(F, w, w.total_M)
+        for g in np.unique(owner):
+            sel = rows[owner == g]
+            sizes = np.zeros(w.G, np.int64)
+            sizes[g] = sel.size
+            res = oracle.grouped_stacked_blockscale(w.XQ[sel], w.WQ, w.x_scale[sel], w.w_scale, sizes)
+            P.assert_rows_match(got[sel], res, rms=P.rms_of(res.bits), label=f"long K cfg {cfg} group {g}")

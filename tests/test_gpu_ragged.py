@@ -126,6 +126,7 @@ K_CASES = [
     (202, [1040], 1040, 300, 264),                                    # one slice, two M tiles, N tail
     (203, np.cumsum(16 * np.random.default_rng(9).integers(0, 5, 12)).tolist(), 16 * 48, 5, 64),  # 12 groups
     (204, [64, 32, 200, 99999], 160, 7, 24),                          # ill-formed: empty, cut at total_K
+    (205, np.cumsum(16 * np.random.default_rng(11).integers(0, 4, 40)).tolist(), 16 * 160, 3, 40),  # 40 groups
 ]
 
 
