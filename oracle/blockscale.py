@@ -86,3 +86,41 @@ def grouped_stacked_blockscale(XQ, WQ, x_scale, w_scale, M_sizes, block_k: int =
         bits[rows] = bf16_rne_from_f64(v)
         row_class[rows] = ROW_WRITTEN
     return OracleResult(values, bits, row_class)
+
+
+def grouped_dynamic_blockscale(XQ, WQ, x_scale, w_scale, zero_start_index_M, zeroing_output_tensor: bool = True,
+                               block_k: int = 128, block_n: int = 128) -> OracleResult:
+    """Padded layout with block scales: XQ [G, em, K], WQ [G, N, K], x_scale
+    [G, em, K / block_k], w_scale [G, N / block_n, K / block_k], zero_start_index_M
+    [G] -> Y [G, em, N].  Row i of slab g is valid if i < clamp(zsi[g], 0, em);
+    padding rows are zero when zeroing_output_tensor, else untouched (flattened
+    row classes [G * em])."""
+    XQ = np.asarray(XQ, np.uint8)
+    WQ = np.asarray(WQ, np.uint8)
+    G, em, K = XQ.shape
+    G2, N, K2 = WQ.shape
+    assert G == G2 and K == K2 and K % block_k == 0 and N % block_n == 0
+    x_scale = np.asarray(x_scale, np.float32)
+    w_scale = np.asarray(w_scale, np.float32)
+    assert x_scale.shape == (G, em, K // block_k) and w_scale.shape == (G, N // block_n, K // block_k)
+    if K == 0:
+        return OracleResult(np.zeros((G, em, N)), np.zeros((G, em, N), np.uint16),
+                            np.full(G * em, ROW_ZEROED, np.int8))
+    valid = np.clip(np.asarray(zero_start_index_M, np.int64), 0, em)
+    values = np.full((G, em, N), np.nan)
+    bits = np.full((G, em, N), UNTOUCHED_SENTINEL, dtype=np.uint16)
+    row_class = np.full((G, em), ROW_UNTOUCHED, np.int8)
+    col_block = column_blocks(N, block_n)
+    for g in range(G):
+        v = int(valid[g])
+        if v:
+            part = block_partials(XQ[g, :v], WQ[g], block_k)
+            out = scale_blocks(part, x_scale[g, :v], w_scale[g][col_block])
+            values[g, :v] = out
+            bits[g, :v] = bf16_rne_from_f64(out)
+            row_class[g, :v] = ROW_WRITTEN
+        if zeroing_output_tensor and v < em:
+            values[g, v:] = 0.0
+            bits[g, v:] = 0
+            row_class[g, v:] = ROW_ZEROED
+    return OracleResult(values, bits, row_class.reshape(-1))

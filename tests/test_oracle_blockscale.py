@@ -86,8 +86,50 @@ def test_blockscale_k_zero_is_zero():
     assert np.all(res.bits == 0) and np.all(res.row_class == oracle.ROW_ZEROED)
 
 
+def _check_dynamic(seed, zsi, em, N, K, bk, bn, zeroing):
+    """Padded layout against the exact brute force of the stacked layout on the
+    compacted valid rows, and the row classes of the padding rows."""
+    G = len(zsi)
+    XQ, WQ, xs, ws, _ = _problem(seed, [em] * G, N, K, bk, bn, False)
+    XQd, xsd = XQ.reshape(G, em, K), xs.reshape(G, em, K // bk)
+    res = oracle.grouped_dynamic_blockscale(XQd, WQ, xsd, ws, zsi, zeroing, bk, bn)
+    valid = np.clip(np.array(zsi), 0, em)
+    rows = np.concatenate([g * em + np.arange(valid[g]) for g in range(G)]).astype(np.int64)
+    exact = exact_ref.blockscale_exact(XQ[rows], WQ, xs[rows], ws, valid, bk, bn)
+    got = res.bits.reshape(G * em, N)[rows]
+    for r, row in enumerate(exact):
+        want = np.array(row, np.int64)
+        zero = (want & 0x7FFF) == 0
+        g = got[r].astype(np.int64)
+        if not (np.array_equal(g[~zero], want[~zero]) and np.all((g[zero] & 0x7FFF) == 0)):
+            return False
+    cls = res.row_class.reshape(G, em)
+    pad = oracle.ROW_ZEROED if zeroing else oracle.ROW_UNTOUCHED
+    for gi in range(G):
+        if not (np.all(cls[gi, :valid[gi]] == oracle.ROW_WRITTEN) and np.all(cls[gi, valid[gi]:] == pad)):
+            return False
+    return True
+
+
+@pytest.mark.parametrize("zeroing", [True, False])
+def test_dynamic_blockscale_equals_exact_bruteforce_on_valid_rows(zeroing):
+    assert _check_dynamic(21, [2, 0, 4, 9], 4, 6, 48, 16, 2, zeroing)
+
+
+def test_dynamic_blockscale_padding_rows_are_zero_and_equal_stacked_on_compacted_rows():
+    G, em, N, K, bk, bn = 3, 5, 8, 64, 32, 4
+    XQ, WQ, xs, ws, _ = _problem(22, [em] * G, N, K, bk, bn, False)
+    zsi = np.array([5, 0, 2])
+    d = oracle.grouped_dynamic_blockscale(XQ.reshape(G, em, K), WQ, xs.reshape(G, em, K // bk), ws, zsi, True, bk, bn)
+    rows = np.concatenate([g * em + np.arange(zsi[g]) for g in range(G)])
+    st = oracle.grouped_stacked_blockscale(XQ[rows], WQ, xs[rows], ws, zsi, bk, bn)
+    assert np.array_equal(d.bits.reshape(G * em, N)[rows], st.bits)
+    pad = np.setdiff1d(np.arange(G * em), rows)
+    assert np.all(d.bits.reshape(G * em, N)[pad] == 0)
+
+
 def _pins_pass():
-    return all(_check(*c) for c in CASES)
+    return all(_check(*c) for c in CASES) and _check_dynamic(21, [2, 0, 4, 9], 4, 6, 48, 16, 2, True)
 
 
 def _mut_shifted_scales(partials, xs, ws_cols):
