@@ -35,6 +35,8 @@ EXPORTS = (
     "f8f8bf16_rowwise_grouped_k_offsets",
     "f8f8bf16_groupwise_grouped_stacked",
     "f8f8bf16_groupwise_grouped_stacked_preshuffle",
+    "f8f8bf16_groupwise_grouped_dynamic",
+    "f8f8bf16_groupwise_grouped_dynamic_preshuffle",
     "f8f8bf16_shuffle_b",
     "f8f8bf16_quantize_rowwise",
     "f8f8bf16_last_error",
@@ -91,6 +93,8 @@ def load() -> ctypes.CDLL:
     lib.f8f8bf16_groupwise_grouped_stacked.argtypes = gemm + [P]
     lib.f8f8bf16_groupwise_grouped_stacked.restype = I
     lib.f8f8bf16_groupwise_grouped_stacked_preshuffle.argtypes = gemm + [P]
+    lib.f8f8bf16_groupwise_grouped_dynamic.argtypes = gemm + [I, P]
+    lib.f8f8bf16_groupwise_grouped_dynamic_preshuffle.argtypes = gemm + [I, P]
     batched = [P, P, P, P, P, I64, I64, I64, I64, P]
     lib.f8f8bf16_rowwise_grouped_batched.argtypes = batched
     lib.f8f8bf16_rowwise_grouped_batched_preshuffle.argtypes = batched

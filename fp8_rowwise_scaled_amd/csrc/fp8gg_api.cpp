@@ -426,48 +426,53 @@ fp8gg_status f8f8bf16_rowwise_grouped_k_offsets(const uint8_t* XQ, const uint8_t
   return run(FP8GG_LAYOUT_K_OFFSETS, 0, XQ, WQ, x_scale, w_scale, k_offsets, Y, G, M, N, K, 0, stream);
 }
 
-static fp8gg_status groupwise_stacked(int preshuffled, const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
-                                      const float* w_scale, const int64_t* M_sizes, uint16_t* Y, int64_t G,
-                                      int64_t total_M, int64_t N, int64_t K, void* stream) {
+// Block-scaled GEMM, stacked (meta = M_sizes, M = total_M) or padded (meta =
+// zero_start_index_M, M = expected_m, zeroing flag) layout.
+static fp8gg_status groupwise(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* WQ,
+                              const float* x_scale, const float* w_scale, const int64_t* meta, uint16_t* Y, int64_t G,
+                              int64_t M, int64_t N, int64_t K, int zeroing, void* stream) {
   constexpr int64_t B = 128;   // scale block along K and along N (whole pre-shuffle blocks too)
-  fp8gg_status st = check_shape(FP8GG_LAYOUT_STACKED, preshuffled, G, total_M, N, K);
+  const bool padded = layout == FP8GG_LAYOUT_PADDED;
+  fp8gg_status st = check_shape(layout, preshuffled, G, M, N, K);
   if (st != FP8GG_OK) return st;
   if (K % B != 0 || N % B != 0)
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE,
                 "block scaling needs K and N to be whole numbers of %lld-wide scale blocks (N=%lld K=%lld)",
                 (long long)B, (long long)N, (long long)K);
-  if (total_M == 0 || N == 0) return ok();
+  const int64_t rows = padded ? G * M : M;
+  if (rows == 0 || N == 0) return ok();
   if (!Y) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y is null");
   if (!aligned(Y, 16)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y must be 16-byte aligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (K == 0) {
-    hipError_t e = fp8gg::launch_zero_fill(Y, total_M * N, s);
+    hipError_t e = fp8gg::launch_zero_fill(Y, rows * N, s);
     if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "zero fill launch failed: %s", hipGetErrorString(e));
     return ok();
   }
   if (G == 0) return ok();
-  if (!XQ || !WQ || !x_scale || !w_scale || !M_sizes)
+  if (!XQ || !WQ || !x_scale || !w_scale || !meta)
     return fail(FP8GG_ERR_INVALID_ARGUMENT, "null input pointer");
-  if (!aligned(XQ, 16) || !aligned(WQ, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(M_sizes, 8))
+  if (!aligned(XQ, 16) || !aligned(WQ, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(meta, 8))
     return fail(FP8GG_ERR_INVALID_ARGUMENT,
-                "XQ and WQ must be 16-byte, x_scale and w_scale 4-byte and M_sizes 8-byte aligned");
-  const Range out{Y, total_M * N * 2, "Y"};
-  const Range ins[] = {{XQ, total_M * K, "XQ"},
+                "XQ and WQ must be 16-byte, x_scale and w_scale 4-byte and the row metadata 8-byte aligned");
+  const Range out{Y, rows * N * 2, "Y"};
+  const Range ins[] = {{XQ, rows * K, "XQ"},
                        {WQ, G * N * K, "WQ"},
-                       {x_scale, total_M * (K / B) * 4, "x_scale"},
+                       {x_scale, rows * (K / B) * 4, "x_scale"},
                        {w_scale, G * (N / B) * (K / B) * 4, "w_scale"},
-                       {M_sizes, G * 8, "M_sizes"}};
+                       {meta, G * 8, "row metadata"}};
   for (const Range& r : ins)
     if (overlap(out, r)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y overlaps %s", r.name);
 
-  // 128 x 256 tiles, on the persistent grid from 256 rows per group on average (as
-  // for rowwise scaling), one per workgroup from 64; 32 x 128 tiles below.
-  // FP8GG_BS_CONFIG (0, 1 or 2) forces one for tests and tuning.
-  const int64_t per_group = (total_M + G - 1) / G;
-  int cfg = per_group >= 256 ? fp8gg::kBlockscalePersistent : (per_group >= 64 ? 0 : 1);
+  // 128 x 256 tiles, on the persistent grid (stacked layout only) from 256 rows per
+  // group on average, as for rowwise scaling; one per workgroup from 64; 32 x 128
+  // tiles below.  FP8GG_BS_CONFIG (0, 1 or 2) forces one for tests and tuning.
+  const int64_t per_group = padded ? M : (M + G - 1) / G;
+  int cfg = (!padded && per_group >= 256) ? fp8gg::kBlockscalePersistent : (per_group >= 64 ? 0 : 1);
   const int forced = env_int("FP8GG_BS_CONFIG", -1);
   if (forced >= 0) {
-    if (forced > 2) return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_BS_CONFIG=%d is not 0, 1 or 2", forced);
+    if (forced > 2 || (padded && forced == fp8gg::kBlockscalePersistent))
+      return fail(FP8GG_ERR_INVALID_ARGUMENT, "FP8GG_BS_CONFIG=%d is not a configuration of this layout", forced);
     cfg = forced;
   }
   const int64_t BM = fp8gg::kBlockscaleTileM[cfg], BN = fp8gg::kBlockscaleTileN[cfg];
@@ -476,28 +481,33 @@ static fp8gg_status groupwise_stacked(int preshuffled, const uint8_t* XQ, const 
   a.W = WQ;
   a.xs = x_scale;
   a.ws = w_scale;
-  a.meta = M_sizes;
+  a.meta = meta;
   a.offs = nullptr;
   a.Y = Y;
   a.G = G;
-  a.M = total_M;
+  a.M = M;
   a.N = N;
   a.K = K;
-  const int64_t ub = (total_M + BM - 1) / BM + G - 1;
-  a.m_tiles = ub < total_M ? ub : total_M;
+  if (padded) {
+    a.m_tiles = (M + BM - 1) / BM;
+  } else {
+    const int64_t ub = (M + BM - 1) / BM + G - 1;
+    a.m_tiles = ub < M ? ub : M;
+  }
   a.n_tiles = (N + BN - 1) / BN;
-  a.zeroing = 0;
+  a.zeroing = padded && zeroing ? 1 : 0;
   // persistent: one workgroup per compute unit (FP8GG_TAIL_GRID overrides it for tests)
   const int forced_grid = env_int("FP8GG_TAIL_GRID", 0);
   const int64_t grid = cfg == fp8gg::kBlockscalePersistent ? (forced_grid > 0 ? forced_grid : device_cus())
-                                                           : a.m_tiles * a.n_tiles;
+                                                           : a.m_tiles * a.n_tiles * (padded ? G : 1);
   if (grid > 0x7FFFFFFFLL)
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "grid of %lld workgroups exceeds the launch limit", (long long)grid);
   if (env_int("FP8GG_LOG", 0))
-    std::fprintf(stderr, "[fp8gg] groupwise G=%lld M=%lld N=%lld K=%lld -> cfg=%d tile=%lldx%lld grid=%lld\n",
-                 (long long)G, (long long)total_M, (long long)N, (long long)K, cfg, (long long)BM, (long long)BN,
+    std::fprintf(stderr, "[fp8gg] groupwise layout=%d G=%lld M=%lld N=%lld K=%lld -> cfg=%d tile=%lldx%lld grid=%lld\n",
+                 layout, (long long)G, (long long)M, (long long)N, (long long)K, cfg, (long long)BM, (long long)BN,
                  (long long)grid);
-  hipError_t e = fp8gg::launch_gemm_blockscale(cfg, preshuffled != 0, a, grid, s);
+  hipError_t e = fp8gg::launch_gemm_blockscale(padded ? fp8gg::kPadded : fp8gg::kStacked, cfg, preshuffled != 0, a,
+                                               grid, s);
   if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -505,14 +515,31 @@ static fp8gg_status groupwise_stacked(int preshuffled, const uint8_t* XQ, const 
 fp8gg_status f8f8bf16_groupwise_grouped_stacked(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
                                                 const float* w_scale, const int64_t* M_sizes, uint16_t* Y, int64_t G,
                                                 int64_t total_M, int64_t N, int64_t K, void* stream) {
-  return groupwise_stacked(0, XQ, WQ, x_scale, w_scale, M_sizes, Y, G, total_M, N, K, stream);
+  return groupwise(FP8GG_LAYOUT_STACKED, 0, XQ, WQ, x_scale, w_scale, M_sizes, Y, G, total_M, N, K, 0, stream);
 }
 
 fp8gg_status f8f8bf16_groupwise_grouped_stacked_preshuffle(const uint8_t* XQ, const uint8_t* WQs, const float* x_scale,
                                                            const float* w_scale, const int64_t* M_sizes, uint16_t* Y,
                                                            int64_t G, int64_t total_M, int64_t N, int64_t K,
                                                            void* stream) {
-  return groupwise_stacked(1, XQ, WQs, x_scale, w_scale, M_sizes, Y, G, total_M, N, K, stream);
+  return groupwise(FP8GG_LAYOUT_STACKED, 1, XQ, WQs, x_scale, w_scale, M_sizes, Y, G, total_M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_groupwise_grouped_dynamic(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                                const float* w_scale, const int64_t* zero_start_index_M, uint16_t* Y,
+                                                int64_t G, int64_t expected_m, int64_t N, int64_t K,
+                                                int zeroing_output_tensor, void* stream) {
+  return groupwise(FP8GG_LAYOUT_PADDED, 0, XQ, WQ, x_scale, w_scale, zero_start_index_M, Y, G, expected_m, N, K,
+                   zeroing_output_tensor, stream);
+}
+
+fp8gg_status f8f8bf16_groupwise_grouped_dynamic_preshuffle(const uint8_t* XQ, const uint8_t* WQs,
+                                                           const float* x_scale, const float* w_scale,
+                                                           const int64_t* zero_start_index_M, uint16_t* Y, int64_t G,
+                                                           int64_t expected_m, int64_t N, int64_t K,
+                                                           int zeroing_output_tensor, void* stream) {
+  return groupwise(FP8GG_LAYOUT_PADDED, 1, XQ, WQs, x_scale, w_scale, zero_start_index_M, Y, G, expected_m, N, K,
+                   zeroing_output_tensor, stream);
 }
 
 fp8gg_status f8f8bf16_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale, int64_t rows, int64_t K,

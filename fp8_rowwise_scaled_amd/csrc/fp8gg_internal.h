@@ -79,7 +79,7 @@ hipError_t launch_gemm_ragged(int layout, int config_id, bool k_tail, const Gemm
 constexpr int kBlockscaleTileM[3] = {128, 32, 128};
 constexpr int kBlockscaleTileN[3] = {256, 128, 256};
 constexpr int kBlockscalePersistent = 2;
-hipError_t launch_gemm_blockscale(int config, bool preshuffled, const GemmArgs& args, int64_t grid,
+hipError_t launch_gemm_blockscale(int layout, int config, bool preshuffled, const GemmArgs& args, int64_t grid,
                                   hipStream_t stream);
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t stream);
 hipError_t launch_quantize_rowwise(const uint16_t* X, uint8_t* XQ, float* x_scale, int64_t rows, int64_t K,

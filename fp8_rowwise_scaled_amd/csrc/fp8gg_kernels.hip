@@ -1276,7 +1276,10 @@ __device__ __forceinline__ void blockscale_tile(E& e, const GemmArgs& a, const T
   e.store_shuffled(a, t, n0, pk);
 }
 
-template <int BM, int BN, int WM, int WN, int STAGES, bool PRE>
+// One tile per workgroup; stacked layout, or padded (the group from the grid,
+// rows past the slab's valid count zeroed under the zeroing flag, whole-padding
+// tiles written as zeros without a K loop).
+template <int LAYOUT, int BM, int BN, int WM, int WN, int STAGES, bool PRE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gg_blockscale_kernel(GemmArgs a) {
   typedef LdsTile<BM, BN, 128, WM, WN, STAGES, false, PRE> E;
@@ -1284,11 +1287,24 @@ gg_blockscale_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(16))) float sc[STAGES * BlockscaleSlots<BM>::SC];
   __shared__ __attribute__((aligned(16))) float sc_dummy[64];
   const int64_t bid = blockIdx.x;
+  const int64_t n0 = (bid % a.n_tiles) * BN;
+  const int64_t rest = bid / a.n_tiles;
   Tile t;
-  if (!resolve_packed<kStacked, BM>(a, bid / a.n_tiles, t)) return;
+  if constexpr (LAYOUT == kPadded) {
+    if (!resolve_padded<BM>(a, rest / a.m_tiles, rest % a.m_tiles, t)) return;
+    if (t.row_base >= t.row_end) {
+      const int64_t tile_row_end = t.row_base + BM;
+      const int64_t r1 = tile_row_end < t.zero_end ? tile_row_end : t.zero_end;
+      const int64_t c1 = n0 + BN < a.N ? n0 + BN : a.N;
+      zero_rect<E::NT>(a.Y, a.N, t.row_base, r1, n0, c1);
+      return;
+    }
+  } else {
+    if (!resolve_packed<kStacked, BM>(a, rest, t)) return;
+  }
   E e;
   e.init(smem);
-  blockscale_tile(e, a, t, (bid % a.n_tiles) * BN, sc, sc_dummy);
+  blockscale_tile(e, a, t, n0, sc, sc_dummy);
 }
 
 // The same on a persistent grid (one workgroup per compute unit): whole tiles w,
@@ -1745,16 +1761,19 @@ hipError_t launch_gemm_ragged(int layout, int config_id, bool k_tail, const Gemm
 // Block-scaled configurations: 0 = 128 x 256 tiles (2 x 4 waves, 3 stages),
 // 1 = 32 x 128 tiles (1 x 4 waves, 3 stages) for few rows per group, 2 = the
 // 128 x 256 tiles on a persistent grid (grid = compute units).
-template <bool PRE>
+template <int LAYOUT, bool PRE>
 static hipError_t launch_blockscale(int config, const GemmArgs& a, int64_t grid, hipStream_t s) {
   switch (config) {
     case 0:
-      hipLaunchKernelGGL((gg_blockscale_kernel<128, 256, 2, 4, 3, PRE>), dim3((uint32_t)grid), dim3(512), 0, s, a);
+      hipLaunchKernelGGL((gg_blockscale_kernel<LAYOUT, 128, 256, 2, 4, 3, PRE>), dim3((uint32_t)grid), dim3(512), 0,
+                         s, a);
       return hipGetLastError();
     case 1:
-      hipLaunchKernelGGL((gg_blockscale_kernel<32, 128, 1, 4, 3, PRE>), dim3((uint32_t)grid), dim3(256), 0, s, a);
+      hipLaunchKernelGGL((gg_blockscale_kernel<LAYOUT, 32, 128, 1, 4, 3, PRE>), dim3((uint32_t)grid), dim3(256), 0, s,
+                         a);
       return hipGetLastError();
     case 2:
+      if (LAYOUT != kStacked) return hipErrorInvalidValue;   // the persistent grid walks packed rows
       hipLaunchKernelGGL((gg_blockscale_persistent_kernel<128, 256, 2, 4, 3, PRE>), dim3((uint32_t)grid), dim3(512),
                          0, s, a);
       return hipGetLastError();
@@ -1762,8 +1781,14 @@ static hipError_t launch_blockscale(int config, const GemmArgs& a, int64_t grid,
   }
 }
 
-hipError_t launch_gemm_blockscale(int config, bool preshuffled, const GemmArgs& a, int64_t grid, hipStream_t s) {
-  return preshuffled ? launch_blockscale<true>(config, a, grid, s) : launch_blockscale<false>(config, a, grid, s);
+hipError_t launch_gemm_blockscale(int layout, int config, bool preshuffled, const GemmArgs& a, int64_t grid,
+                                  hipStream_t s) {
+  if (layout == kPadded)
+    return preshuffled ? launch_blockscale<kPadded, true>(config, a, grid, s)
+                       : launch_blockscale<kPadded, false>(config, a, grid, s);
+  if (layout != kStacked) return hipErrorInvalidValue;
+  return preshuffled ? launch_blockscale<kStacked, true>(config, a, grid, s)
+                     : launch_blockscale<kStacked, false>(config, a, grid, s);
 }
 
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t s) {

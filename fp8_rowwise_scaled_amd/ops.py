@@ -258,6 +258,47 @@ def f8f8bf16_groupwise_grouped_stacked_preshuffle(XQ, WQs, x_scale, w_scale, M_s
     return _groupwise("f8f8bf16_groupwise_grouped_stacked_preshuffle", XQ, WQs, x_scale, w_scale, M_sizes, out)
 
 
+def f8f8bf16_groupwise_grouped_dynamic(XQ, WQ, x_scale, w_scale, zero_start_index_M, zeroing_output_tensor=True,
+                                       out=None):
+    """Y [G, expected_m, N] bf16 for the padded layout with block scales: x_scale
+    [G, expected_m, K/128], w_scale [G, N/128, K/128] (see include/fp8gg.h)."""
+    return _groupwise_dynamic("f8f8bf16_groupwise_grouped_dynamic", XQ, WQ, x_scale, w_scale, zero_start_index_M,
+                              zeroing_output_tensor, out)
+
+
+def f8f8bf16_groupwise_grouped_dynamic_preshuffle(XQ, WQs, x_scale, w_scale, zero_start_index_M,
+                                                  zeroing_output_tensor=True, out=None):
+    """As the block-scaled padded op, with WQs produced by f8f8bf16_shuffle_b."""
+    return _groupwise_dynamic("f8f8bf16_groupwise_grouped_dynamic_preshuffle", XQ, WQs, x_scale, w_scale,
+                              zero_start_index_M, zeroing_output_tensor, out)
+
+
+def _groupwise_dynamic(fn_name, XQ, WQ, x_scale, w_scale, zero_start_index_M, zeroing_output_tensor, out):
+    XQ = _bytes(XQ, "XQ")
+    WQ = _bytes(WQ, "WQ")
+    if XQ.dim() != 3 or WQ.dim() != 3:
+        raise ValueError("XQ must be [G, expected_m, K] and WQ [G, N, K]")
+    G, em, K = XQ.shape
+    G2, N, K2 = WQ.shape
+    if G2 != G or K2 != K:
+        raise ValueError(f"shape mismatch: XQ {tuple(XQ.shape)} vs WQ {tuple(WQ.shape)}")
+    if K % 128 or N % 128:
+        raise ValueError(f"block scaling needs K and N to be multiples of 128 (N={N}, K={K})")
+    _check(XQ, "XQ", torch.uint8, (G, em, K))
+    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _check(x_scale, "x_scale", torch.float32, (G, em, K // 128))
+    _check(w_scale, "w_scale", torch.float32, (G, N // 128, K // 128))
+    _check(zero_start_index_M, "zero_start_index_M", torch.int64, (G,))
+    if out is None:
+        out = torch.empty((G, em, N), dtype=torch.bfloat16, device=XQ.device)
+    _check(out, "out", torch.bfloat16, (G, em, N))
+    st = getattr(_lib.load(), fn_name)(XQ.data_ptr(), WQ.data_ptr(), x_scale.data_ptr(), w_scale.data_ptr(),
+                                       zero_start_index_M.data_ptr(), out.data_ptr(), G, em, N, K,
+                                       int(bool(zeroing_output_tensor)), _stream(XQ.device))
+    _lib.check(st, fn_name)
+    return out
+
+
 def _groupwise(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out):
     XQ = _bytes(XQ, "XQ")
     WQ = _bytes(WQ, "WQ")

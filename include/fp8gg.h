@@ -257,6 +257,23 @@ fp8gg_status f8f8bf16_groupwise_grouped_stacked_preshuffle(
     const int64_t* M_sizes, uint16_t* Y,
     int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
 
+/* Block scaling in the padded ("dynamic") layout: XQ [G, expected_m, K], x_scale
+ * [G, expected_m, K / 128], w_scale [G, N / 128, K / 128], zero_start_index_M [G]
+ * (int64, on device, clamped to [0, expected_m]), Y [G, expected_m, N].  Rows of
+ * slab g at or past zero_start_index_M[g] are written as zero when
+ * zeroing_output_tensor is non-zero, else left untouched; K == 0 zero-fills Y.
+ * Same block sizes and shape rule as the stacked op; with WQs from
+ * f8f8bf16_shuffle_b in the _preshuffle sibling. */
+fp8gg_status f8f8bf16_groupwise_grouped_dynamic(
+    const uint8_t* XQ, const uint8_t* WQ, const float* x_scale, const float* w_scale,
+    const int64_t* zero_start_index_M, uint16_t* Y,
+    int64_t G, int64_t expected_m, int64_t N, int64_t K, int zeroing_output_tensor, void* stream);
+
+fp8gg_status f8f8bf16_groupwise_grouped_dynamic_preshuffle(
+    const uint8_t* XQ, const uint8_t* WQs, const float* x_scale, const float* w_scale,
+    const int64_t* zero_start_index_M, uint16_t* Y,
+    int64_t G, int64_t expected_m, int64_t N, int64_t K, int zeroing_output_tensor, void* stream);
+
 /*
  * Rearranges WQ [G, N, K] into the pre-shuffled order WQs (same size, must not
  * overlap WQ).  Byte layout: for group g, N-block nb (FP8GG_SHUFFLE_N rows) and

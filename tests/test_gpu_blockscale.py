@@ -167,3 +167,50 @@ def test_blockscale_long_k(F):
             sizes[g] = sel.size
             res = oracle.grouped_stacked_blockscale(w.XQ[sel], w.WQ, w.x_scale[sel], w.w_scale, sizes)
             P.assert_rows_match(got[sel], res, rms=P.rms_of(res.bits), label=f"long K cfg {cfg} group {g}")
+
+
+def _dynamic_inputs(zsi, em, N, K, seed):
+    """Padded-layout block-scaled inputs: every slab row drawn and quantised per
+    (row, 128) block, W per 128 x 128 block (the stacked generator, reshaped)."""
+    G = len(zsi)
+    w = wl.make_stacked_blockscale([em] * G, N, K, seed=seed)
+    return (w.XQ.reshape(G, em, K), w.WQ, w.x_scale.reshape(G, em, K // 128), w.w_scale,
+            np.asarray(zsi, np.int64))
+
+
+def run_dynamic(F, XQ, WQ, xs, ws, zsi, zeroing, pre=False):
+    G, em, _ = XQ.shape
+    whole, y = P.guarded_output((G, em, WQ.shape[1]))
+    fn = F.f8f8bf16_groupwise_grouped_dynamic_preshuffle if pre else F.f8f8bf16_groupwise_grouped_dynamic
+    Wd = F.f8f8bf16_shuffle_b(P.dev(WQ)) if pre else P.dev(WQ)
+    fn(P.dev(XQ), Wd, P.dev(xs), P.dev(ws), P.dev(zsi), zeroing_output_tensor=zeroing, out=y)
+    torch.cuda.synchronize()
+    P.check_guards(whole)
+    return P.bits_of(y)
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+@pytest.mark.parametrize("zeroing", [True, False])
+def test_dynamic_blockscale_matches_oracle(F, cfg, zeroing):
+    """Slabs of 200 rows (the last M tile overhangs the slab), valid counts 0, full,
+    37, past the slab (clamped) and 129, padding zeroed or left untouched."""
+    XQ, WQ, xs, ws, zsi = _dynamic_inputs([0, 200, 37, 205, 129], 200, 256, 384, seed=990)
+    with forced(cfg):
+        got = run_dynamic(F, XQ, WQ, xs, ws, zsi, zeroing)
+    res = oracle.grouped_dynamic_blockscale(XQ, WQ, xs, ws, zsi, zeroing)
+    P.assert_rows_match(got.reshape(-1, WQ.shape[1]), res, label=f"dynamic blockscale cfg {cfg} zeroing {zeroing}")
+
+
+@pytest.mark.parametrize("cfg", [0, 1])
+def test_dynamic_blockscale_bitwise_equal_stacked_on_compacted_rows_and_preshuffled(F, cfg):
+    XQ, WQ, xs, ws, zsi = _dynamic_inputs([3, 0, 130, 64], 160, 384, 512, seed=991)
+    G, em, K = XQ.shape
+    with forced(cfg):
+        d = run_dynamic(F, XQ, WQ, xs, ws, zsi, True)
+        dp = run_dynamic(F, XQ, WQ, xs, ws, zsi, True, pre=True)
+        rows = np.concatenate([g * em + np.arange(zsi[g]) for g in range(G)]).astype(np.int64)
+        y = F.f8f8bf16_groupwise_grouped_stacked(P.dev(XQ.reshape(G * em, K)[rows]), P.dev(WQ),
+                                                 P.dev(xs.reshape(G * em, -1)[rows]), P.dev(ws), P.dev(zsi))
+        torch.cuda.synchronize()
+    assert np.array_equal(dp, d)
+    assert np.array_equal(d.reshape(G * em, -1)[rows], P.bits_of(y))
