@@ -35,7 +35,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 WORKLOADS = ["moe_gate_up", "tiny_stacked", "dense_expert", "dense_expert_preshuffle", "padded_tails",
              "moe_gate_up_offsets", "dense_expert_batched", "moe_n_offsets", "moe_wgrad_k_offsets", "moe_gate_up_blockscale",
-             "moe_gate_up_blockscale_preshuffle"] + \
+             "moe_gate_up_blockscale_preshuffle", "padded_blockscale"] + \
     [f"moe_down_M{m}" for m in (1, 8, 32, 256, 2048, 8192)]
 
 
@@ -69,6 +69,8 @@ def make_workload(name):
         return wl.moe_gate_up_blockscale(), "blockscale", False
     if name == "moe_gate_up_blockscale_preshuffle":
         return wl.moe_gate_up_blockscale(), "blockscale", True
+    if name == "padded_blockscale":
+        return wl.padded_blockscale(), "padded_blockscale", False
     if name == "moe_n_offsets":
         return wl.moe_n_offsets(), "n_offsets", False
     if name == "moe_wgrad_k_offsets":
@@ -108,6 +110,14 @@ def algorithmic_work(w, layout):
         flop = 2 * N * K * R
         nbytes = R * K + g_ne * N * K + 4 * R * nkb + 4 * g_ne * (N // w.block_n) * nkb + 2 * N * R + 8 * G
         return flop, nbytes, R, g_ne
+    if layout == "padded_blockscale":
+        # padded slabs, zeroed padding rows written; block scales per (row, K block) and W block
+        em = w.expected_m
+        valid = np.clip(w.zero_start_index_M, 0, em)
+        R, g_ne, nkb = int(valid.sum()), int((valid > 0).sum()), K // 128
+        flop = 2 * N * K * R
+        nbytes = R * K + g_ne * N * K + 4 * R * nkb + 4 * g_ne * (N // 128) * nkb + 2 * N * G * em + 8 * G
+        return flop, nbytes, R, g_ne
     if layout in ("stacked", "offsets", "batched"):
         sizes = np.clip(w.M_sizes, 0, None)
         R = int(min(sizes.sum(), w.total_M))
@@ -136,7 +146,7 @@ GEMM_SOURCES = ("fp8gg_api.cpp", "fp8gg_internal.h", "fp8gg_kernels.hip")
 
 def group_meta(w, layout):
     """The workload's group metadata as a list (row counts, valid rows or offsets)."""
-    if layout == "padded":
+    if layout in ("padded", "padded_blockscale"):
         return w.zero_start_index_M.tolist()
     if layout == "n_offsets":
         return w.n_offsets.tolist()
@@ -191,6 +201,8 @@ def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=50):
             oracle.grouped_batched(w.XQ.reshape(w.G, M, w.K), w.WQ, w.x_scale.reshape(w.G, M), w.w_scale)
         elif layout == "blockscale":
             oracle.grouped_stacked_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
+        elif layout == "padded_blockscale":
+            oracle.grouped_dynamic_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.zero_start_index_M, True)
         elif layout == "n_offsets":
             oracle.grouped_n_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, w.n_offsets)
         elif layout == "k_offsets":
@@ -342,6 +354,8 @@ def main():
         meta = torch.from_numpy(offsets_of(w)).to(dev)
     elif layout == "blockscale":
         meta = torch.from_numpy(w.M_sizes).to(dev)
+    elif layout == "padded_blockscale":
+        meta = torch.from_numpy(w.zero_start_index_M).to(dev)
     elif layout == "batched":
         meta = torch.zeros(1, dtype=torch.int64, device=dev)   # the batched layout has no metadata
         Gb, Mb = w.G, w.total_M // w.G
@@ -356,6 +370,7 @@ def main():
         sets.append(tuple(t.clone() for t in sets[0]))
     out_shape = {"stacked": lambda: (w.total_M, w.N), "offsets": lambda: (w.total_M, w.N),
                  "blockscale": lambda: (w.total_M, w.N),
+                 "padded_blockscale": lambda: (w.G, w.expected_m, w.N),
                  "batched": lambda: (w.G, w.total_M // w.G, w.N), "n_offsets": lambda: (w.M, w.N),
                  "k_offsets": lambda: (w.G, w.M, w.N),
                  "padded": lambda: (w.G, w.expected_m, w.N)}[layout]()
@@ -371,6 +386,12 @@ def main():
         def call(i):
             s = sets[i % rotate]
             fn(s[0], s[1], s[2], s[3], s[4], out=outs[i % rotate])
+    elif layout == "padded_blockscale":
+        fn = F.f8f8bf16_groupwise_grouped_dynamic
+
+        def call(i):
+            s = sets[i % rotate]
+            fn(s[0], s[1], s[2], s[3], s[4], zeroing_output_tensor=True, out=outs[i % rotate])
     elif layout == "blockscale":
         fn = F.f8f8bf16_groupwise_grouped_stacked_preshuffle if pre else F.f8f8bf16_groupwise_grouped_stacked
 
@@ -452,7 +473,7 @@ def main():
             "layout": layout,
             "preshuffled": pre,
             "G": w.G,
-            "rows": int(w.G * w.expected_m if layout == "padded" else
+            "rows": int(w.G * w.expected_m if layout in ("padded", "padded_blockscale") else
                         (w.M if layout == "n_offsets" else (w.G * w.M if layout == "k_offsets" else w.total_M))),
             "valid_rows": R,
             "N": w.N,

@@ -449,3 +449,22 @@ def moe_gate_up_blockscale() -> StackedBlockscale:
     128 x 128 weight blocks and 1 x 128 activation blocks."""
     sizes = zipf_sizes(2002, 4096, 8)
     return make_stacked_blockscale(sizes, 4096, 7168, seed=8008, name="moe_gate_up_blockscale_G8_M4096_N4096_K7168")
+
+
+def make_dynamic_blockscale(zero_start_index_M, expected_m: int, N: int, K: int, seed: int, sigma: float = 1.0,
+                            name: str = "") -> Dynamic:
+    """Padded-layout inputs with block scales: every slab row drawn, X quantised per
+    (row, 128) block (x_scale [G, expected_m, K/128]) and each W[g] per 128 x 128
+    block (w_scale [G, N/128, K/128])."""
+    zsi = np.asarray(zero_start_index_M, dtype=np.int64)
+    G = int(zsi.shape[0])
+    w = make_stacked_blockscale([expected_m] * G, N, K, seed, sigma)
+    return Dynamic(w.XQ.reshape(G, expected_m, K), w.WQ, w.x_scale.reshape(G, expected_m, K // 128), w.w_scale,
+                   zsi, name)
+
+
+def padded_blockscale() -> Dynamic:
+    """The padded workload's slabs and valid rows (G=16, expected_m=512) with block
+    scales, at N=1024, K=7168 (whole 128-wide blocks)."""
+    z = padded_valid_rows(5005, 16, 512)
+    return make_dynamic_blockscale(z, 512, 1024, 7168, seed=9009, name="padded_blockscale_G16_em512_N1024_K7168")
