@@ -28,4 +28,5 @@ from .grouped_gemm import (  # noqa: F401
     stacked_row_groups,
 )
 from .quantize import e4m3fn_rne, quantize_rowwise  # noqa: F401,E402
-from .blockscale import grouped_dynamic_blockscale, grouped_stacked_blockscale  # noqa: F401,E402
+from .blockscale import (grouped_batched_blockscale, grouped_dynamic_blockscale,  # noqa: F401,E402
+                         grouped_offsets_blockscale, grouped_stacked_blockscale)

@@ -28,7 +28,7 @@ from __future__ import annotations
 import numpy as np
 
 from .grouped_gemm import (ROW_UNTOUCHED, ROW_WRITTEN, ROW_ZEROED, UNTOUCHED_SENTINEL, OracleResult,
-                           _accumulate, bf16_rne_from_f64, stacked_row_groups)
+                           _accumulate, bf16_rne_from_f64, offsets_row_groups, stacked_row_groups)
 
 
 def column_blocks(N: int, block_n: int) -> np.ndarray:
@@ -61,6 +61,31 @@ def grouped_stacked_blockscale(XQ, WQ, x_scale, w_scale, M_sizes, block_k: int =
     [total_M, K / block_k], w_scale [G, N / block_n, K / block_k], M_sizes [G]
     -> Y [total_M, N]; rows of no group untouched."""
     XQ = np.asarray(XQ, np.uint8)
+    return _packed_blockscale(XQ, WQ, x_scale, w_scale, stacked_row_groups(M_sizes, XQ.shape[0]), block_k, block_n)
+
+
+def grouped_offsets_blockscale(XQ, WQ, x_scale, w_scale, offsets, block_k: int = 128,
+                               block_n: int = 128) -> OracleResult:
+    """Offsets layout (int32 inclusive prefix of the group row counts) with block
+    scales; otherwise as grouped_stacked_blockscale."""
+    XQ = np.asarray(XQ, np.uint8)
+    return _packed_blockscale(XQ, WQ, x_scale, w_scale, offsets_row_groups(offsets, XQ.shape[0]), block_k, block_n)
+
+
+def grouped_batched_blockscale(XQ, WQ, x_scale, w_scale, block_k: int = 128, block_n: int = 128) -> OracleResult:
+    """Batched layout with block scales: XQ [G, M, K], x_scale [G, M, K / block_k],
+    every group a full slab of M rows -> Y [G, M, N] (flattened row classes)."""
+    XQ = np.asarray(XQ, np.uint8)
+    G, M, K = XQ.shape
+    owner = np.repeat(np.arange(G, dtype=np.int64), M)
+    res = _packed_blockscale(XQ.reshape(G * M, K), WQ, np.asarray(x_scale, np.float32).reshape(G * M, -1),
+                             w_scale, owner, block_k, block_n)
+    N = np.asarray(WQ).shape[1]
+    return OracleResult(res.values.reshape(G, M, N), res.bits.reshape(G, M, N), res.row_class)
+
+
+def _packed_blockscale(XQ, WQ, x_scale, w_scale, owner, block_k, block_n) -> OracleResult:
+    """Groups packed along M with block scales; owner[r] is the group of row r (-1: none)."""
     WQ = np.asarray(WQ, np.uint8)
     total_M, K = XQ.shape
     G, N, K2 = WQ.shape
@@ -74,7 +99,6 @@ def grouped_stacked_blockscale(XQ, WQ, x_scale, w_scale, M_sizes, block_k: int =
     if K == 0:
         return OracleResult(np.zeros((total_M, N)), np.zeros((total_M, N), np.uint16),
                             np.full(total_M, ROW_ZEROED, np.int8))
-    owner = stacked_row_groups(M_sizes, total_M)
     col_block = column_blocks(N, block_n)
     for g in range(G):
         rows = np.nonzero(owner == g)[0]

@@ -128,6 +128,23 @@ def test_dynamic_blockscale_padding_rows_are_zero_and_equal_stacked_on_compacted
     assert np.all(d.bits.reshape(G * em, N)[pad] == 0)
 
 
+def test_offsets_and_batched_blockscale_reduce_to_stacked():
+    """The offsets layout with offsets = the running sum of M_sizes, and the batched
+    layout with equal slabs, are the stacked layout on the same rows (the
+    stacked block-scaled oracle is the one pinned to the exact brute force)."""
+    bk, bn, N, K = 16, 4, 8, 48
+    sizes = np.array([3, 0, 5, 2])
+    XQ, WQ, xs, ws, _ = _problem(23, sizes, N, K, bk, bn, False)
+    st = oracle.grouped_stacked_blockscale(XQ, WQ, xs, ws, sizes, bk, bn)
+    of = oracle.grouped_offsets_blockscale(XQ, WQ, xs, ws, np.cumsum(sizes).astype(np.int32), bk, bn)
+    assert np.array_equal(st.bits, of.bits) and np.array_equal(st.row_class, of.row_class)
+    G, M = 3, 4
+    XQ, WQ, xs, ws, _ = _problem(24, [M] * G, N, K, bk, bn, False)
+    st = oracle.grouped_stacked_blockscale(XQ, WQ, xs, ws, [M] * G, bk, bn)
+    ba = oracle.grouped_batched_blockscale(XQ.reshape(G, M, K), WQ, xs.reshape(G, M, -1), ws, bk, bn)
+    assert np.array_equal(st.bits.reshape(G, M, N), ba.bits) and np.all(ba.row_class == oracle.ROW_WRITTEN)
+
+
 def _pins_pass():
     return all(_check(*c) for c in CASES) and _check_dynamic(21, [2, 0, 4, 9], 4, 6, 48, 16, 2, True)
 
