@@ -17,8 +17,12 @@ from ._lib import (  # noqa: F401
     plan,
 )
 from .ops import (  # noqa: F401
+    f8f8bf16_groupwise_grouped_batched,
+    f8f8bf16_groupwise_grouped_batched_preshuffle,
     f8f8bf16_groupwise_grouped_dynamic,
     f8f8bf16_groupwise_grouped_dynamic_preshuffle,
+    f8f8bf16_groupwise_grouped_offsets,
+    f8f8bf16_groupwise_grouped_offsets_preshuffle,
     f8f8bf16_groupwise_grouped_stacked,
     f8f8bf16_groupwise_grouped_stacked_preshuffle,
     f8f8bf16_rowwise_grouped_batched,

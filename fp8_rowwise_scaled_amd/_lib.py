@@ -36,6 +36,10 @@ EXPORTS = (
     "f8f8bf16_groupwise_grouped_stacked",
     "f8f8bf16_groupwise_grouped_stacked_preshuffle",
     "f8f8bf16_groupwise_grouped_dynamic",
+    "f8f8bf16_groupwise_grouped_offsets",
+    "f8f8bf16_groupwise_grouped_offsets_preshuffle",
+    "f8f8bf16_groupwise_grouped_batched",
+    "f8f8bf16_groupwise_grouped_batched_preshuffle",
     "f8f8bf16_groupwise_grouped_dynamic_preshuffle",
     "f8f8bf16_shuffle_b",
     "f8f8bf16_quantize_rowwise",
@@ -91,15 +95,18 @@ def load() -> ctypes.CDLL:
     lib.f8f8bf16_rowwise_grouped_n_offsets.argtypes = gemm + [P]
     lib.f8f8bf16_rowwise_grouped_k_offsets.argtypes = gemm + [P]
     lib.f8f8bf16_groupwise_grouped_stacked.argtypes = gemm + [P]
-    lib.f8f8bf16_groupwise_grouped_stacked.restype = I
     lib.f8f8bf16_groupwise_grouped_stacked_preshuffle.argtypes = gemm + [P]
     lib.f8f8bf16_groupwise_grouped_dynamic.argtypes = gemm + [I, P]
+    lib.f8f8bf16_groupwise_grouped_offsets.argtypes = gemm + [P]
+    lib.f8f8bf16_groupwise_grouped_offsets_preshuffle.argtypes = gemm + [P]
     lib.f8f8bf16_groupwise_grouped_dynamic_preshuffle.argtypes = gemm + [I, P]
     batched = [P, P, P, P, P, I64, I64, I64, I64, P]
     lib.f8f8bf16_rowwise_grouped_batched.argtypes = batched
     lib.f8f8bf16_rowwise_grouped_batched_preshuffle.argtypes = batched
+    lib.f8f8bf16_groupwise_grouped_batched.argtypes = batched
+    lib.f8f8bf16_groupwise_grouped_batched_preshuffle.argtypes = batched
     for name in EXPORTS:
-        if name.startswith("f8f8bf16_rowwise_grouped_"):
+        if name.startswith(("f8f8bf16_rowwise_grouped_", "f8f8bf16_groupwise_grouped_")):
             getattr(lib, name).restype = I
     lib.f8f8bf16_shuffle_b.argtypes = [P, P, I64, I64, I64, P]
     lib.f8f8bf16_shuffle_b.restype = I

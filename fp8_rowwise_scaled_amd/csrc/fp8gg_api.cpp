@@ -426,20 +426,24 @@ fp8gg_status f8f8bf16_rowwise_grouped_k_offsets(const uint8_t* XQ, const uint8_t
   return run(FP8GG_LAYOUT_K_OFFSETS, 0, XQ, WQ, x_scale, w_scale, k_offsets, Y, G, M, N, K, 0, stream);
 }
 
-// Block-scaled GEMM, stacked (meta = M_sizes, M = total_M) or padded (meta =
-// zero_start_index_M, M = expected_m, zeroing flag) layout.
+// Block-scaled GEMM: stacked (meta = int64 M_sizes, M = total_M), padded (meta =
+// int64 zero_start_index_M, M = expected_m, zeroing flag), offsets (meta = int32
+// inclusive prefix, M = total_M) or batched (no meta, M = slab height) layout.
 static fp8gg_status groupwise(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* WQ,
-                              const float* x_scale, const float* w_scale, const int64_t* meta, uint16_t* Y, int64_t G,
+                              const float* x_scale, const float* w_scale, const void* meta, uint16_t* Y, int64_t G,
                               int64_t M, int64_t N, int64_t K, int zeroing, void* stream) {
   constexpr int64_t B = 128;   // scale block along K and along N (whole pre-shuffle blocks too)
   const bool padded = layout == FP8GG_LAYOUT_PADDED;
+  const bool slabs = padded || layout == FP8GG_LAYOUT_BATCHED;
+  const bool has_meta = layout != FP8GG_LAYOUT_BATCHED;
+  const int64_t meta_elem = layout == FP8GG_LAYOUT_OFFSETS ? 4 : 8;
   fp8gg_status st = check_shape(layout, preshuffled, G, M, N, K);
   if (st != FP8GG_OK) return st;
   if (K % B != 0 || N % B != 0)
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE,
                 "block scaling needs K and N to be whole numbers of %lld-wide scale blocks (N=%lld K=%lld)",
                 (long long)B, (long long)N, (long long)K);
-  const int64_t rows = padded ? G * M : M;
+  const int64_t rows = slabs ? G * M : M;
   if (rows == 0 || N == 0) return ok();
   if (!Y) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y is null");
   if (!aligned(Y, 16)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y must be 16-byte aligned");
@@ -450,24 +454,26 @@ static fp8gg_status groupwise(int layout, int preshuffled, const uint8_t* XQ, co
     return ok();
   }
   if (G == 0) return ok();
-  if (!XQ || !WQ || !x_scale || !w_scale || !meta)
+  if (!XQ || !WQ || !x_scale || !w_scale || (has_meta && !meta))
     return fail(FP8GG_ERR_INVALID_ARGUMENT, "null input pointer");
-  if (!aligned(XQ, 16) || !aligned(WQ, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) || !aligned(meta, 8))
+  if (!aligned(XQ, 16) || !aligned(WQ, 16) || !aligned(x_scale, 4) || !aligned(w_scale, 4) ||
+      (has_meta && !aligned(meta, meta_elem)))
     return fail(FP8GG_ERR_INVALID_ARGUMENT,
-                "XQ and WQ must be 16-byte, x_scale and w_scale 4-byte and the row metadata 8-byte aligned");
+                "XQ and WQ must be 16-byte, x_scale and w_scale 4-byte and the row metadata %d-byte aligned",
+                (int)meta_elem);
   const Range out{Y, rows * N * 2, "Y"};
   const Range ins[] = {{XQ, rows * K, "XQ"},
                        {WQ, G * N * K, "WQ"},
                        {x_scale, rows * (K / B) * 4, "x_scale"},
                        {w_scale, G * (N / B) * (K / B) * 4, "w_scale"},
-                       {meta, G * 8, "row metadata"}};
+                       {has_meta ? meta : nullptr, G * meta_elem, "row metadata"}};
   for (const Range& r : ins)
     if (overlap(out, r)) return fail(FP8GG_ERR_INVALID_ARGUMENT, "Y overlaps %s", r.name);
 
   // 128 x 256 tiles, on the persistent grid (stacked layout only) from 256 rows per
   // group on average, as for rowwise scaling; one per workgroup from 64; 32 x 128
   // tiles below.  FP8GG_BS_CONFIG (0, 1 or 2) forces one for tests and tuning.
-  const int64_t per_group = padded ? M : (M + G - 1) / G;
+  const int64_t per_group = slabs ? M : (M + G - 1) / G;
   int cfg = (!padded && per_group >= 256) ? fp8gg::kBlockscalePersistent : (per_group >= 64 ? 0 : 1);
   const int forced = env_int("FP8GG_BS_CONFIG", -1);
   if (forced >= 0) {
@@ -481,8 +487,8 @@ static fp8gg_status groupwise(int layout, int preshuffled, const uint8_t* XQ, co
   a.W = WQ;
   a.xs = x_scale;
   a.ws = w_scale;
-  a.meta = meta;
-  a.offs = nullptr;
+  a.meta = layout == FP8GG_LAYOUT_STACKED || padded ? static_cast<const int64_t*>(meta) : nullptr;
+  a.offs = layout == FP8GG_LAYOUT_OFFSETS ? static_cast<const int32_t*>(meta) : nullptr;
   a.Y = Y;
   a.G = G;
   a.M = M;
@@ -490,6 +496,8 @@ static fp8gg_status groupwise(int layout, int preshuffled, const uint8_t* XQ, co
   a.K = K;
   if (padded) {
     a.m_tiles = (M + BM - 1) / BM;
+  } else if (layout == FP8GG_LAYOUT_BATCHED) {
+    a.m_tiles = G * ((M + BM - 1) / BM);   // exactly: every group a full slab
   } else {
     const int64_t ub = (M + BM - 1) / BM + G - 1;
     a.m_tiles = ub < M ? ub : M;
@@ -506,8 +514,7 @@ static fp8gg_status groupwise(int layout, int preshuffled, const uint8_t* XQ, co
     std::fprintf(stderr, "[fp8gg] groupwise layout=%d G=%lld M=%lld N=%lld K=%lld -> cfg=%d tile=%lldx%lld grid=%lld\n",
                  layout, (long long)G, (long long)M, (long long)N, (long long)K, cfg, (long long)BM, (long long)BN,
                  (long long)grid);
-  hipError_t e = fp8gg::launch_gemm_blockscale(padded ? fp8gg::kPadded : fp8gg::kStacked, cfg, preshuffled != 0, a,
-                                               grid, s);
+  hipError_t e = fp8gg::launch_gemm_blockscale(layout, cfg, preshuffled != 0, a, grid, s);
   if (e != hipSuccess) return fail(FP8GG_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   return ok();
 }
@@ -523,6 +530,31 @@ fp8gg_status f8f8bf16_groupwise_grouped_stacked_preshuffle(const uint8_t* XQ, co
                                                            int64_t G, int64_t total_M, int64_t N, int64_t K,
                                                            void* stream) {
   return groupwise(FP8GG_LAYOUT_STACKED, 1, XQ, WQs, x_scale, w_scale, M_sizes, Y, G, total_M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_groupwise_grouped_offsets(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                                const float* w_scale, const int32_t* offsets, uint16_t* Y, int64_t G,
+                                                int64_t total_M, int64_t N, int64_t K, void* stream) {
+  return groupwise(FP8GG_LAYOUT_OFFSETS, 0, XQ, WQ, x_scale, w_scale, offsets, Y, G, total_M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_groupwise_grouped_offsets_preshuffle(const uint8_t* XQ, const uint8_t* WQs,
+                                                           const float* x_scale, const float* w_scale,
+                                                           const int32_t* offsets, uint16_t* Y, int64_t G,
+                                                           int64_t total_M, int64_t N, int64_t K, void* stream) {
+  return groupwise(FP8GG_LAYOUT_OFFSETS, 1, XQ, WQs, x_scale, w_scale, offsets, Y, G, total_M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_groupwise_grouped_batched(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,
+                                                const float* w_scale, uint16_t* Y, int64_t G, int64_t M, int64_t N,
+                                                int64_t K, void* stream) {
+  return groupwise(FP8GG_LAYOUT_BATCHED, 0, XQ, WQ, x_scale, w_scale, nullptr, Y, G, M, N, K, 0, stream);
+}
+
+fp8gg_status f8f8bf16_groupwise_grouped_batched_preshuffle(const uint8_t* XQ, const uint8_t* WQs,
+                                                           const float* x_scale, const float* w_scale, uint16_t* Y,
+                                                           int64_t G, int64_t M, int64_t N, int64_t K, void* stream) {
+  return groupwise(FP8GG_LAYOUT_BATCHED, 1, XQ, WQs, x_scale, w_scale, nullptr, Y, G, M, N, K, 0, stream);
 }
 
 fp8gg_status f8f8bf16_groupwise_grouped_dynamic(const uint8_t* XQ, const uint8_t* WQ, const float* x_scale,

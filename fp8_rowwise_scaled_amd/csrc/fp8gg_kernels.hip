@@ -1276,9 +1276,10 @@ __device__ __forceinline__ void blockscale_tile(E& e, const GemmArgs& a, const T
   e.store_shuffled(a, t, n0, pk);
 }
 
-// One tile per workgroup; stacked layout, or padded (the group from the grid,
-// rows past the slab's valid count zeroed under the zeroing flag, whole-padding
-// tiles written as zeros without a K loop).
+// One tile per workgroup; the packed layouts (stacked, offsets, batched: the
+// group from the row metadata or the slab arithmetic), or padded (the group from
+// the grid, rows past the slab's valid count zeroed under the zeroing flag,
+// whole-padding tiles written as zeros without a K loop).
 template <int LAYOUT, int BM, int BN, int WM, int WN, int STAGES, bool PRE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gg_blockscale_kernel(GemmArgs a) {
@@ -1300,7 +1301,7 @@ gg_blockscale_kernel(GemmArgs a) {
       return;
     }
   } else {
-    if (!resolve_packed<kStacked, BM>(a, rest, t)) return;
+    if (!resolve_packed<LAYOUT, BM>(a, rest, t)) return;
   }
   E e;
   e.init(smem);
@@ -1311,7 +1312,7 @@ gg_blockscale_kernel(GemmArgs a) {
 // w + P, ..., then, when the last round is partial, its tiles as (BM/2) x (BN/2)
 // quarter tiles by the rule of the rowwise persistent kernel (tail_quarters), so a
 // partial round costs a fraction of a tile.  No pipelining across tiles.
-template <int BM, int BN, int WM, int WN, int STAGES, bool PRE>
+template <int LAYOUT, int BM, int BN, int WM, int WN, int STAGES, bool PRE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gg_blockscale_persistent_kernel(GemmArgs a) {
   typedef LdsTile<BM, BN, 128, WM, WN, STAGES, false, PRE> E;
@@ -1328,12 +1329,12 @@ gg_blockscale_persistent_kernel(GemmArgs a) {
 
   const int64_t P = gridDim.x;
   const int64_t w = blockIdx.x;
-  const int64_t T = count_m_tiles<kStacked, BM>(a) * a.n_tiles;
+  const int64_t T = count_m_tiles<LAYOUT, BM>(a) * a.n_tiles;
   const int64_t rem = tail_quarters(T, P, 0) ? T % P : 0;
   const int64_t whole = T - rem;
   for (int64_t tile = w; tile < whole; tile += P) {
     Tile t;
-    resolve_packed<kStacked, BM>(a, tile / a.n_tiles, t);
+    resolve_packed<LAYOUT, BM>(a, tile / a.n_tiles, t);
     E e;
     e.init(smem);
     blockscale_tile(e, a, t, (tile % a.n_tiles) * BN, sc, sc_dummy);
@@ -1342,7 +1343,7 @@ gg_blockscale_persistent_kernel(GemmArgs a) {
     const int64_t tile = whole + qn / 4;
     const int q = (int)(qn % 4);
     Tile t;
-    resolve_packed<kStacked, BM>(a, tile / a.n_tiles, t);
+    resolve_packed<LAYOUT, BM>(a, tile / a.n_tiles, t);
     t.row_base += (q >> 1) * (BM / 2);
     const int64_t n0 = (tile % a.n_tiles) * BN + (q & 1) * (BN / 2);
     if (t.row_base >= t.row_end || n0 >= a.N) continue;
@@ -1773,22 +1774,29 @@ static hipError_t launch_blockscale(int config, const GemmArgs& a, int64_t grid,
                          a);
       return hipGetLastError();
     case 2:
-      if (LAYOUT != kStacked) return hipErrorInvalidValue;   // the persistent grid walks packed rows
-      hipLaunchKernelGGL((gg_blockscale_persistent_kernel<128, 256, 2, 4, 3, PRE>), dim3((uint32_t)grid), dim3(512),
-                         0, s, a);
-      return hipGetLastError();
+      if constexpr (LAYOUT == kPadded) {
+        return hipErrorInvalidValue;   // the persistent grid walks packed rows only
+      } else {
+        hipLaunchKernelGGL((gg_blockscale_persistent_kernel<LAYOUT, 128, 256, 2, 4, 3, PRE>), dim3((uint32_t)grid),
+                           dim3(512), 0, s, a);
+        return hipGetLastError();
+      }
     default: return hipErrorInvalidValue;
   }
 }
 
 hipError_t launch_gemm_blockscale(int layout, int config, bool preshuffled, const GemmArgs& a, int64_t grid,
                                   hipStream_t s) {
-  if (layout == kPadded)
-    return preshuffled ? launch_blockscale<kPadded, true>(config, a, grid, s)
-                       : launch_blockscale<kPadded, false>(config, a, grid, s);
-  if (layout != kStacked) return hipErrorInvalidValue;
-  return preshuffled ? launch_blockscale<kStacked, true>(config, a, grid, s)
-                     : launch_blockscale<kStacked, false>(config, a, grid, s);
+  switch (layout) {
+#define FP8GG_BS_LAYOUT(L) \
+  case L: return preshuffled ? launch_blockscale<L, true>(config, a, grid, s) : launch_blockscale<L, false>(config, a, grid, s);
+    FP8GG_BS_LAYOUT(kStacked)
+    FP8GG_BS_LAYOUT(kPadded)
+    FP8GG_BS_LAYOUT(kOffsets)
+    FP8GG_BS_LAYOUT(kBatched)
+#undef FP8GG_BS_LAYOUT
+    default: return hipErrorInvalidValue;
+  }
 }
 
 hipError_t launch_zero_fill(uint16_t* Y, int64_t n_elems, hipStream_t s) {

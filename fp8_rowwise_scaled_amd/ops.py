@@ -299,7 +299,55 @@ def _groupwise_dynamic(fn_name, XQ, WQ, x_scale, w_scale, zero_start_index_M, ze
     return out
 
 
-def _groupwise(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out):
+def f8f8bf16_groupwise_grouped_offsets(XQ, WQ, x_scale, w_scale, offsets, out=None):
+    """Y [total_M, N] bf16 for the offsets layout (int32 inclusive prefix) with
+    block scales (see include/fp8gg.h)."""
+    return _groupwise("f8f8bf16_groupwise_grouped_offsets", XQ, WQ, x_scale, w_scale, offsets, out,
+                      "offsets", torch.int32)
+
+
+def f8f8bf16_groupwise_grouped_offsets_preshuffle(XQ, WQs, x_scale, w_scale, offsets, out=None):
+    """As the block-scaled offsets op, with WQs produced by f8f8bf16_shuffle_b."""
+    return _groupwise("f8f8bf16_groupwise_grouped_offsets_preshuffle", XQ, WQs, x_scale, w_scale, offsets, out,
+                      "offsets", torch.int32)
+
+
+def f8f8bf16_groupwise_grouped_batched(XQ, WQ, x_scale, w_scale, out=None):
+    """Y [G, M, N] bf16 for the batched layout with block scales: XQ [G, M, K],
+    x_scale [G, M, K/128], w_scale [G, N/128, K/128] (see include/fp8gg.h)."""
+    return _groupwise_batched("f8f8bf16_groupwise_grouped_batched", XQ, WQ, x_scale, w_scale, out)
+
+
+def f8f8bf16_groupwise_grouped_batched_preshuffle(XQ, WQs, x_scale, w_scale, out=None):
+    """As the block-scaled batched op, with WQs produced by f8f8bf16_shuffle_b."""
+    return _groupwise_batched("f8f8bf16_groupwise_grouped_batched_preshuffle", XQ, WQs, x_scale, w_scale, out)
+
+
+def _groupwise_batched(fn_name, XQ, WQ, x_scale, w_scale, out):
+    XQ = _bytes(XQ, "XQ")
+    WQ = _bytes(WQ, "WQ")
+    if XQ.dim() != 3 or WQ.dim() != 3:
+        raise ValueError("XQ must be [G, M, K] and WQ [G, N, K]")
+    G, M, K = XQ.shape
+    G2, N, K2 = WQ.shape
+    if G2 != G or K2 != K:
+        raise ValueError(f"shape mismatch: XQ {tuple(XQ.shape)} vs WQ {tuple(WQ.shape)}")
+    if K % 128 or N % 128:
+        raise ValueError(f"block scaling needs K and N to be multiples of 128 (N={N}, K={K})")
+    _check(XQ, "XQ", torch.uint8, (G, M, K))
+    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _check(x_scale, "x_scale", torch.float32, (G, M, K // 128))
+    _check(w_scale, "w_scale", torch.float32, (G, N // 128, K // 128))
+    if out is None:
+        out = torch.empty((G, M, N), dtype=torch.bfloat16, device=XQ.device)
+    _check(out, "out", torch.bfloat16, (G, M, N))
+    st = getattr(_lib.load(), fn_name)(XQ.data_ptr(), WQ.data_ptr(), x_scale.data_ptr(), w_scale.data_ptr(),
+                                       out.data_ptr(), G, M, N, K, _stream(XQ.device))
+    _lib.check(st, fn_name)
+    return out
+
+
+def _groupwise(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out, meta_name="M_sizes", meta_dtype=torch.int64):
     XQ = _bytes(XQ, "XQ")
     WQ = _bytes(WQ, "WQ")
     if XQ.dim() != 2 or WQ.dim() != 3:
@@ -314,7 +362,7 @@ def _groupwise(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out):
     _check(WQ, "WQ", torch.uint8, (G, N, K))
     _check(x_scale, "x_scale", torch.float32, (total_M, K // 128))
     _check(w_scale, "w_scale", torch.float32, (G, N // 128, K // 128))
-    _check(M_sizes, "M_sizes", torch.int64, (G,))
+    _check(M_sizes, meta_name, meta_dtype, (G,))
     if out is None:
         out = torch.empty((total_M, N), dtype=torch.bfloat16, device=XQ.device)
     _check(out, "out", torch.bfloat16, (total_M, N))

@@ -257,6 +257,28 @@ fp8gg_status f8f8bf16_groupwise_grouped_stacked_preshuffle(
     const int64_t* M_sizes, uint16_t* Y,
     int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
 
+/* Block scaling in the offsets layout (int32 inclusive prefix of the group row
+ * counts, clamped as for f8f8bf16_rowwise_grouped_offsets) and in the batched
+ * layout (XQ [G, M, K], x_scale [G, M, K / 128], Y [G, M, N], every row valid, no
+ * metadata).  Scales, block sizes and shape rule as for the stacked op. */
+fp8gg_status f8f8bf16_groupwise_grouped_offsets(
+    const uint8_t* XQ, const uint8_t* WQ, const float* x_scale, const float* w_scale,
+    const int32_t* offsets, uint16_t* Y,
+    int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
+
+fp8gg_status f8f8bf16_groupwise_grouped_offsets_preshuffle(
+    const uint8_t* XQ, const uint8_t* WQs, const float* x_scale, const float* w_scale,
+    const int32_t* offsets, uint16_t* Y,
+    int64_t G, int64_t total_M, int64_t N, int64_t K, void* stream);
+
+fp8gg_status f8f8bf16_groupwise_grouped_batched(
+    const uint8_t* XQ, const uint8_t* WQ, const float* x_scale, const float* w_scale,
+    uint16_t* Y, int64_t G, int64_t M, int64_t N, int64_t K, void* stream);
+
+fp8gg_status f8f8bf16_groupwise_grouped_batched_preshuffle(
+    const uint8_t* XQ, const uint8_t* WQs, const float* x_scale, const float* w_scale,
+    uint16_t* Y, int64_t G, int64_t M, int64_t N, int64_t K, void* stream);
+
 /* Block scaling in the padded ("dynamic") layout: XQ [G, expected_m, K], x_scale
  * [G, expected_m, K / 128], w_scale [G, N / 128, K / 128], zero_start_index_M [G]
  * (int64, on device, clamped to [0, expected_m]), Y [G, expected_m, N].  Rows of

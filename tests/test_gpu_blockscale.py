@@ -214,3 +214,38 @@ def test_dynamic_blockscale_bitwise_equal_stacked_on_compacted_rows_and_preshuff
         torch.cuda.synchronize()
     assert np.array_equal(dp, d)
     assert np.array_equal(d.reshape(G * em, -1)[rows], P.bits_of(y))
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2])
+def test_offsets_and_batched_blockscale_bitwise_equal_stacked(F, cfg):
+    """The offsets layout (int32 prefix of the same row counts) and the batched
+    layout (equal slabs) run the stacked layout's tiles and K order: bit-identical
+    results on the same rows, for every configuration; and the oracle within the
+    tolerance."""
+    w = wl.make_stacked_blockscale([0, 3, 130, 257], 384, 640, seed=995)
+    offs = P.dev(np.cumsum(w.M_sizes).astype(np.int32))
+    with forced(cfg):
+        st = run(F, w, w.total_M)
+        whole, y = P.guarded_output((w.total_M, w.N))
+        F.f8f8bf16_groupwise_grouped_offsets(P.dev(w.XQ), P.dev(w.WQ), P.dev(w.x_scale), P.dev(w.w_scale), offs,
+                                             out=y)
+        torch.cuda.synchronize()
+        P.check_guards(whole)
+        of = P.bits_of(y)
+    assert np.array_equal(of, st)
+    res = oracle.grouped_offsets_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, np.cumsum(w.M_sizes).astype(np.int32))
+    P.assert_rows_match(of, res, label=f"offsets blockscale cfg {cfg}")
+
+    G, M = 3, 150
+    b = wl.make_stacked_blockscale([M] * G, 256, 512, seed=996)
+    with forced(cfg):
+        st = run(F, b, b.total_M)
+        whole, y = P.guarded_output((G, M, b.N))
+        F.f8f8bf16_groupwise_grouped_batched(P.dev(b.XQ.reshape(G, M, -1)), P.dev(b.WQ),
+                                             P.dev(b.x_scale.reshape(G, M, -1)), P.dev(b.w_scale), out=y)
+        torch.cuda.synchronize()
+        P.check_guards(whole)
+        ba = P.bits_of(y)
+    assert np.array_equal(ba.reshape(G * M, -1), st)
+    res = oracle.grouped_batched_blockscale(b.XQ.reshape(G, M, -1), b.WQ, b.x_scale.reshape(G, M, -1), b.w_scale)
+    P.assert_rows_match(ba.reshape(G * M, -1), res, label=f"batched blockscale cfg {cfg}")
