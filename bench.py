@@ -33,7 +33,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 MALL_BYTES = 256 * 2 ** 20    # Infinity Cache
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
-WORKLOADS = ["moe_gate_up", "tiny_stacked", "dense_expert", "dense_expert_preshuffle", "padded_tails",
+WORKLOADS = ["moe_gate_up", "moe_gate_up_preshuffle", "tiny_stacked", "dense_expert", "dense_expert_preshuffle", "padded_tails",
              "moe_gate_up_offsets", "dense_expert_batched", "moe_n_offsets", "moe_wgrad_k_offsets", "moe_gate_up_blockscale",
              "moe_gate_up_blockscale_preshuffle", "padded_blockscale"] + \
     [f"moe_down_M{m}" for m in (1, 8, 32, 256, 2048, 8192)]
@@ -47,6 +47,10 @@ def make_workload(name):
     import workloads as wl
     if name == "moe_gate_up":
         return wl.moe_gate_up(), "stacked", False
+    if name == "moe_gate_up_preshuffle":
+        w = wl.moe_gate_up()
+        w.name += "_preshuffle"
+        return w, "stacked", True
     if name == "tiny_stacked":
         return wl.tiny_stacked(), "stacked", False
     if name == "dense_expert":
