@@ -312,7 +312,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="moe_gate_up", choices=WORKLOADS)
+    ap.add_argument("--workload", default="moe_gate_up_preshuffle", choices=WORKLOADS)
     ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate over (0 = automatic)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-small-m", action="store_true", help="skip the graph-replayed small-M timings")
@@ -488,7 +488,7 @@ def main():
         },
         "roofline": roof,
     }
-    if not args.no_small_m and args.workload == "moe_gate_up":
+    if not args.no_small_m and args.workload in ("moe_gate_up", "moe_gate_up_preshuffle"):
         result["small_m"] = small_m_us_per_call(F, torch)
         result["quantize"] = quantize_us_per_call(F, torch)
     if not args.no_cpu_baseline:
