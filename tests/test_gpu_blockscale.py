@@ -249,3 +249,13 @@ def test_offsets_and_batched_blockscale_bitwise_equal_stacked(F, cfg):
     assert np.array_equal(ba.reshape(G * M, -1), st)
     res = oracle.grouped_batched_blockscale(b.XQ.reshape(G, M, -1), b.WQ, b.x_scale.reshape(G, M, -1), b.w_scale)
     P.assert_rows_match(ba.reshape(G * M, -1), res, label=f"batched blockscale cfg {cfg}")
+
+
+@pytest.mark.parametrize("cfg", [2, 3])
+def test_blockscale_forced_config_refusals(F, cfg):
+    """The persistent configuration (2) walks packed rows only, so the padded
+    layout refuses it before any launch; configuration 3 does not exist."""
+    XQ, WQ, xs, ws, zsi = _dynamic_inputs([3, 5], 64, 128, 256, seed=995)
+    with forced(cfg):
+        with pytest.raises(ValueError, match="not a configuration"):
+            run_dynamic(F, XQ, WQ, xs, ws, zsi, True)
