@@ -321,7 +321,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (this build has no "
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the library has no "
               "multi-GPU path; the grouped GEMM shards by expert group, one process per GPU).", file=sys.stderr)
         sys.exit(2)
 
