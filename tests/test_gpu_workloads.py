@@ -72,8 +72,14 @@ def check_stacked_full_size(F, w, cols=None, pre=False, per_group=10, seed=0):
     return out
 
 
-def test_gate_up_full_size(F):
-    check_stacked_full_size(F, wl.moe_gate_up(), seed=1)
+def test_gate_up_full_size_plain_and_preshuffled(F):
+    """The bench workload through both entry points (the bench times the
+    pre-shuffled one): every column of sampled rows against the oracle, and the two
+    outputs equal bit for bit (same tiles, same K order)."""
+    w = wl.moe_gate_up()
+    plain = check_stacked_full_size(F, w, seed=1)
+    pre = check_stacked_full_size(F, w, pre=True, seed=1)
+    assert torch.equal(plain.view(torch.int16), pre.view(torch.int16)), "pre-shuffled differs from plain"
 
 
 @pytest.mark.parametrize("total_M", wl.DOWN_PROJ_TOTAL_M)
