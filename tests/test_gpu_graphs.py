@@ -2,9 +2,11 @@
 
 Every call only enqueues kernels on the caller's stream (no allocation, copy,
 memset or synchronisation), so a sequence of calls can be captured into one HIP
-graph.  The graph here holds an n_offsets, a k_offsets, a block-scaled and a
-quantiser call; it is replayed several times with eager work on other buffers
-in between, and every replay must reproduce the eager results bit for bit.
+graph.  The graphs here hold an n_offsets, a k_offsets, a block-scaled and a
+quantiser call, and a pre-shuffled stacked call (persistent grid) with a padded
+call that zeroes its padding rows; each is replayed several times with eager work
+on other buffers in between, and every replay must reproduce the eager results
+bit for bit.
 """
 import numpy as np
 import pytest
@@ -76,5 +78,53 @@ def test_new_entry_points_under_graph_replay(F):
         g.replay()
         torch.cuda.synchronize()
         for name, o, e in zip(("n_offsets", "k_offsets", "blockscale", "codes", "scales"), outs, eager):
+            assert torch.equal(o.view(torch.uint8), e.view(torch.uint8)), \
+                f"replay {rep}: {name} differs from the eager result"
+
+
+def test_preshuffled_and_padded_entry_points_under_graph_replay(F):
+    # stacked, 354 rows per group on average: the persistent grid on pre-shuffled W
+    st = wl.make_stacked([600, 0, 517, 300], 512, 1024, seed=1410)
+    # padded slabs of 200 rows, valid counts 0, 64, full and 129, padding zeroed
+    dy = wl.make_dynamic([0, 64, 200, 129], 200, 384, 640, seed=1411)
+    sin = [P.dev(a) for a in (st.XQ, st.WQ, st.x_scale, st.w_scale, st.M_sizes)]
+    sin[1] = F.f8f8bf16_shuffle_b(sin[1])          # once, as at weight load
+    din = [P.dev(a) for a in (dy.XQ, dy.WQ, dy.x_scale, dy.w_scale, dy.zero_start_index_M)]
+    ys = torch.empty((st.total_M, st.N), dtype=torch.bfloat16, device="cuda")
+    yd = torch.empty((dy.XQ.shape[0], dy.XQ.shape[1], dy.WQ.shape[1]), dtype=torch.bfloat16, device="cuda")
+    outs = (ys, yd)
+    assert F.plan(F.LAYOUT_STACKED, True, 4, st.total_M, st.N, st.K)["persistent"] == 1
+
+    def calls():
+        F.f8f8bf16_rowwise_grouped_stacked_preshuffle(*sin, out=ys)
+        F.f8f8bf16_rowwise_grouped_dynamic(*din, zeroing_output_tensor=True, out=yd)
+
+    def reset():
+        for o in outs:
+            o.view(torch.uint8).fill_(0xC1)
+
+    reset()
+    calls()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    assert bool((yd[0].view(torch.int16) == 0).all()), "the empty slab's padding was not zeroed"
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        calls()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        calls()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for rep in range(3):
+        reset()
+        scratch.add_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, o, e in zip(("stacked_preshuffle", "dynamic"), outs, eager):
             assert torch.equal(o.view(torch.uint8), e.view(torch.uint8)), \
                 f"replay {rep}: {name} differs from the eager result"
