@@ -48,6 +48,13 @@ def e4m3fn_rne(y: np.ndarray) -> np.ndarray:
     return (code | np.where(np.signbit(y), np.uint8(0x80), np.uint8(0))).astype(np.uint8)
 
 
+def row_quotient(x: np.ndarray, s: np.ndarray) -> np.ndarray:
+    """y[r, k] = x[r, k] / s[r]: one correctly rounded fp32 IEEE division per
+    element (not a multiplication by a rounded reciprocal, which differs in the
+    last bit for some inputs and so changes some codes)."""
+    return (np.asarray(x, np.float32) / np.asarray(s, np.float32)[:, None]).astype(np.float32)
+
+
 def quantize_rowwise(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     """x_bits: uint16 bf16 patterns [rows, K] -> (codes uint8 [rows, K], scales
     float32 [rows])."""
@@ -58,6 +65,6 @@ def quantize_rowwise(x_bits: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
     amax = np.nanmax(np.abs(x), axis=1).astype(np.float32)
     s = (amax / E4M3_MAX).astype(np.float32)
     s = np.where(amax == 0, np.float32(1.0), s).astype(np.float32)
-    y = (x / s[:, None]).astype(np.float32)
+    y = row_quotient(x, s)
     y = np.where(y > E4M3_MAX, E4M3_MAX, np.where(y < -E4M3_MAX, -E4M3_MAX, y)).astype(np.float32)
     return e4m3fn_rne(y), s

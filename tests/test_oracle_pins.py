@@ -86,6 +86,58 @@ def test_bf16_golden_cases():
     assert n >= 15
 
 
+def test_bf16_ulp_golden_cases():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "bf16_ulp_cases.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        x_s, u_s = line.split()[:2]
+        got = float(oracle.bf16_ulp(np.array([float.fromhex(x_s)]))[0])
+        assert got == float.fromhex(u_s), (x_s, got.hex(), u_s)
+        n += 1
+    assert n >= 10
+
+
+def _bf16_values_torch(bits):
+    """bf16 bit patterns -> fp64 through torch's own bfloat16 type (not the oracle's
+    bit shift)."""
+    b = torch.from_numpy(np.asarray(bits, np.uint16).view(np.int16).copy())
+    return b.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def test_bf16_ulp_equals_successor_spacing():
+    """bf16_ulp(|x|) is the distance between consecutive bf16 numbers around |x|:
+    for every positive finite pattern b, the gap v(b + 1) - v(b) (values decoded by
+    torch) must equal bf16_ulp at v(b), at random points strictly inside [v(b),
+    v(b + 1)) and at -v(b); and above 2^-126 it must equal 2^16 times numpy's fp32
+    spacing (fp32 has 16 more fraction bits)."""
+    b = np.arange(0x0000, 0x7F7F, dtype=np.uint16)           # 0 .. the largest finite - 1
+    v = _bf16_values_torch(b)
+    gap = _bf16_values_torch(b + 1) - v
+    assert np.array_equal(oracle.bf16_ulp(v), gap)
+    assert np.array_equal(oracle.bf16_ulp(-v), gap)
+    rng = np.random.default_rng(60)
+    inside = v + gap * rng.uniform(0.0, 1.0, v.size)
+    inside = np.where(inside < v + gap, inside, v)            # stay inside the half-open gap
+    assert np.array_equal(oracle.bf16_ulp(inside), gap)
+    normal = v >= 2.0 ** -126
+    f32_step = np.spacing(v[normal].astype(np.float32)).astype(np.float64) * 2.0 ** 16
+    assert np.array_equal(oracle.bf16_ulp(v[normal]), f32_step)
+
+
+def test_planted_ulp_mistake_is_caught(monkeypatch):
+    """A doubled ulp (it would silently widen every GPU tolerance) trips the pins."""
+    orig = og.bf16_ulp
+    for wrong in (lambda x: 2.0 * orig(x), lambda x: 0.5 * orig(x)):
+        monkeypatch.setattr(og, "bf16_ulp", wrong)
+        monkeypatch.setattr(oracle, "bf16_ulp", wrong)
+        with pytest.raises(AssertionError):
+            test_bf16_ulp_equals_successor_spacing()
+        with pytest.raises(AssertionError):
+            test_bf16_ulp_golden_cases()
+
+
 def test_bf16_matches_torch_on_fp32_inputs():
     rng = np.random.default_rng(7)
     u = rng.integers(0, 2 ** 32, size=200_000, dtype=np.uint64).astype(np.uint32)
@@ -788,3 +840,57 @@ def test_planted_truncation_in_quantiser_is_caught(monkeypatch):
     monkeypatch.setattr(oracle, "e4m3fn_rne", truncate)
     with pytest.raises(AssertionError):
         test_e4m3fn_rne_matches_torch_cast()
+
+
+def _torch_quantize_rowwise(x_bits):
+    """The amax/448 rowwise quantisation composed from torch's own CPU operations:
+    fp32 amax and scale, torch's fp32 division, clamp to +-448, torch's cast to
+    float8_e4m3fn."""
+    x = torch.from_numpy(np.asarray(x_bits, np.uint16).view(np.int16).copy()).view(torch.bfloat16).float()
+    amax = x.abs().amax(dim=1)
+    s = amax / 448.0
+    s = torch.where(amax == 0, torch.ones_like(s), s)
+    y = torch.clamp(x / s[:, None], -448.0, 448.0)
+    return y.to(torch.float8_e4m3fn).view(torch.uint8).numpy(), s.numpy()
+
+
+def _quantize_pin_inputs():
+    """About 1M bf16 values: N(0, 1) rows under scales 2^-8 .. 2^8, rows whose
+    largest magnitude sits in the subnormal-scale range, a zero row, a single
+    non-zero entry, signed zeros."""
+    rng = np.random.default_rng(61)
+    rows, K = 2048, 512
+    x = rng.standard_normal((rows, K)).astype(np.float32)
+    x *= (2.0 ** rng.uniform(-8, 8, (rows, 1))).astype(np.float32)
+    x[0] = 0.0
+    x[1] = 0.0
+    x[1, 7] = -3.5
+    x[2, ::2] = -0.0
+    x[3] *= np.float32(2.0 ** -120)
+    return _bf16_bits(x)
+
+
+def test_quantize_rowwise_matches_torch_composition():
+    """Codes and scales equal, bit for bit, a composition of torch's own fp32
+    division, clamp and e4m3fn cast on ~1M values ([MSLK-471], Design notes: one
+    scale per row, constant along K)."""
+    bits = _quantize_pin_inputs()
+    q, s = oracle.quantize_rowwise(bits)
+    q_t, s_t = _torch_quantize_rowwise(bits)
+    assert np.array_equal(s.view(np.uint32), s_t.view(np.uint32))
+    assert np.array_equal(q, q_t)
+
+
+def test_planted_reciprocal_quotient_is_caught(monkeypatch):
+    """x * (1 / s) rounds twice and changes some codes: the torch composition pin
+    catches it."""
+    from oracle import quantize as oq
+
+    def reciprocal(x, s):
+        with np.errstate(over="ignore"):   # 1 / s overflows for the subnormal-scale row
+            r = (np.float32(1.0) / np.asarray(s, np.float32)).astype(np.float32)
+        return (np.asarray(x, np.float32) * r[:, None]).astype(np.float32)
+
+    monkeypatch.setattr(oq, "row_quotient", reciprocal)
+    with pytest.raises(AssertionError):
+        test_quantize_rowwise_matches_torch_composition()
