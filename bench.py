@@ -7,11 +7,18 @@ A step is one call of the grouped GEMM (group resolution, K loop, scaled
 epilogue) over one batch of the workload's inputs, which are resident in HBM
 before timing starts.  Prints ONE JSON line on stdout; diagnostics go to stderr.
 
-Timing: W untimed warm-up calls, then exactly K timed calls bracketed by device
-synchronisation.  Each call is also bracketed by HIP events recorded on the
-stream the kernel runs on, which gives the kernel's average duration for the
-roofline figure.  When a workload's bytes are small against the 256 MB
-Infinity Cache, calls rotate over several copies of the inputs.
+The default workload is the dense expert (G=4, 512 rows per group, N=8192,
+K=28672) through the pre-shuffled-weight entry point (weights shuffled once
+before timing, as at weight load).
+
+Timing: a clock ramp (at least 0.5 s of untimed calls, synchronised in small
+batches, so that the GPU clock has settled), W counted untimed warm-up calls,
+then exactly K timed calls bracketed by device synchronisation.  Each call is
+also bracketed by HIP events recorded on the stream the kernel runs on, which
+gives the kernel's average duration for the roofline figure.  When a workload's
+bytes are small against the 256 MB Infinity Cache, calls rotate over several
+copies of the inputs.  Decode-sized calls (the down-projection sweep) are timed
+under graph replay.
 """
 from __future__ import annotations
 
@@ -183,169 +190,124 @@ def measured_traffic(workload, src_hash):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=50):
-    """The oracle as it stands, on the full workload, on this host's cores: whole
-    calls repeated until about min_seconds of CPU work (at most max_runs calls)."""
-    import oracle
+def _blas_info():
+    """(vendor, threads) of numpy's BLAS as threadpoolctl reports it."""
     try:
         from threadpoolctl import threadpool_info
-        threads = max((i.get("num_threads") or 1) for i in threadpool_info()) if threadpool_info() else 1
+        for i in threadpool_info():
+            if i.get("user_api") == "blas":
+                return f"{i.get('internal_api')} {i.get('version')}", int(i.get("num_threads") or 1)
     except Exception:  # pragma: no cover
-        threads = os.cpu_count() or 1
+        pass
+    return "unknown", 1
+
+
+def _oracle_call(w, layout):
+    import oracle
+    if layout == "stacked":
+        oracle.grouped_stacked(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
+    elif layout == "offsets":
+        oracle.grouped_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, offsets_of(w))
+    elif layout == "batched":
+        M = w.total_M // w.G
+        oracle.grouped_batched(w.XQ.reshape(w.G, M, w.K), w.WQ, w.x_scale.reshape(w.G, M), w.w_scale)
+    elif layout == "blockscale":
+        oracle.grouped_stacked_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
+    elif layout == "padded_blockscale":
+        oracle.grouped_dynamic_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.zero_start_index_M, True)
+    elif layout == "n_offsets":
+        oracle.grouped_n_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, w.n_offsets)
+    elif layout == "k_offsets":
+        oracle.grouped_k_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, w.k_offsets)
+    else:
+        oracle.grouped_dynamic(w.XQ, w.WQ, w.x_scale, w.w_scale, w.zero_start_index_M, True)
+
+
+def cpu_baseline(w, layout, flop, min_seconds=10.0, max_runs=50, single_thread=True):
+    """The oracle as it stands on this host's cores: whole calls of the workload
+    repeated until about min_seconds of CPU work (at least one call), with numpy's
+    BLAS on every core of the process's affinity mask; then, single-threaded, the
+    tiny workload and the down projection at total_M = 1, 8, 32."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    vendor, blas_threads = _blas_info()
     times = []
     t_all = time.perf_counter()
     while len(times) < max_runs and (time.perf_counter() - t_all) < min_seconds:
         t0 = time.perf_counter()
-        if layout == "stacked":
-            oracle.grouped_stacked(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
-        elif layout == "offsets":
-            oracle.grouped_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, offsets_of(w))
-        elif layout == "batched":
-            M = w.total_M // w.G
-            oracle.grouped_batched(w.XQ.reshape(w.G, M, w.K), w.WQ, w.x_scale.reshape(w.G, M), w.w_scale)
-        elif layout == "blockscale":
-            oracle.grouped_stacked_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
-        elif layout == "padded_blockscale":
-            oracle.grouped_dynamic_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.zero_start_index_M, True)
-        elif layout == "n_offsets":
-            oracle.grouped_n_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, w.n_offsets)
-        elif layout == "k_offsets":
-            oracle.grouped_k_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, w.k_offsets)
-        else:
-            oracle.grouped_dynamic(w.XQ, w.WQ, w.x_scale, w.w_scale, w.zero_start_index_M, True)
+        _oracle_call(w, layout)
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
-    return {"value": round(flop / med / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"the full workload, {len(times)} whole call(s) over {sum(times):.1f} s, "
-                      f"median {med:.3f} s per call "
-                      "(e4m3fn table decode, fp64 matmul per group, fp64 scales, bf16 RNE)"}
-
-
-def small_m_us_per_call(F, torch, totals=(1, 8, 32), calls_per_graph=64, replays=20):
-    """µs per call of the down-proj workload at small total_M, timed as the pages time
-    decode-sized GEMMs: many calls captured in one HIP graph (rotating over enough
-    input copies to defeat the Infinity Cache), replayed, divided by the call count."""
-    import workloads as wl
-    out = {}
-    dev = torch.device("cuda", 0)
-    for m in totals:
-        w = wl.moe_down(m)
-        _, nbytes, _, _ = algorithmic_work(w, "stacked")
-        rot = max(1, min(64, math.ceil(2 * MALL_BYTES / max(nbytes, 1))))
-        base = [torch.from_numpy(a).to(dev) for a in (w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)]
-        sets = [base] + [[t.clone() for t in base] for _ in range(rot - 1)]
-        outs = [torch.empty((w.total_M, w.N), dtype=torch.bfloat16, device=dev) for _ in range(rot)]
-
-        def calls():
-            for i in range(calls_per_graph):
-                s_ = sets[i % rot]
-                F.f8f8bf16_rowwise_grouped_stacked(*s_, out=outs[i % rot])
-        calls()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            calls()
-        for _ in range(3):
-            g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(replays):
-            g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (replays * calls_per_graph)
-        out[f"moe_down_M{m}"] = {"us_per_call": round(us, 3), "GB_per_s": round(nbytes / us / 1e3, 1),
-                                 "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4), "input_copies": rot}
-        log(f"small M: {w.name}: {us:.2f} us/call under graph replay ({nbytes / us / 1e3:.0f} GB/s, "
-            f"{rot} input copies)")
-        del sets, outs, base, g
+    out = {"value": round(flop / med / 1e12, 6), "unit": "TFLOP/s", "cores": int(blas_threads), "kind": "oracle",
+           "sample": f"the full workload, {len(times)} whole call(s) over {sum(times):.1f} s, "
+                     f"median {med:.3f} s per call "
+                     "(e4m3fn table decode, fp64 matmul per group, fp64 scales, bf16 RNE)",
+           "affinity_cores": cores, "blas": vendor, "s_per_call": round(med, 4)}
+    if single_thread:
+        import workloads as wl
+        from threadpoolctl import threadpool_limits
+        st = {}
+        with threadpool_limits(limits=1):
+            for name, make in [("tiny_stacked", wl.tiny_stacked)] + \
+                    [(f"moe_down_M{m}", lambda m=m: wl.moe_down(m)) for m in (1, 8, 32)]:
+                wx = make()
+                runs = []
+                t_all = time.perf_counter()
+                while len(runs) < 5 and (time.perf_counter() - t_all) < 3.0:
+                    t0 = time.perf_counter()
+                    _oracle_call(wx, "stacked")
+                    runs.append(time.perf_counter() - t0)
+                st[name] = {"s_per_call": round(statistics.median(runs), 5), "calls": len(runs)}
+        out["single_thread"] = st
+        log("CPU oracle, one thread: " + ", ".join(f"{k} {v['s_per_call'] * 1e3:.1f} ms" for k, v in st.items()))
+    log(f"CPU oracle: {out['value']:.4f} TFLOP/s, {med:.2f} s per call, BLAS {vendor} on {blas_threads} threads, "
+        f"{cores} cores in the affinity mask")
     return out
 
 
-def quantize_us_per_call(F, torch, rows=4096, K=7168, calls=200):
-    """The rowwise activation quantiser (bf16 [rows, K] -> e4m3fn codes + fp32 row
-    scales) on the gate_up activations' shape, rotating over enough input copies to
-    defeat the Infinity Cache.  HBM-bound: 2 bytes read and 1 written per element,
-    4 bytes written per row."""
-    dev = torch.device("cuda", 0)
-    nbytes = 3 * rows * K + 4 * rows
-    rot = max(1, min(16, math.ceil(2 * MALL_BYTES / nbytes)))
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(7001)
-    xs = [torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
-          for _ in range(rot)]
-    qs = [torch.empty((rows, K), dtype=torch.uint8, device=dev) for _ in range(rot)]
-    ss = [torch.empty((rows,), dtype=torch.float32, device=dev) for _ in range(rot)]
-    stream = torch.cuda.current_stream(dev)
-    for i in range(20):
-        F.f8f8bf16_quantize_rowwise(xs[i % rot], qs[i % rot], ss[i % rot])
+def ramp(fn, seconds, batch):
+    """Untimed calls, synchronised every `batch` calls, until `seconds` of wall time
+    have passed: the GPU runs the workload continuously for that long, so its clock
+    has settled before anything is timed."""
+    import torch
+    t0 = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(batch):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+    return time.perf_counter() - t0, i
+
+
+def graph_us_per_call(torch, call, calls_per_graph, ramp_s, replays=20):
+    """Per-call time of `calls_per_graph` calls captured into one HIP graph,
+    replayed after a clock ramp; HIP events around the replays."""
+    for i in range(calls_per_graph):
+        call(i)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls_per_graph):
+            call(i)
+    ramp(lambda i: g.replay(), ramp_s, 2)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(calls):
-        F.f8f8bf16_quantize_rowwise(xs[i % rot], qs[i % rot], ss[i % rot])
-    e1.record(stream)
+    e0.record()
+    for _ in range(replays):
+        g.replay()
+    e1.record()
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / calls
-    gbs = nbytes / us / 1e3
-    log(f"quantize: bf16 [{rows}, {K}] -> e4m3fn: {us:.2f} us/call ({gbs:.0f} GB/s, {rot} input copies)")
-    del xs, qs, ss
-    return {"shape": [rows, K], "us_per_call": round(us, 3), "GB_per_s": round(gbs, 1),
-            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "input_copies": rot}
+    us = e0.elapsed_time(e1) * 1e3 / (replays * calls_per_graph)
+    del g
+    return us
 
 
-def copy_calibration(nbytes):
-    """A plain device copy of known size, profiled beside the GEMM to scale the
-    HBM byte counters."""
-    import torch
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
-    b = torch.empty_like(a)
-    for _ in range(5):
-        b.copy_(a)
-    torch.cuda.synchronize()
-    log(f"copy calibration: {nbytes} bytes read and written per copy, 5 copies")
-
-
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=1000)
-    ap.add_argument("--workload", default="moe_gate_up_preshuffle", choices=WORKLOADS)
-    ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate over (0 = automatic)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-small-m", action="store_true", help="skip the graph-replayed small-M timings")
-    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
-                    help="only run a plain copy of this many bytes (for counter calibration)")
-    args = ap.parse_args()
-
-    if args.gpus != 1:
-        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the library has no "
-              "multi-GPU path; the grouped GEMM shards by expert group, one process per GPU).", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(1)
-    if args.copy_calibration:
-        copy_calibration(args.copy_calibration)
-        return
-
-    import fp8_rowwise_scaled_amd as F
-
-    F.load()
-    w, layout, pre = make_workload(args.workload)
-    flop, nbytes, R, G_ne = algorithmic_work(w, layout)
-    log(f"workload {w.name}: layout={layout} preshuffled={pre} G={w.G} N={w.N} K={w.K} R={R} G_ne={G_ne} "
-        f"flop={flop:.4g} bytes={nbytes:.4g}")
-
+def prepare(F, torch, w, layout, pre, rotate):
+    """Device copies of the workload's inputs (`rotate` sets, resident in HBM) and
+    call(i), one call of the grouped GEMM on set i % rotate."""
     dev = torch.device("cuda", 0)
-    touched = nbytes
-    rotate = args.rotate or max(1, min(64, math.ceil(2 * MALL_BYTES / max(touched, 1))))
     X = torch.from_numpy(w.XQ).to(dev)
     Wt = torch.from_numpy(w.WQ).to(dev)
     xs = torch.from_numpy(w.x_scale).to(dev)
@@ -379,85 +341,213 @@ def main():
                  "k_offsets": lambda: (w.G, w.M, w.N),
                  "padded": lambda: (w.G, w.expected_m, w.N)}[layout]()
     outs = [torch.empty(out_shape, dtype=torch.bfloat16, device=dev) for _ in range(rotate)]
-    log(f"rotating over {rotate} input set(s)")
+    padded = layout in ("padded", "padded_blockscale")
+    fn = {("stacked", False): F.f8f8bf16_rowwise_grouped_stacked,
+          ("stacked", True): F.f8f8bf16_rowwise_grouped_stacked_preshuffle,
+          ("offsets", False): F.f8f8bf16_rowwise_grouped_offsets,
+          ("offsets", True): F.f8f8bf16_rowwise_grouped_offsets_preshuffle,
+          ("batched", False): F.f8f8bf16_rowwise_grouped_batched,
+          ("batched", True): F.f8f8bf16_rowwise_grouped_batched_preshuffle,
+          ("padded", False): F.f8f8bf16_rowwise_grouped_dynamic,
+          ("padded", True): F.f8f8bf16_rowwise_grouped_dynamic_preshuffle,
+          ("blockscale", False): F.f8f8bf16_groupwise_grouped_stacked,
+          ("blockscale", True): F.f8f8bf16_groupwise_grouped_stacked_preshuffle,
+          ("padded_blockscale", False): F.f8f8bf16_groupwise_grouped_dynamic,
+          ("padded_blockscale", True): F.f8f8bf16_groupwise_grouped_dynamic_preshuffle,
+          ("n_offsets", False): F.f8f8bf16_rowwise_grouped_n_offsets,
+          ("k_offsets", False): F.f8f8bf16_rowwise_grouped_k_offsets}[(layout, pre)]
 
-    if layout in ("stacked", "offsets"):
-        if layout == "stacked":
-            fn = F.f8f8bf16_rowwise_grouped_stacked_preshuffle if pre else F.f8f8bf16_rowwise_grouped_stacked
-        else:
-            fn = F.f8f8bf16_rowwise_grouped_offsets_preshuffle if pre else F.f8f8bf16_rowwise_grouped_offsets
-
-        def call(i):
-            s = sets[i % rotate]
-            fn(s[0], s[1], s[2], s[3], s[4], out=outs[i % rotate])
-    elif layout == "padded_blockscale":
-        fn = F.f8f8bf16_groupwise_grouped_dynamic
-
-        def call(i):
-            s = sets[i % rotate]
-            fn(s[0], s[1], s[2], s[3], s[4], zeroing_output_tensor=True, out=outs[i % rotate])
-    elif layout == "blockscale":
-        fn = F.f8f8bf16_groupwise_grouped_stacked_preshuffle if pre else F.f8f8bf16_groupwise_grouped_stacked
-
-        def call(i):
-            s = sets[i % rotate]
-            fn(s[0], s[1], s[2], s[3], s[4], out=outs[i % rotate])
-    elif layout in ("n_offsets", "k_offsets"):
-        fn = F.f8f8bf16_rowwise_grouped_n_offsets if layout == "n_offsets" else F.f8f8bf16_rowwise_grouped_k_offsets
-
-        def call(i):
-            s = sets[i % rotate]
-            fn(s[0], s[1], s[2], s[3], s[4], out=outs[i % rotate])
-    elif layout == "batched":
-        fn = F.f8f8bf16_rowwise_grouped_batched_preshuffle if pre else F.f8f8bf16_rowwise_grouped_batched
-
-        def call(i):
-            s = sets[i % rotate]
+    def call(i):
+        s = sets[i % rotate]
+        if layout == "batched":
             fn(s[0], s[1], s[2], s[3], out=outs[i % rotate])
-    else:
-        fn = F.f8f8bf16_rowwise_grouped_dynamic_preshuffle if pre else F.f8f8bf16_rowwise_grouped_dynamic
-
-        def call(i):
-            s = sets[i % rotate]
+        elif padded:
             fn(s[0], s[1], s[2], s[3], s[4], zeroing_output_tensor=True, out=outs[i % rotate])
+        else:
+            fn(s[0], s[1], s[2], s[3], s[4], out=outs[i % rotate])
+    return call
 
-    stream = torch.cuda.current_stream(dev)
-    for i in range(args.warmup):
+
+def time_eager(torch, call, steps, warmup, ramp_s):
+    """Clock ramp, `warmup` counted untimed calls, then exactly `steps` timed calls
+    between device synchronisations, each bracketed by HIP events on the stream
+    the kernels are launched on (the current stream)."""
+    stream = torch.cuda.current_stream()
+    ramp_done, ramp_calls = ramp(call, ramp_s, 8)
+    for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
-
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         starts[i].record(stream)
         call(i)
         ends[i].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     durs = [s.elapsed_time(e) * 1e-3 for s, e in zip(starts, ends)]
-    avg = sum(durs) / len(durs)
-    med = statistics.median(durs)
-    region = starts[0].elapsed_time(ends[-1]) * 1e-3 / args.steps
-    ms_per_step = wall / args.steps * 1e3
-    value = flop / (wall / args.steps) / 1e12
-    log(f"per call: wall {ms_per_step * 1e3:.2f} us, kernel avg {avg * 1e6:.2f} us, median {med * 1e6:.2f} us, "
-        f"min {min(durs) * 1e6:.2f} us, timed region / calls {region * 1e6:.2f} us")
+    region = starts[0].elapsed_time(ends[-1]) * 1e-3 / steps
+    return {"wall": wall, "durs": durs, "avg": sum(durs) / len(durs), "median": statistics.median(durs),
+            "min": min(durs), "region": region, "ramp_s": ramp_done, "ramp_calls": ramp_calls}
 
+
+def roofline_of(flop, nbytes, avg, traffic):
     mfma_bound = flop / (PEAK_FP8_TFLOPS * 1e12) >= nbytes / (PEAK_HBM_GBS * 1e9)
-    src_hash = kernel_source_hash()
-    traffic = measured_traffic(args.workload, src_hash)
     if mfma_bound:
         achieved = flop / avg / 1e12
-        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
+        return {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_FP8_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_FP8_TFLOPS, 4), "traffic": traffic}
-    else:
-        achieved = nbytes / avg / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+    achieved = nbytes / avg / 1e9
+    return {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic}
+
+
+def auto_rotate(nbytes):
+    """Input copies so that the calls together touch twice the Infinity Cache."""
+    return max(1, min(64, math.ceil(2 * MALL_BYTES / max(nbytes, 1))))
+
+
+def extra_workload(F, torch, name, ramp_s, steps=50):
+    """A further workload timed like the headline one (clock ramp, eager calls with
+    HIP events around each), for the extra keys of the JSON line."""
+    w, layout, pre = make_workload(name)
+    flop, nbytes, R, _ = algorithmic_work(w, layout)
+    call = prepare(F, torch, w, layout, pre, auto_rotate(nbytes))
+    t = time_eager(torch, call, steps, 5, ramp_s)
+    avg = t["avg"]
+    r = {"workload": w.name, "us_per_call": round(avg * 1e6, 3), "TFLOP_per_s": round(flop / avg / 1e12, 1),
+         "mfma_frac": round(flop / avg / 1e12 / PEAK_FP8_TFLOPS, 4), "GB_per_s": round(nbytes / avg / 1e9, 1),
+         "hbm_frac": round(nbytes / avg / 1e9 / PEAK_HBM_GBS, 4)}
+    log(f"{name}: {avg * 1e6:.2f} us/call, {r['TFLOP_per_s']} TFLOP/s ({r['mfma_frac']:.1%}), "
+        f"{r['GB_per_s']} GB/s ({r['hbm_frac']:.1%})")
+    del call
+    torch.cuda.empty_cache()
+    return r
+
+
+def small_m_us_per_call(F, torch, ramp_s, totals=(1, 8, 32, 256, 2048, 8192)):
+    """µs per call of the down-proj workload at each total_M, timed as the pages time
+    decode-sized GEMMs: many calls captured in one HIP graph (rotating over enough
+    input copies to defeat the Infinity Cache), replayed, divided by the call count."""
+    import workloads as wl
+    out = {}
+    for m in totals:
+        w = wl.moe_down(m)
+        flop, nbytes, _, _ = algorithmic_work(w, "stacked")
+        rot = auto_rotate(nbytes)
+        call = prepare(F, torch, w, "stacked", False, rot)
+        per_graph = 64 if m <= 256 else 16
+        us = graph_us_per_call(torch, call, per_graph, ramp_s)
+        out[f"moe_down_M{m}"] = {"us_per_call": round(us, 3), "GB_per_s": round(nbytes / us / 1e3, 1),
+                                 "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                                 "TFLOP_per_s": round(flop / us / 1e6, 1),
+                                 "mfma_frac": round(flop / us / 1e6 / PEAK_FP8_TFLOPS, 4), "input_copies": rot}
+        log(f"down-proj M={m}: {us:.2f} us/call under graph replay ({nbytes / us / 1e3:.0f} GB/s, "
+            f"{flop / us / 1e6:.0f} TFLOP/s, {rot} input copies)")
+        del call
+        torch.cuda.empty_cache()
+    return out
+
+
+def quantize_us_per_call(F, torch, ramp_s, rows=4096, K=7168, calls=200):
+    """The rowwise activation quantiser (bf16 [rows, K] -> e4m3fn codes + fp32 row
+    scales) on the gate_up activations' shape, rotating over enough input copies to
+    defeat the Infinity Cache.  HBM-bound: 2 bytes read and 1 written per element,
+    4 bytes written per row."""
+    dev = torch.device("cuda", 0)
+    nbytes = 3 * rows * K + 4 * rows
+    rot = max(1, min(16, math.ceil(2 * MALL_BYTES / nbytes)))
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7001)
+    xs = [torch.randn((rows, K), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+          for _ in range(rot)]
+    qs = [torch.empty((rows, K), dtype=torch.uint8, device=dev) for _ in range(rot)]
+    ss = [torch.empty((rows,), dtype=torch.float32, device=dev) for _ in range(rot)]
+
+    def call(i):
+        F.f8f8bf16_quantize_rowwise(xs[i % rot], qs[i % rot], ss[i % rot])
+    t = time_eager(torch, call, calls, 20, ramp_s)
+    us = t["avg"] * 1e6
+    gbs = nbytes / us / 1e3
+    log(f"quantize: bf16 [{rows}, {K}] -> e4m3fn: {us:.2f} us/call ({gbs:.0f} GB/s, {rot} input copies)")
+    del xs, qs, ss
+    return {"shape": [rows, K], "us_per_call": round(us, 3), "GB_per_s": round(gbs, 1),
+            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "input_copies": rot}
+
+
+def copy_calibration(nbytes):
+    """A plain device copy of known size, profiled beside the GEMM to scale the
+    HBM byte counters."""
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(5):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {nbytes} bytes read and written per copy, 5 copies")
+
+
+DEFAULT_WORKLOAD = "dense_expert_preshuffle"
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD, choices=WORKLOADS)
+    ap.add_argument("--ramp", type=float, default=1.0,
+                    help="seconds of untimed calls before the counted warm-up (default 1.0; shorter only for "
+                         "profiler runs)")
+    ap.add_argument("--rotate", type=int, default=0, help="input copies to rotate over (0 = automatic)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the extra workloads (plain W, gate_up, padded tails, down-proj sweep, quantiser)")
+    ap.add_argument("--no-small-m", action="store_true", help="same as --no-extras")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain copy of this many bytes (for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: --gpus {args.gpus} is not supported (the library has no "
+              "multi-GPU path; the grouped GEMM shards by expert group, one process per GPU).", file=sys.stderr)
+        sys.exit(2)
+    ramp_s = max(0.0, args.ramp)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
+    import fp8_rowwise_scaled_amd as F
+
+    F.load()
+    w, layout, pre = make_workload(args.workload)
+    flop, nbytes, R, G_ne = algorithmic_work(w, layout)
+    log(f"workload {w.name}: layout={layout} preshuffled={pre} G={w.G} N={w.N} K={w.K} R={R} G_ne={G_ne} "
+        f"flop={flop:.4g} bytes={nbytes:.4g}")
+    rotate = args.rotate or auto_rotate(nbytes)
+    call = prepare(F, torch, w, layout, pre, rotate)
+    log(f"rotating over {rotate} input set(s); clock ramp {ramp_s:.1f} s")
+    t = time_eager(torch, call, args.steps, args.warmup, ramp_s)
+    avg, wall = t["avg"], t["wall"]
+    ms_per_step = wall / args.steps * 1e3
+    value = flop / (wall / args.steps) / 1e12
+    log(f"ramp: {t['ramp_calls']} calls over {t['ramp_s']:.2f} s")
+    log(f"per call: wall {ms_per_step * 1e3:.2f} us, kernel avg {avg * 1e6:.2f} us, median {t['median'] * 1e6:.2f} us, "
+        f"min {t['min'] * 1e6:.2f} us, timed region / calls {t['region'] * 1e6:.2f} us")
+    src_hash = kernel_source_hash()
+    roof = roofline_of(flop, nbytes, avg, measured_traffic(args.workload, src_hash))
     log(f"kernel: {flop / avg / 1e12:.1f} TFLOP/s ({flop / avg / 1e12 / PEAK_FP8_TFLOPS:.1%} of fp8 peak), "
         f"{nbytes / avg / 1e9:.0f} GB/s ({nbytes / avg / 1e9 / PEAK_HBM_GBS:.1%} of HBM); source hash {src_hash}")
+    del call
+    torch.cuda.empty_cache()
 
     result = {
         "metric": METRIC,
@@ -473,7 +563,7 @@ def main():
         "dtype": "fp8_e4m3fn",
         "data": "synthetic",
         "config": {
-            "workload": w.name,
+            "workload": w.name + ("_preshuffle" if pre and not w.name.endswith("_preshuffle") else ""),
             "layout": layout,
             "preshuffled": pre,
             "G": w.G,
@@ -485,15 +575,22 @@ def main():
             "group_rows": group_meta(w, layout),
             "rotating_input_sets": rotate,
             "us_per_call": round(avg * 1e6, 3),
+            "us_per_call_median": round(t["median"] * 1e6, 3),
+            "clock_ramp_s": round(t["ramp_s"], 3),
+            "clock_ramp_calls": t["ramp_calls"],
         },
         "roofline": roof,
     }
-    if not args.no_small_m and args.workload in ("moe_gate_up", "moe_gate_up_preshuffle"):
-        result["small_m"] = small_m_us_per_call(F, torch)
-        result["quantize"] = quantize_us_per_call(F, torch)
+    extras = not (args.no_extras or args.no_small_m) and args.workload == DEFAULT_WORKLOAD
+    if extras:
+        result["dense_expert_plain_w"] = extra_workload(F, torch, "dense_expert", ramp_s)
+        result["gate_up"] = extra_workload(F, torch, "moe_gate_up_preshuffle", ramp_s)
+        result["padded_tails"] = extra_workload(F, torch, "padded_tails", ramp_s)
+        result["small_m"] = small_m_us_per_call(F, torch, ramp_s)
+        result["quantize"] = quantize_us_per_call(F, torch, ramp_s)
     if not args.no_cpu_baseline:
         log("timing the CPU oracle ...")
-        result["cpu_baseline"] = cpu_baseline(w, layout, flop)
+        result["cpu_baseline"] = cpu_baseline(w, layout, flop, single_thread=extras)
     print(json.dumps(result), flush=True)
 
 

@@ -28,6 +28,7 @@ struct GemmArgs {
   int64_t m_tiles;       // packed: upper bound of M tiles over all groups; padded: per slab
   int64_t n_tiles;
   int32_t zeroing;       // padded: write zeros into padding rows
+  int32_t xcd_group;     // data-parallel grid: 1 = each XCD takes a contiguous eighth of the tiles (xcd_slot)
 };
 
 // A compiled kernel configuration (workgroup tile and pipeline).
@@ -63,9 +64,7 @@ __host__ __device__ inline bool tail_quarters(int64_t T, int64_t P, int mode) {
 
 inline int lds_bytes(const KernelConfig& c) {
   if (c.kind == kKindSkinny) return 3 * (c.BM / 32) * 16 * 64 * 4;
-  const int stages = c.stages * (c.BM + c.BN) * c.BK;
-  // persistent: two scale blocks and a dummy word per lane
-  return c.kind == kKindPersistent ? stages + 2 * (c.BM + c.BN) * 4 + 256 : stages;
+  return c.stages * (c.BM + c.BN) * c.BK;
 }
 
 hipError_t launch_gemm(int layout, int config_id, bool k_tail, const GemmArgs& args,

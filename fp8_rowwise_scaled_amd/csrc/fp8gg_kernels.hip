@@ -38,12 +38,13 @@
 //   * W rows are placed in LDS in "MFMA order": LDS row 32*fn + rho of a wave's
 //     slice holds the output column that MFMA row rho of block fn produces in the
 //     chosen lane -> column map, so the loads do the permutation for free.
-//   * Large stacked calls run on a persistent grid whose LDS ring continues from
-//     one tile to the next (gg_persistent_kernel); small-M calls use 32-row tiles
-//     with a deep ring, or stream W straight into registers (gg_skinny_kernel).
-//   * Kernels that run one tile per workgroup (gg_lds_kernel, gg_ragged_kernel,
-//     gg_blockscale_kernel) store the output tile through their idle LDS ring, so
-//     each store instruction covers whole rows (LdsTile::store_shuffled).
+//   * Large stacked calls run on a persistent grid (one workgroup per compute
+//     unit) whose partial last round runs as quarter tiles (gg_persistent_kernel);
+//     small-M calls use 32-row tiles with a deep ring, or stream W straight into
+//     registers (gg_skinny_kernel).
+//   * After its K loop a tile stores its output through the then idle LDS ring, so
+//     each store instruction covers whole rows (LdsTile::store_shuffled); only the
+//     persistent kernel's quarter tiles store straight from registers.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -408,6 +409,18 @@ __device__ __forceinline__ bool resolve_k_offsets(const GemmArgs& a, int64_t b, 
   return t.row_base < t.row_end;
 }
 
+// Tile order across the XCDs.  MI355X dispatches consecutive workgroups of a grid
+// to its eight XCDs in turn, and each XCD has its own L2, so workgroup w runs on
+// XCD w % 8.  xcd_slot only reorders work (every tile is still computed by one
+// workgroup in the same K order, so results do not depend on it): within P
+// consecutive workgroups (P a multiple of 8) it gives workgroup w position
+// (w % 8) * (P / 8) + w / 8, so that XCD x takes the contiguous positions
+// [x * P / 8, (x + 1) * P / 8) and the workgroups running together on one XCD
+// share operands.
+__device__ __forceinline__ int64_t xcd_slot(int64_t w, int64_t P) {
+  return (P % 8 == 0) ? (w % 8) * (P / 8) + w / 8 : w;
+}
+
 // ---------------------------------------------------------------------------
 // The grouped GEMM with both operands staged through LDS (plain or pre-shuffled W)
 // ---------------------------------------------------------------------------
@@ -660,71 +673,15 @@ struct LdsTile {
         for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wf[ks][fn], xf[ks][fm], acc[fm][fn]);
   }
 
-  // The tile's scales as an LDS block of BN + BM floats: w_scale[g, n0 .. n0+BN)
-  // then x_scale[row_base .. row_base+BM), copied 64 floats per wave (4 bytes per
-  // lane) by the same copy engine as the operands, so they travel with a K stage.
-  // Columns past N and rows past the group read a valid neighbour (never stored).
-  // Every wave issues exactly one copy, the waves beyond the block into a dummy
-  // word, so that a stage carrying scales adds one to every wave's count.
-  static constexpr int SCALE_FLOATS = BN + BM;
-  __device__ __forceinline__ void issue_scales(const GemmArgs& a, const Tile& t, int64_t n0, float* sbuf,
-                                               float* dummy) const {
-    static_assert(SCALE_FLOATS % 64 == 0 && SCALE_FLOATS <= NT, "one scale copy per wave");
-    const int f = wave * 64 + lane;
-    const float* src;
-    float* dst;
-    if (wave < SCALE_FLOATS / 64) {
-      if (f < BN) {
-        int64_t c = n0 + f;
-        c = c < a.N ? c : a.N - 1;
-        src = a.ws + t.g * a.N + c;
-      } else {
-        int64_t r = t.row_base + (f - BN);
-        r = r < t.row_end ? r : t.row_end - 1;
-        src = a.xs + r;
-      }
-      dst = sbuf + wave * 64;
-    } else {
-      src = a.ws + t.g * a.N;
-      dst = dummy;
-    }
-    copy4_to_lds(src, lds_addr(dst));
-  }
-
-  // scale() with the scales taken from an LDS block written by issue_scales.
-  __device__ __forceinline__ void scale_lds(const Acc& acc, const float* sbuf, Packed& pk) const {
-#pragma unroll
-    for (int fm = 0; fm < FM; ++fm) {
-      const float xsv = sbuf[BN + wm * TM + 32 * fm + r32];
-#pragma unroll
-      for (int fn = 0; fn < FN; ++fn)
-#pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const float* wl = sbuf + col_of(fn) + 8 * half;
-          const v4f w0 = *(const v4f*)(wl);
-          const v4f w1 = *(const v4f*)(wl + 4);
-          const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-          uint32_t q[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int i = 8 * half + 2 * e;
-            q[e] = pack_bf16x2((acc[fm][fn][i] * xsv) * wv[2 * e], (acc[fm][fn][i + 1] * xsv) * wv[2 * e + 1]);
-          }
-          pk[fm][fn][half] = v4i{(int)q[0], (int)q[1], (int)q[2], (int)q[3]};
-        }
-    }
-  }
-
   __device__ __forceinline__ void run(int kb, int ke, int nk, int64_t K, Acc& acc) {
     prologue(kb, ke, nk, K);
     mainloop(kb, ke, nk, K, acc);
   }
 
   // The epilogue, y = bf16((acc * x_scale[m]) * w_scale[g, n]) under row and
-  // column masks, in two halves so that a persistent workgroup can issue the next
-  // tile's first copies between them: scale() loads the scales and turns the
-  // accumulators into packed bf16 pairs, store() writes them (and writes rows
-  // [row_end, zero_end) as zero).  Lane (h, r32) holds, for block (fm, fn), slot
+  // column masks, in two halves: scale() loads the scales and turns the
+  // accumulators into packed bf16 pairs, store() (or store_shuffled()) writes them
+  // (and writes rows [row_end, zero_end) as zero).  Lane (h, r32) holds, for block (fm, fn), slot
   // i = 4*j + tt, output row wm*TM + 32*fm + r32 and column col0 + 16*fn + i; pair
   // q of Packed[fm][fn] holds slots 2q and 2q + 1.
 
@@ -882,7 +839,8 @@ gg_lds_kernel(GemmArgs a) {
   typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL, PRE> E;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
 
-  const int64_t bid = blockIdx.x;
+  // xcd_group: each XCD takes a contiguous eighth of the tile order
+  const int64_t bid = a.xcd_group ? xcd_slot(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
   const int64_t n_tile = bid % a.n_tiles;
   const int64_t rest = bid / a.n_tiles;
   Tile t;
@@ -960,9 +918,10 @@ __device__ __forceinline__ int64_t count_m_tiles(const GemmArgs& a) {
 
 // Persistent kernel (packed layouts: stacked, offsets, batched).
 //
-// Schedule.  A grid of P workgroups, one per compute unit, walks the T output
-// tiles in data-parallel order: workgroup w computes whole tiles w, w + P, ...
-// When T is not a multiple of P, the rem = T % P tiles of the last round would keep
+// A grid of P workgroups, one per compute unit, walks the T output tiles in
+// data-parallel order: workgroup w computes whole tiles w, w + P, ..., each with
+// its own prologue and the coalesced store through the then idle LDS ring.  When T
+// is not a multiple of P, the rem = T % P tiles of the last round would keep
 // P - rem compute units idle for a whole tile.  When 4 * rem <= 2 * P those tiles
 // are computed as quarter tiles instead, (BM/2) x (BN/2) each: quarter q of
 // remainder tile i is quarter number 4i + q, and workgroup w computes quarters w,
@@ -973,135 +932,8 @@ __device__ __forceinline__ int64_t count_m_tiles(const GemmArgs& a) {
 // one workgroup in the same K order as in the data-parallel kernel, so the result
 // is bitwise that of the data-parallel kernel whatever the grid.
 //
-// Pipeline.  A workgroup's whole tiles form one stream of K stages through the LDS
-// ring: while the last stages of one tile are multiplied, the first stages of the
-// next are already being copied, and the finished tile's epilogue runs with them
-// in flight.  Each tile's scales travel with its first stage into one of two LDS
-// scale blocks, so the epilogue reads no global memory.  Copies of a tile two ahead
-// wait until the tile before it is done, which keeps two scale blocks enough.  The
-// wait before each stage counts the copies issued after that stage exactly (stores
-// issued since then only make it stricter: vector memory operations complete in
-// order).  Quarter tiles run one after another, each with its own prologue.
-//
 // tail_mode: 0 chooses quarters by the rule above, 1 never uses them, 2 always
 // does when rem > 0.
-template <int LAYOUT, typename E>
-__device__ __forceinline__ void persistent_whole_tiles(const GemmArgs& a, int64_t w, int64_t P, int64_t whole,
-                                                       int nk, uint8_t* smem, float (*scales)[E::SCALE_FLOATS],
-                                                       float* scale_dummy) {
-  constexpr int STAGES = E::STAGES_;
-  // Deferring a finished tile's stores by one stage keeps them out of the next
-  // stage's wait; it needs the packed outputs live across one more MFMA step,
-  // which fits the register budget of the smaller tiles only.
-  constexpr bool DEFER_STORES = E::ACC_FLOATS <= 64;
-  static_assert(E::EVEN_LOADS, "the stage wait counts assume equal copies per wave");
-  if (w >= whole) return;
-
-  E e;
-  e.init(smem);
-
-  struct Item {
-    Tile t;
-    int64_t tile, n0;
-    int seq;
-  };
-  int64_t next = w;
-  auto take = [&](Item& it, int seq) -> bool {
-    if (next >= whole) return false;
-    it.tile = next;
-    it.seq = seq;
-    next += P;
-    resolve_packed<LAYOUT, E::BM_>(a, it.tile / a.n_tiles, it.t);
-    it.n0 = (it.tile % a.n_tiles) * E::BN_;
-    return true;
-  };
-
-  Item C;                       // the tile whose stages are being multiplied
-  take(C, 0);
-  Item I = C;                   // the tile whose stages are being copied
-  bool more = true;             // tiles may remain after I
-  int kt_i = 0;
-  int u_i = 0, u_c = 0;         // stages issued / multiplied so far (LDS slot = u % STAGES)
-  int ahead = 0;                // stages issued and not yet multiplied
-  uint32_t firsts = 0;          // bit j: the j-th oldest of those is a tile's first stage
-  e.setup(a, I.t, I.n0);
-
-  auto issue_next = [&]() {
-    if (kt_i == nk) {
-      if (!more || I.seq != C.seq) return;
-      Item nx;
-      if (!take(nx, I.seq + 1)) {
-        more = false;
-        return;
-      }
-      I = nx;
-      kt_i = 0;
-      e.setup(a, I.t, I.n0);
-    }
-    const bool first = kt_i == 0;
-    e.issue(kt_i, u_i % STAGES, nk, a.K);
-    if (first) e.issue_scales(a, I.t, I.n0, scales[I.seq & 1], scale_dummy);
-    firsts |= (uint32_t)first << ahead;
-    ++ahead;
-    ++kt_i;
-    ++u_i;
-  };
-
-#pragma unroll
-  for (int j = 0; j < STAGES - 1; ++j) issue_next();
-
-  // One step of the stage stream: wait for stage u_c, make it visible, issue the
-  // next copies, multiply.
-  auto step = [&](typename E::Acc& acc, bool stores, const Tile& st, int64_t sn0, const typename E::Packed& pk) {
-    // Stage u_c has landed once only the copies issued after it are outstanding:
-    // L per younger stage, plus one for each younger stage that carries scales.
-    if (STAGES == 2 || ahead == 1) {
-      wait_vmcnt_le(0);
-    } else if (STAGES == 3) {
-      if (firsts & 2u) wait_vmcnt_le(E::LOADS_PER_STAGE + 1);
-      else wait_vmcnt_le(E::LOADS_PER_STAGE);
-    } else {
-      wait_vmcnt_le((ahead - 1) * E::LOADS_PER_STAGE + __builtin_popcount(firsts >> 1));
-    }
-    block_barrier();
-    if (stores) e.store(a, st, sn0, pk);
-    issue_next();
-    e.compute(u_c % STAGES, acc);
-    ++u_c;
-    --ahead;
-    firsts >>= 1;
-  };
-
-  typename E::Packed pk;
-  Tile st = C.t;                // tile of the stores deferred into the next tile's first stage
-  int64_t sn0 = 0;
-  bool pending = false;
-  for (;;) {
-    typename E::Acc acc;
-#pragma unroll
-    for (int i = 0; i < E::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < E::FN; ++j) acc[i][j] = v16f{0};
-    // The first stage of the tile is peeled off: it carries the previous tile's
-    // deferred stores, so the loop over the remaining stages carries only acc.
-    step(acc, DEFER_STORES && pending, st, sn0, pk);
-    pending = false;
-    for (int kt = 1; kt < nk; ++kt) step(acc, false, st, sn0, pk);
-
-    e.scale_lds(acc, scales[C.seq & 1], pk);
-    const bool last_tile = I.seq == C.seq;   // nothing was taken after C
-    if (DEFER_STORES && !last_tile) {
-      st = C.t;
-      sn0 = C.n0;
-      pending = true;
-    } else {
-      e.store(a, C.t, C.n0, pk);
-    }
-    if (last_tile) return;
-    C = I;
-  }
-}
-
 template <int LAYOUT, int BM, int BN, int BK, int WM, int WN, int STAGES, bool KTAIL, bool PRE>
 __global__ void __launch_bounds__(WM * WN * 64)
 gg_persistent_kernel(GemmArgs a, int tail_mode) {
@@ -1112,8 +944,6 @@ gg_persistent_kernel(GemmArgs a, int tail_mode) {
   typedef LdsTile<BM / 2, BN / 2, BK, WM, WN, Q_STAGES, KTAIL, PRE> Q;
   static_assert(Q::SMEM_BYTES <= E::SMEM_BYTES, "quarter tiles reuse the LDS ring");
   __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
-  __shared__ __attribute__((aligned(16))) float scales[2][E::SCALE_FLOATS];
-  __shared__ __attribute__((aligned(16))) float scale_dummy[64];
 
   const int64_t P = gridDim.x;
   const int64_t w = blockIdx.x;
@@ -1122,7 +952,21 @@ gg_persistent_kernel(GemmArgs a, int tail_mode) {
   const int64_t rem = tail_quarters(T, P, tail_mode) ? T % P : 0;
   const int64_t whole = T - rem;
 
-  persistent_whole_tiles<LAYOUT, E>(a, w, P, whole, nk, smem, scales, scale_dummy);
+  for (int64_t tile = w; tile < whole; tile += P) {
+    Tile t;
+    resolve_packed<LAYOUT, BM>(a, tile / a.n_tiles, t);
+    const int64_t n0 = (tile % a.n_tiles) * BN;
+    E e;
+    e.init(smem);
+    e.setup(a, t, n0);
+    typename E::Acc acc;
+#pragma unroll
+    for (int i = 0; i < E::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < E::FN; ++j) acc[i][j] = v16f{0};
+    e.run(0, nk, nk, a.K, acc);   // starts with a barrier: the ring is free to reuse
+    e.epilogue_shuffled(a, t, n0, acc);
+  }
 
   for (int64_t qn = w; qn < 4 * rem; qn += P) {
     const int64_t tile = whole + qn / 4;
