@@ -338,6 +338,7 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
     const int xg = layout == FP8GG_LAYOUT_PADDED && c0.kind == fp8gg::kKindLds && c0.BM >= 128 ? 1 : 0;
     a.xcd_group = env_int("FP8GG_XCD", xg) ? 1 : 0;
   }
+  a.skip_dead = env_int("FP8GG_SKIP_DEAD", 1) ? 1 : 0;
   if (env_int("FP8GG_LOG", 0))
     std::fprintf(stderr,
                  "[fp8gg] layout=%d pre=%d G=%lld M=%lld N=%lld K=%lld -> cfg=%d tile=%dx%dx%d thr=%d st=%d "

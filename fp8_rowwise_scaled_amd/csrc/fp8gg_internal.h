@@ -29,6 +29,7 @@ struct GemmArgs {
   int64_t n_tiles;
   int32_t zeroing;       // padded: write zeros into padding rows
   int32_t xcd_group;     // data-parallel grid: 1 = each XCD takes a contiguous eighth of the tiles (xcd_slot)
+  int32_t skip_dead;     // 1: waves whose rows all lie past the tile's group issue no MFMAs
 };
 
 // A compiled kernel configuration (workgroup tile and pipeline).

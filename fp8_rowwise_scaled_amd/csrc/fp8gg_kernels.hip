@@ -475,6 +475,10 @@ struct LdsTile {
 
   uint8_t* smem;
   int tid, lane, wave, wm, wn, h, r32;
+  // Whether any of this wave's TM rows belongs to the tile's group.  A wave whose
+  // rows all lie past the group (a sparse last tile of a group) reads no fragments
+  // and issues no MFMAs: its outputs are never stored.  Wave-uniform.
+  bool rows_live;
   int loads_per_stage;
   const uint8_t* a_src[A_LOADS];
   int a_kc[A_LOADS];
@@ -508,6 +512,7 @@ struct LdsTile {
     const int64_t K = a.K;
     const int64_t k0 = tile_k0(t);
     const int64_t xd = tile_x_delta(t);
+    rows_live = !a.skip_dead || t.row_end - t.row_base > (int64_t)wm * TM;
 #pragma unroll
     for (int i = 0; i < A_LOADS; ++i) {
       const int q = i * NT + tid;
@@ -645,32 +650,17 @@ struct LdsTile {
       else wait_vmcnt_le(0);
       block_barrier();
       if (kt + STAGES - 1 < ke) issue(kt + STAGES - 1, (j + STAGES - 1) % STAGES, nk, K);
-      v8i xf[KS][FM], wf[KS][FN];
-      read_frags(j % STAGES, xf, wf);
+      if (rows_live) {
+        v8i xf[KS][FM], wf[KS][FN];
+        read_frags(j % STAGES, xf, wf);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm)
+          for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-          for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wf[ks][fn], xf[ks][fm], acc[fm][fn]);
+            for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wf[ks][fn], xf[ks][fm], acc[fm][fn]);
+      }
     }
-  }
-
-  // acc += the products of the stage in LDS slot `slot` (all waves, after the
-  // barrier that follows that stage's copies).
-  __device__ __forceinline__ void compute(int slot, Acc& acc) const {
-    v8i xf[KS][FM], wf[KS][FN];
-    read_frags(slot, xf, wf);
-    mfmas(xf, wf, acc);
-  }
-
-  __device__ __forceinline__ static void mfmas(const v8i (&xf)[KS][FM], const v8i (&wf)[KS][FN], Acc& acc) {
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < FN; ++fn) acc[fm][fn] = mfma_32x32x64_fp8(wf[ks][fn], xf[ks][fm], acc[fm][fn]);
   }
 
   __device__ __forceinline__ void run(int kb, int ke, int nk, int64_t K, Acc& acc) {
