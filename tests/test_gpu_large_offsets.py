@@ -1,4 +1,4 @@
-"""GPU parity past 2 GiB: 64-bit addressing of X, W and Y (and of the quantiser).
+"""GPU parity past 2 GiB: 64-bit addressing of X, W and Y on every layout family.
 
 Each case puts the group that is checked beyond the first 2^31 bytes of one
 operand, so a 32-bit byte offset anywhere on its path (copy descriptors, the
@@ -67,8 +67,8 @@ def device_codes(shape, seed):
     g = torch.Generator(device="cuda")
     g.manual_seed(seed)
     b = torch.randint(0, 256, shape, dtype=torch.uint8, device="cuda", generator=g)
-    b[(b & 0x7F) == 0x7F] -= 1
-    return b
+    # elementwise: masked indexing builds an index list, which breaks past 2^31 elements
+    return torch.where((b & 0x7F) == 0x7F, b - 1, b)
 
 
 def scales(rng, n):
@@ -218,3 +218,48 @@ def test_quantiser_rows_past_2gib(F):
     q_ref, s_ref = oracle.quantize_rowwise(x_tail)
     assert np.array_equal(s[rows - tail:].cpu().numpy().view(np.uint32), s_ref.view(np.uint32))
     assert np.array_equal(q[rows - tail:].cpu().numpy(), q_ref)
+
+
+def test_n_offsets_w_rows_past_2gib(F):
+    """n_offsets, K = 32768: group 0 owns W rows [0, 65600) (2.15 GB), group 1's 64
+    rows start past 2^31 bytes; group 1's output columns are checked."""
+    rng = np.random.default_rng(9960)
+    K, M, N0, N1 = 32768, 16, 65600, 64
+    assert N0 * K > TWO_GIB
+    W = device_codes((N0 + N1, K), 9960)
+    X = host_codes(rng, (2, M, K))
+    xs = scales(rng, 2 * M).reshape(2, M)
+    ws = scales(rng, N0 + N1)
+    offs = np.array([N0, N0 + N1], np.int32)
+    whole, y = guarded(M * (N0 + N1))
+    print("case n_offsets W past 2 GiB", flush=True)
+    F.f8f8bf16_rowwise_grouped_n_offsets(P.dev(X), W, P.dev(xs), P.dev(ws), P.dev(offs),
+                                         out=y.view(torch.bfloat16).view(M, N0 + N1))
+    torch.cuda.synchronize()
+    assert guards_intact(whole)
+    ref = oracle.grouped_n_offsets(X[1:2], W[N0:].cpu().numpy(), xs[1:2], ws[N0:], np.array([N1], np.int32))
+    got = bits(y.view(M, N0 + N1)[:, N0:])
+    assert np.all(ref.col_class == oracle.ROW_WRITTEN)
+    P.assert_rows_match(got, ref, label="n_offsets group 1")
+
+
+def test_k_offsets_rows_past_2gib(F):
+    """k_offsets with total_K = 2^21 and 1100 rows (2.3 GB of X): group 1 contracts
+    over the last 2048 columns, which for rows 1024 on lie past 2^31 bytes."""
+    rng = np.random.default_rng(9970)
+    M, N, K, S = 1100, 64, 1 << 21, 2048
+    assert 1024 * K + K - S > TWO_GIB
+    X = device_codes((M, K), 9971)
+    W = device_codes((N, K), 9972)
+    xs = scales(rng, 2 * M).reshape(2, M)
+    ws = scales(rng, 2 * N).reshape(2, N)
+    offs = np.array([K - S, K], np.int32)
+    whole, y = guarded(2 * M * N)
+    print("case k_offsets rows past 2 GiB", flush=True)
+    F.f8f8bf16_rowwise_grouped_k_offsets(X, W, P.dev(xs), P.dev(ws), P.dev(offs),
+                                         out=y.view(torch.bfloat16).view(2, M, N))
+    torch.cuda.synchronize()
+    assert guards_intact(whole)
+    ref = oracle.grouped_k_offsets(X[:, K - S:].cpu().numpy(), W[:, K - S:].cpu().numpy(), xs[1:2], ws[1:2],
+                                   np.array([S], np.int32))
+    P.assert_rows_match(bits(y.view(2, M, N)[1]), ref, label="k_offsets group 1")
