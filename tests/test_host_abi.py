@@ -120,6 +120,43 @@ def test_entry_points_refuse_before_any_gpu_call():
     assert st == _lib.OK and F.last_error() == ""
 
 
+def test_last_error_is_per_thread():
+    """Eight threads fail host-side checks concurrently, each with its own kind of
+    error, and each reads back its own message (the message is thread-local; ctypes
+    releases the GIL around every call, so the calls really overlap)."""
+    import threading
+    lib = _lib.load()
+    a = 0x10000000
+    calls = {
+        "multiple of 16": lambda: lib.f8f8bf16_rowwise_grouped_stacked(a, a, a, a, a, a + 0x1000000, 2, 8, 16, 24,
+                                                                       None),
+        "null": lambda: lib.f8f8bf16_rowwise_grouped_stacked(None, a, a, a, a, a + 0x1000000, 2, 8, 16, 32, None),
+        "aligned": lambda: lib.f8f8bf16_rowwise_grouped_dynamic(a, a, a, a, a, a + 0x1000002, 2, 8, 16, 32, 1,
+                                                                None),
+        "": lambda: lib.f8f8bf16_rowwise_grouped_stacked(None, None, None, None, None, None, 4, 0, 16, 32, None),
+    }
+    kinds = list(calls)
+    failures = []
+    start = threading.Barrier(8)
+
+    def worker(t):
+        start.wait()
+        for i in range(300):
+            kind = kinds[(t + i) % len(kinds)]
+            calls[kind]()
+            msg = F.last_error()
+            if (kind == "" and msg != "") or kind not in msg:
+                failures.append((t, i, kind, msg))
+                return
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(8)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not failures, failures[:3]
+
+
 def test_plan_n_offsets_bounds_column_tiles():
     """n_offsets: column tiles over the groups' ranges are at most ceil(N/BN) + G - 1
     (each holds a column), row tiles cover one slab."""
