@@ -123,6 +123,10 @@ fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int6
   return FP8GG_OK;
 }
 
+// Fixed selector (measured on MI355X; no benchmarking inside a call).  The key is
+// the rows one group contributes on average -- total_M normalised by G for the
+// packed layouts, the slab height otherwise -- because a tile only ever sees one
+// group.
 // Compute units the selector plans for (MI355X).  Only a heuristic: the persistent
 // grid itself is sized from the device at launch.
 constexpr int64_t kPlanCus = 256;
@@ -140,10 +144,6 @@ int select_ragged(int layout, int64_t G, int64_t M, int64_t N) {
   return cols <= 64 ? 21 : 18;
 }
 
-// Fixed selector (measured on MI355X; no benchmarking inside a call).  The key is
-// the rows one group contributes on average -- total_M normalised by G for the
-// packed layouts, the slab height otherwise -- because a tile only ever sees one
-// group.
 int select_config(int layout, int preshuffled, int64_t G, int64_t M, int64_t N, int64_t K) {
   (void)K;
   if (ragged(layout)) return select_ragged(layout, G, M, N);
