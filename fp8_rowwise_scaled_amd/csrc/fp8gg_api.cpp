@@ -132,13 +132,22 @@ fp8gg_status check_shape(int layout, int preshuffled, int64_t G, int64_t M, int6
 constexpr int64_t kPlanCus = 256;
 
 // The ragged layouts (n_offsets, k_offsets) run one tile per workgroup on the
-// configurations compiled for them (2, 7, 9, 18, 21), keyed on the slab height
-// and, for n_offsets, on the columns a group owns on average.
-bool ragged_config(int cfg) { return cfg == 2 || cfg == 7 || cfg == 9 || cfg == 18 || cfg == 21; }
+// configurations compiled for them (2, 7, 9, 18, 21, 28), keyed on the slab
+// height and, for n_offsets, on the columns a group owns on average.
+bool ragged_config(int cfg) { return cfg == 2 || cfg == 7 || cfg == 9 || cfg == 18 || cfg == 21 || cfg == 28; }
 
 int select_ragged(int layout, int64_t G, int64_t M, int64_t N) {
   const int64_t cols = layout == FP8GG_LAYOUT_N_OFFSETS && G > 0 ? (N + G - 1) / G : N;
-  if (M >= 256 && cols >= 256) return 7;
+  if (M >= 256 && cols >= 256) {
+    // 256x256 tiles, unless 192x256 tiles still make a single round of the compute
+    // units (bounded from the host: n_offsets column tiles <= ceil(N/256) + G - 1):
+    // then the smaller tiles put more units to work.  Measured on 8 slabs of 512
+    // rows, N = 16384: 198 tiles of 192x256 in 90.5 us against 132 of 256x256 in
+    // 101.1 us; with several rounds (k_offsets, 1792 tiles) 256x256 stays ahead.
+    const int64_t ub = (N + 255) / 256 + G - 1;
+    const int64_t col_tiles = layout == FP8GG_LAYOUT_N_OFFSETS ? (ub < N ? ub : N) : G * ((N + 255) / 256);
+    return ((M + 191) / 192) * col_tiles <= kPlanCus ? 28 : 7;
+  }
   if (M >= 128) return 9;
   if (M >= 48) return 2;
   return cols <= 64 ? 21 : 18;

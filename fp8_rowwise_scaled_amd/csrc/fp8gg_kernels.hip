@@ -1455,6 +1455,7 @@ const KernelConfig kConfigs[] = {
     /* 25 */ {256, 256, 128, 2, 4, 2, 0, 0, 0, 1},
     /* 26 */ {256, 256, 128, 2, 4, 2, 4, 0, 25, 1},
     /* 27 */ {32, 64, 128, 1, 2, 4, 0, 0, 0, 1},
+    /* 28 */ {192, 256, 128, 2, 4, 2, 0, 0, 0},
 };
 const int kNumConfigs = sizeof(kConfigs) / sizeof(kConfigs[0]);
 
@@ -1521,6 +1522,7 @@ static hipError_t launch_layout(int config_id, bool k_tail, const GemmArgs& a, i
     case 24: return launch_lds<LAYOUT, 32, 64, 128, 1, 2, 8>(k_tail, a, grid, s);
     case 25: return launch_lds<LAYOUT, 256, 256, 128, 2, 4, 2, true>(k_tail, a, grid, s);
     case 27: return launch_lds<LAYOUT, 32, 64, 128, 1, 2, 4, true>(k_tail, a, grid, s);
+    case 28: return launch_lds<LAYOUT, 192, 256, 128, 2, 4, 2>(k_tail, a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1580,6 +1582,7 @@ static hipError_t launch_ragged_layout(int config_id, bool k_tail, const GemmArg
     case 9: return launch_ragged<LAYOUT, 128, 256, 128, 2, 4, 3>(k_tail, a, grid, s);
     case 18: return launch_ragged<LAYOUT, 32, 128, 128, 1, 4, 3>(k_tail, a, grid, s);
     case 21: return launch_ragged<LAYOUT, 32, 64, 128, 1, 2, 4>(k_tail, a, grid, s);
+    case 28: return launch_ragged<LAYOUT, 192, 256, 128, 2, 4, 2>(k_tail, a, grid, s);
     default: return hipErrorInvalidValue;
   }
 }

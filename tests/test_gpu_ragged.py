@@ -20,7 +20,7 @@ from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 
-RAGGED_CONFIGS = [2, 7, 9, 18, 21]
+RAGGED_CONFIGS = [2, 7, 9, 18, 21, 28]
 FINITE = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
 
 

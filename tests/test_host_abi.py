@@ -168,6 +168,23 @@ def test_plan_n_offsets_bounds_column_tiles():
         assert p["persistent"] == 0 and p["k_tail"] == (K % p["BK"] != 0)
 
 
+def test_ragged_selector_takes_192_row_tiles_only_within_one_round():
+    """Large ragged calls use 256x256 tiles, or 192x256 when those still make at most
+    one round of 256 compute units (a host-side bound on the tile count)."""
+    # 8 slabs of 512 rows, N = 16384: at most 3 x 71 = 213 tiles of 192x256
+    p = F.plan(F.LAYOUT_N_OFFSETS, False, 8, 512, 16384, 7168)
+    assert (p["BM"], p["BN"]) == (192, 256) and p["m_tiles"] * p["n_tiles"] <= 256
+    # 2048-row slabs: 11 x 71 tiles would take several rounds
+    p = F.plan(F.LAYOUT_N_OFFSETS, False, 8, 2048, 16384, 7168)
+    assert (p["BM"], p["BN"]) == (256, 256)
+    # k_offsets, the weight-gradient shape: 8 x 8 x 28 tiles of 256x256
+    p = F.plan(F.LAYOUT_K_OFFSETS, False, 8, 2048, 7168, 4096)
+    assert (p["BM"], p["BN"]) == (256, 256)
+    # a small k_offsets call that fits one round either way
+    p = F.plan(F.LAYOUT_K_OFFSETS, False, 2, 512, 1024, 4096)
+    assert (p["BM"], p["BN"]) == (192, 256) and p["grid"] == 2 * 3 * 4
+
+
 def test_plan_k_offsets_always_masks_the_tail():
     p = F.plan(F.LAYOUT_K_OFFSETS, False, 8, 2048, 7168, 4096)
     assert p["k_tail"] == 1 and p["persistent"] == 0
