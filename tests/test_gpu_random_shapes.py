@@ -205,3 +205,74 @@ def test_random_shape_matches_oracle(F, case):
             torch.cuda.synchronize()
         P.check_guards(whole)
         P.assert_rows_match(P.bits_of(y), ref, label=f"case {case}")
+
+
+BS_KINDS = ["stacked", "stacked_pre", "offsets", "offsets_pre", "batched", "batched_pre", "padded", "padded_pre"]
+N_BS_CASES = 64
+
+
+def run_blockscale(F, kind, XQ, WQ, xs, ws, meta, out_shape, zeroing=True):
+    """One block-scaled call on device copies; returns the output bits (guards checked)."""
+    pre = kind.endswith("_pre")
+    base = kind[:-4] if pre else kind
+    whole, y = P.guarded_output(out_shape)
+    W = F.f8f8bf16_shuffle_b(P.dev(WQ)) if pre else P.dev(WQ)
+    fn = getattr(F, f"f8f8bf16_groupwise_grouped_{'dynamic' if base == 'padded' else base}"
+                    + ("_preshuffle" if pre else ""))
+    if base == "batched":
+        fn(P.dev(XQ), W, P.dev(xs), P.dev(ws), out=y)
+    elif base == "padded":
+        fn(P.dev(XQ), W, P.dev(xs), P.dev(ws), P.dev(meta), zeroing_output_tensor=zeroing, out=y)
+    else:
+        fn(P.dev(XQ), W, P.dev(xs), P.dev(ws), P.dev(meta), out=y)
+    torch.cuda.synchronize()
+    P.check_guards(whole)
+    return P.bits_of(y)
+
+
+@pytest.mark.parametrize("case", range(N_BS_CASES))
+def test_random_blockscale_matches_oracle(F, case):
+    """Block scales on every layout, plain or pre-shuffled W: random group counts and
+    sizes (empty groups included), N and K whole 128-wide blocks, the default or a
+    forced tile configuration (the persistent one only where the layout takes it)."""
+    rng = np.random.default_rng(13000 + case)
+    kind = BS_KINDS[case % len(BS_KINDS)]
+    base = kind[:-4] if kind.endswith("_pre") else kind
+    G = int(rng.integers(1, 9))
+    N = 128 * int(rng.integers(1, 6))
+    K = 128 * int(rng.integers(1, 7))
+    seed = 13500 + case
+    cfg = None if rng.random() < 0.35 else int(rng.integers(0, 2 if base == "padded" else 3))
+    if base in ("stacked", "offsets"):
+        sizes = sizes_with_empties(rng, G, 300)
+        w = wl.make_stacked_blockscale(sizes, N, K, seed=seed)
+        offs = np.cumsum(sizes).astype(np.int32)
+        print(f"case bs{case}: {kind} G={G} sizes={sizes.tolist()} N={N} K={K} cfg={cfg}", flush=True)
+        if base == "stacked":
+            ref = oracle.grouped_stacked_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes)
+            meta = w.M_sizes
+        else:
+            ref = oracle.grouped_offsets_blockscale(w.XQ, w.WQ, w.x_scale, w.w_scale, offs)
+            meta = offs
+        with env("FP8GG_BS_CONFIG", cfg):
+            got = run_blockscale(F, kind, w.XQ, w.WQ, w.x_scale, w.w_scale, meta, (int(sizes.sum()), N))
+        P.assert_rows_match(got, ref, label=f"case bs{case}")
+    else:
+        em = int(rng.integers(1, 300))
+        if base == "batched":
+            z = np.full(G, em, np.int64)
+        else:
+            z = rng.integers(0, em + 1, G).astype(np.int64)
+            z[rng.random(G) < 0.2] = 0
+        zeroing = bool(rng.random() < 0.5)
+        d = wl.make_dynamic_blockscale(z, em, N, K, seed=seed)
+        print(f"case bs{case}: {kind} G={G} em={em} valid={z.tolist()} zeroing={zeroing} N={N} K={K} cfg={cfg}",
+              flush=True)
+        if base == "batched":
+            ref = oracle.grouped_batched_blockscale(d.XQ, d.WQ, d.x_scale, d.w_scale)
+        else:
+            ref = oracle.grouped_dynamic_blockscale(d.XQ, d.WQ, d.x_scale, d.w_scale, d.zero_start_index_M, zeroing)
+        with env("FP8GG_BS_CONFIG", cfg):
+            got = run_blockscale(F, kind, d.XQ, d.WQ, d.x_scale, d.w_scale, d.zero_start_index_M, (G, em, N),
+                                 zeroing)
+        P.assert_rows_match(got.reshape(G * em, N), ref, label=f"case bs{case}")
