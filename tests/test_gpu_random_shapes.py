@@ -3,8 +3,9 @@
 The edge-case lists elsewhere pick their shapes by hand; these cases draw them: a
 layout (stacked, offsets, batched, padded with either zeroing flag, each with plain
 or pre-shuffled W where the layout takes it, n_offsets, k_offsets, block-scaled
-stacked), a group count, group sizes with empty groups, N and K off every tile
-multiple, and either the default configuration or a forced one drawn from those the
+stacked; and, in a second set, block scales on the stacked, offsets, batched and
+padded layouts with plain or pre-shuffled W), a group count, group sizes with empty
+groups, N and K off every tile multiple (whole 128-wide blocks under block scales), and either the default configuration or a forced one drawn from those the
 planner accepts.  Every case is compared with the oracle element by element, with
 the sentinel and guard-band checks of the other parity tests.  The draws are fixed
 by the case number, so a failure names a reproducible shape.
