@@ -3,10 +3,11 @@
 Every call only enqueues kernels on the caller's stream (no allocation, copy,
 memset or synchronisation), so a sequence of calls can be captured into one HIP
 graph.  The graphs here hold an n_offsets, a k_offsets, a block-scaled and a
-quantiser call, and a pre-shuffled stacked call (persistent grid) with a padded
-call that zeroes its padding rows; each is replayed several times with eager work
-on other buffers in between, and every replay must reproduce the eager results
-bit for bit.
+quantiser call, a pre-shuffled stacked call (persistent grid) with a padded call
+that zeroes its padding rows, and a decode-sized call (register kernel) with the
+offsets and batched layouts, a K = 0 call and the weight shuffle; each is replayed
+several times with eager work on other buffers in between, and every replay must
+reproduce the eager results bit for bit.
 """
 import numpy as np
 import pytest
@@ -126,5 +127,67 @@ def test_preshuffled_and_padded_entry_points_under_graph_replay(F):
         g.replay()
         torch.cuda.synchronize()
         for name, o, e in zip(("stacked_preshuffle", "dynamic"), outs, eager):
+            assert torch.equal(o.view(torch.uint8), e.view(torch.uint8)), \
+                f"replay {rep}: {name} differs from the eager result"
+
+
+def test_decode_offsets_batched_zero_fill_and_shuffle_under_graph_replay(F):
+    """The calls a decode step or a weight reload would capture: one token over eight
+    groups (the small-M register kernel), the offsets and batched layouts, a call with
+    K = 0 (the zero-fill kernel) and the weight shuffle."""
+    dec = wl.make_stacked([0, 0, 1, 0, 0, 0, 0, 0], 1024, 512, seed=1420)
+    off = wl.make_stacked([37, 0, 130, 64], 264, 336, seed=1421)
+    bat = wl.make_dynamic([77, 77, 77], 77, 256, 448, seed=1422)
+    assert F.plan(F.LAYOUT_STACKED, False, 8, 1, 1024, 512)["config_id"] in (13, 14, 15)   # the register kernel
+    din = [P.dev(a) for a in (dec.XQ, dec.WQ, dec.x_scale, dec.w_scale, dec.M_sizes)]
+    oin = [P.dev(a) for a in (off.XQ, off.WQ, off.x_scale, off.w_scale)] + \
+        [P.dev(np.cumsum(off.M_sizes).astype(np.int32))]
+    bin_ = [P.dev(a) for a in (bat.XQ, bat.WQ, bat.x_scale, bat.w_scale)]
+    zin = [torch.empty((40, 0), dtype=torch.uint8, device="cuda"), torch.empty((2, 96, 0), dtype=torch.uint8,
+                                                                               device="cuda"),
+           torch.empty((40,), dtype=torch.float32, device="cuda"), torch.ones((2, 96), device="cuda"),
+           P.dev(np.array([25, 15], np.int64))]
+    yd = torch.empty((1, 1024), dtype=torch.bfloat16, device="cuda")
+    yo = torch.empty((off.total_M, off.N), dtype=torch.bfloat16, device="cuda")
+    yb = torch.empty((bat.G, bat.expected_m, bat.N), dtype=torch.bfloat16, device="cuda")
+    yz = torch.empty((40, 96), dtype=torch.bfloat16, device="cuda")
+    wsrc = P.dev(bat.WQ)                           # N = 256, K = 448: whole shuffle granules
+    ws = torch.empty_like(wsrc)
+    outs = (yd, yo, yb, yz, ws)
+
+    def calls():
+        F.f8f8bf16_rowwise_grouped_stacked(*din, out=yd)
+        F.f8f8bf16_rowwise_grouped_offsets(*oin, out=yo)
+        F.f8f8bf16_rowwise_grouped_batched(*bin_, out=yb)
+        F.f8f8bf16_rowwise_grouped_stacked(*zin, out=yz)
+        F.f8f8bf16_shuffle_b(wsrc, out=ws)
+
+    def reset():
+        for o in outs:
+            o.view(torch.uint8).fill_(0xC1)
+
+    reset()
+    calls()
+    torch.cuda.synchronize()
+    eager = [o.clone() for o in outs]
+    assert bool((yz.view(torch.int16) == 0).all()), "K = 0 did not zero-fill the output"
+
+    stream = torch.cuda.Stream()
+    stream.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(stream):
+        calls()
+    torch.cuda.current_stream().wait_stream(stream)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        calls()
+    scratch = torch.zeros(1 << 20, device="cuda")
+    for rep in range(3):
+        reset()
+        scratch.add_(1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for name, o, e in zip(("decode", "offsets", "batched", "zero fill", "shuffle"), outs, eager):
             assert torch.equal(o.view(torch.uint8), e.view(torch.uint8)), \
                 f"replay {rep}: {name} differs from the eager result"
