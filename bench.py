@@ -17,8 +17,12 @@ then exactly K timed calls bracketed by device synchronisation.  Each call is
 also bracketed by HIP events recorded on the stream the kernel runs on, which
 gives the kernel's average duration for the roofline figure.  When a workload's
 bytes are small against the 256 MB Infinity Cache, calls rotate over several
-copies of the inputs.  Decode-sized calls (the down-projection sweep) are timed
-under graph replay.
+copies of the inputs.  The same calls are then also timed under graph replay:
+enough calls captured into one HIP graph for a replay to last about 2 ms, a clock
+ramp of replays, then seven replays each bracketed by HIP events; the median per
+call is reported with its minimum, interquartile range and T*/T (T* the roofline
+time of the call).  The extra keys (plain weights, gate_up, padded tails, the
+down-projection sweep, the quantiser) are timed that way only.
 """
 from __future__ import annotations
 
@@ -282,26 +286,40 @@ def ramp(fn, seconds, batch):
     return time.perf_counter() - t0, i
 
 
-def graph_us_per_call(torch, call, calls_per_graph, ramp_s, replays=20):
-    """Per-call time of `calls_per_graph` calls captured into one HIP graph,
-    replayed after a clock ramp; HIP events around the replays."""
-    for i in range(calls_per_graph):
-        call(i)
+def graph_stats(torch, call, ramp_s, flop, nbytes, target_us=2000.0, replays=7):
+    """Per-call time under graph replay: enough calls captured into one HIP graph for
+    a replay to last about `target_us`, replayed for a clock ramp, then `replays`
+    replays each bracketed by HIP events.  Returns the median per-call time with its
+    minimum and interquartile range, and T*/T for the roofline time
+    T* = max(flop / fp8 peak, bytes / HBM peak)."""
+    call(0)
     torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        for i in range(calls_per_graph):
-            call(i)
-    ramp(lambda i: g.replay(), ramp_s, 2)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for _ in range(replays):
-        g.replay()
+    for i in range(3):
+        call(i)
     e1.record()
     torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / (replays * calls_per_graph)
+    est_us = max(e0.elapsed_time(e1) * 1e3 / 3, 1.0)
+    n = max(1, min(512, math.ceil(target_us / est_us)))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(n):
+            call(i)
+    ramp(lambda i: g.replay(), ramp_s, 2)
+    per_call = []
+    for _ in range(replays):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        per_call.append(e0.elapsed_time(e1) * 1e3 / n)
     del g
-    return us
+    q1, _, q3 = statistics.quantiles(per_call, n=4)
+    med = statistics.median(per_call)
+    t_star = max(flop / (PEAK_FP8_TFLOPS * 1e6), nbytes / (PEAK_HBM_GBS * 1e3))   # µs
+    return {"us_per_call": round(med, 3), "us_min": round(min(per_call), 3), "us_iqr": round(q3 - q1, 3),
+            "calls_per_graph": n, "replays": replays, "t_star_over_t": round(t_star / med, 4)}
 
 
 def prepare(F, torch, w, layout, pre, rotate):
@@ -409,19 +427,26 @@ def auto_rotate(nbytes):
     return max(1, min(64, math.ceil(2 * MALL_BYTES / max(nbytes, 1))))
 
 
-def extra_workload(F, torch, name, ramp_s, steps=50):
-    """A further workload timed like the headline one (clock ramp, eager calls with
-    HIP events around each), for the extra keys of the JSON line."""
+def rates(flop, nbytes, us):
+    """TFLOP/s over valid rows and GB/s of algorithmic bytes at `us` per call, with
+    their fractions of the fp8 MFMA and HBM peaks."""
+    return {"TFLOP_per_s": round(flop / us / 1e6, 1), "mfma_frac": round(flop / us / 1e6 / PEAK_FP8_TFLOPS, 4),
+            "GB_per_s": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4)}
+
+
+def extra_workload(F, torch, name, ramp_s):
+    """A further workload for the extra keys of the JSON line, timed under graph
+    replay (median of seven replays with min and IQR, rotating over enough input
+    copies to defeat the Infinity Cache)."""
     w, layout, pre = make_workload(name)
     flop, nbytes, R, _ = algorithmic_work(w, layout)
-    call = prepare(F, torch, w, layout, pre, auto_rotate(nbytes))
-    t = time_eager(torch, call, steps, 5, ramp_s)
-    avg = t["avg"]
-    r = {"workload": w.name, "us_per_call": round(avg * 1e6, 3), "TFLOP_per_s": round(flop / avg / 1e12, 1),
-         "mfma_frac": round(flop / avg / 1e12 / PEAK_FP8_TFLOPS, 4), "GB_per_s": round(nbytes / avg / 1e9, 1),
-         "hbm_frac": round(nbytes / avg / 1e9 / PEAK_HBM_GBS, 4)}
-    log(f"{name}: {avg * 1e6:.2f} us/call, {r['TFLOP_per_s']} TFLOP/s ({r['mfma_frac']:.1%}), "
-        f"{r['GB_per_s']} GB/s ({r['hbm_frac']:.1%})")
+    rot = auto_rotate(nbytes)
+    call = prepare(F, torch, w, layout, pre, rot)
+    st = graph_stats(torch, call, ramp_s, flop, nbytes)
+    r = {"workload": w.name, **st, **rates(flop, nbytes, st["us_per_call"]), "input_copies": rot}
+    log(f"{name}: {st['us_per_call']:.2f} us/call (min {st['us_min']:.2f}, IQR {st['us_iqr']:.2f}), "
+        f"{r['TFLOP_per_s']} TFLOP/s ({r['mfma_frac']:.1%}), {r['GB_per_s']} GB/s ({r['hbm_frac']:.1%}), "
+        f"T*/T {st['t_star_over_t']:.2f}")
     del call
     torch.cuda.empty_cache()
     return r
@@ -438,14 +463,12 @@ def small_m_us_per_call(F, torch, ramp_s, totals=(1, 8, 32, 256, 2048, 8192)):
         flop, nbytes, _, _ = algorithmic_work(w, "stacked")
         rot = auto_rotate(nbytes)
         call = prepare(F, torch, w, "stacked", False, rot)
-        per_graph = 64 if m <= 256 else 16
-        us = graph_us_per_call(torch, call, per_graph, ramp_s)
-        out[f"moe_down_M{m}"] = {"us_per_call": round(us, 3), "GB_per_s": round(nbytes / us / 1e3, 1),
-                                 "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
-                                 "TFLOP_per_s": round(flop / us / 1e6, 1),
-                                 "mfma_frac": round(flop / us / 1e6 / PEAK_FP8_TFLOPS, 4), "input_copies": rot}
-        log(f"down-proj M={m}: {us:.2f} us/call under graph replay ({nbytes / us / 1e3:.0f} GB/s, "
-            f"{flop / us / 1e6:.0f} TFLOP/s, {rot} input copies)")
+        st = graph_stats(torch, call, ramp_s, flop, nbytes)
+        us = st["us_per_call"]
+        out[f"moe_down_M{m}"] = {**st, **rates(flop, nbytes, us), "input_copies": rot}
+        log(f"down-proj M={m}: {us:.2f} us/call under graph replay (min {st['us_min']:.2f}, IQR "
+            f"{st['us_iqr']:.2f}; {nbytes / us / 1e3:.0f} GB/s, {flop / us / 1e6:.0f} TFLOP/s, {rot} input copies, "
+            f"T*/T {st['t_star_over_t']:.2f})")
         del call
         torch.cuda.empty_cache()
     return out
@@ -468,13 +491,14 @@ def quantize_us_per_call(F, torch, ramp_s, rows=4096, K=7168, calls=200):
 
     def call(i):
         F.f8f8bf16_quantize_rowwise(xs[i % rot], qs[i % rot], ss[i % rot])
-    t = time_eager(torch, call, calls, 20, ramp_s)
-    us = t["avg"] * 1e6
+    st = graph_stats(torch, call, ramp_s, 0, nbytes)
+    us = st["us_per_call"]
     gbs = nbytes / us / 1e3
-    log(f"quantize: bf16 [{rows}, {K}] -> e4m3fn: {us:.2f} us/call ({gbs:.0f} GB/s, {rot} input copies)")
+    log(f"quantize: bf16 [{rows}, {K}] -> e4m3fn: {us:.2f} us/call under graph replay (min {st['us_min']:.2f}, "
+        f"IQR {st['us_iqr']:.2f}; {gbs:.0f} GB/s, {rot} input copies)")
     del xs, qs, ss
-    return {"shape": [rows, K], "us_per_call": round(us, 3), "GB_per_s": round(gbs, 1),
-            "hbm_frac": round(gbs / PEAK_HBM_GBS, 4), "input_copies": rot}
+    return {"shape": [rows, K], **st, "GB_per_s": round(gbs, 1), "hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "input_copies": rot}
 
 
 def copy_calibration(nbytes):
@@ -546,6 +570,10 @@ def main():
     roof = roofline_of(flop, nbytes, avg, measured_traffic(args.workload, src_hash))
     log(f"kernel: {flop / avg / 1e12:.1f} TFLOP/s ({flop / avg / 1e12 / PEAK_FP8_TFLOPS:.1%} of fp8 peak), "
         f"{nbytes / avg / 1e9:.0f} GB/s ({nbytes / avg / 1e9 / PEAK_HBM_GBS:.1%} of HBM); source hash {src_hash}")
+    # the same calls under graph replay (median of seven replays, min, IQR, T*/T)
+    graph = graph_stats(torch, call, min(ramp_s, 0.5), flop, nbytes)
+    log(f"graph replay: {graph['us_per_call']:.2f} us/call (min {graph['us_min']:.2f}, IQR {graph['us_iqr']:.2f}, "
+        f"{graph['calls_per_graph']} calls per replay), T*/T {graph['t_star_over_t']:.2f}")
     del call
     torch.cuda.empty_cache()
 
@@ -578,6 +606,7 @@ def main():
             "us_per_call_median": round(t["median"] * 1e6, 3),
             "clock_ramp_s": round(t["ramp_s"], 3),
             "clock_ramp_calls": t["ramp_calls"],
+            "graph_replay": {**graph, **rates(flop, nbytes, graph["us_per_call"])},
         },
         "roofline": roof,
     }
