@@ -474,11 +474,13 @@ def small_m_us_per_call(F, torch, ramp_s, totals=(1, 8, 32, 256, 2048, 8192)):
     return out
 
 
-def quantize_us_per_call(F, torch, ramp_s, rows=4096, K=7168, calls=200):
+def quantize_us_per_call(F, torch, ramp_s, rows=4096, K=7168, eager_steps=0, warmup=20):
     """The rowwise activation quantiser (bf16 [rows, K] -> e4m3fn codes + fp32 row
     scales) on the gate_up activations' shape, rotating over enough input copies to
     defeat the Infinity Cache.  HBM-bound: 2 bytes read and 1 written per element,
-    4 bytes written per row."""
+    4 bytes written per row.  Timed under graph replay, or, with eager_steps > 0,
+    as that many eager calls with HIP events around each (for profiler runs, whose
+    counters are taken per dispatch)."""
     dev = torch.device("cuda", 0)
     nbytes = 3 * rows * K + 4 * rows
     rot = max(1, min(16, math.ceil(2 * MALL_BYTES / nbytes)))
@@ -491,6 +493,15 @@ def quantize_us_per_call(F, torch, ramp_s, rows=4096, K=7168, calls=200):
 
     def call(i):
         F.f8f8bf16_quantize_rowwise(xs[i % rot], qs[i % rot], ss[i % rot])
+    if eager_steps > 0:
+        t = time_eager(torch, call, eager_steps, warmup, ramp_s)
+        us = t["avg"] * 1e6
+        log(f"quantize: bf16 [{rows}, {K}] -> e4m3fn: {us:.2f} us/call over {eager_steps} eager calls "
+            f"({nbytes / us / 1e3:.0f} GB/s, {rot} input copies)")
+        del xs, qs, ss
+        return {"shape": [rows, K], "us_per_call": round(us, 3), "eager_calls": eager_steps,
+                "GB_per_s": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / PEAK_HBM_GBS, 4),
+                "input_copies": rot}
     st = graph_stats(torch, call, ramp_s, 0, nbytes)
     us = st["us_per_call"]
     gbs = nbytes / us / 1e3
@@ -530,6 +541,9 @@ def main():
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the extra workloads (plain W, gate_up, padded tails, down-proj sweep, quantiser)")
     ap.add_argument("--no-small-m", action="store_true", help="same as --no-extras")
+    ap.add_argument("--quantize-only", action="store_true",
+                    help="time only the rowwise activation quantiser, as --steps eager calls after --warmup "
+                         "(for profiler runs); prints {\"quantize\": ...}")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain copy of this many bytes (for counter calibration)")
     args = ap.parse_args()
@@ -552,6 +566,10 @@ def main():
     import fp8_rowwise_scaled_amd as F
 
     F.load()
+    if args.quantize_only:
+        print(json.dumps({"quantize": quantize_us_per_call(F, torch, ramp_s, eager_steps=max(1, args.steps),
+                                                           warmup=args.warmup)}), flush=True)
+        return
     w, layout, pre = make_workload(args.workload)
     flop, nbytes, R, G_ne = algorithmic_work(w, layout)
     log(f"workload {w.name}: layout={layout} preshuffled={pre} G={w.G} N={w.N} K={w.K} R={R} G_ne={G_ne} "
