@@ -526,6 +526,11 @@ static fp8gg_status groupwise(int layout, int preshuffled, const uint8_t* XQ, co
   }
   a.n_tiles = (N + BN - 1) / BN;
   a.zeroing = padded && zeroing ? 1 : 0;
+  // The padded layout's 128x256 grid in XCD order, as for rowwise scaling (each XCD
+  // holds whole groups: 79.3-80.0 against 81.8-82.6 us on the padded block-scaled
+  // workload, HBM reads of each group's W no longer repeated on every XCD).
+  // FP8GG_XCD overrides for measurements.
+  a.xcd_group = env_int("FP8GG_XCD", padded && cfg == 0 ? 1 : 0) ? 1 : 0;
   // persistent: one workgroup per compute unit (FP8GG_TAIL_GRID overrides it for tests)
   const int forced_grid = env_int("FP8GG_TAIL_GRID", 0);
   const int64_t grid = cfg == fp8gg::kBlockscalePersistent ? (forced_grid > 0 ? forced_grid : device_cus())

@@ -1121,7 +1121,8 @@ gg_blockscale_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
   __shared__ __attribute__((aligned(16))) float sc[STAGES * BlockscaleSlots<BM>::SC];
   __shared__ __attribute__((aligned(16))) float sc_dummy[64];
-  const int64_t bid = blockIdx.x;
+  // xcd_group: each XCD takes a contiguous eighth of the tile order
+  const int64_t bid = a.xcd_group ? xcd_slot(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
   const int64_t n0 = (bid % a.n_tiles) * BN;
   const int64_t rest = bid / a.n_tiles;
   Tile t;

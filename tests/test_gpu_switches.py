@@ -1,8 +1,8 @@
 """GPU tests of the two scheduling switches that only reorder or skip work.
 
-* FP8GG_XCD: the padded layout's data-parallel grid hands each XCD a contiguous
-  eighth of its tiles (the default) instead of every eighth tile.  Every tile is
-  still computed by one workgroup in the same K order.
+* FP8GG_XCD: the padded layout's data-parallel grid (rowwise and block-scaled)
+  hands each XCD a contiguous eighth of its tiles (the default) instead of every
+  eighth tile.  Every tile is still computed by one workgroup in the same K order.
 * FP8GG_SKIP_DEAD: a wave whose rows all lie past its tile's group reads no
   fragments and issues no MFMAs (the default); those outputs are never stored.
 
@@ -86,6 +86,35 @@ def test_padded_xcd_order_is_bitwise_neutral(F, env, zeroing, K):
     P.assert_rows_match(got.reshape(-1, w.N), ref, label=f"padded xcd order K={K}")
     env("FP8GG_XCD", 0)
     assert np.array_equal(run_padded(F, w, zeroing), got)
+
+
+@pytest.mark.parametrize("zeroing", [True, False])
+@pytest.mark.parametrize("pre", [False, True])
+def test_padded_blockscale_xcd_order_is_bitwise_neutral(F, env, zeroing, pre):
+    """The block-scaled padded grid in XCD order (its default for 128x256 tiles):
+    16 slabs of 512 rows, N = 1024, K = 1024 (whole 128-wide blocks)."""
+    zsi = np.array([0, 512, 141, 272, 339, 132, 218, 294, 393, 466, 259, 272, 455, 300, 169, 61], np.int64)
+    d = wl.make_dynamic_blockscale(zsi, 512, 1024, 1024, seed=7800)
+    ref = oracle.grouped_dynamic_blockscale(d.XQ, d.WQ, d.x_scale, d.w_scale, d.zero_start_index_M, zeroing)
+    args = [P.dev(a) for a in (d.XQ, d.WQ, d.x_scale, d.w_scale, d.zero_start_index_M)]
+    fn = F.f8f8bf16_groupwise_grouped_dynamic
+    if pre:
+        args[1] = F.f8f8bf16_shuffle_b(args[1])
+        fn = F.f8f8bf16_groupwise_grouped_dynamic_preshuffle
+
+    def run():
+        whole, out = P.guarded_output((d.G, d.expected_m, d.N))
+        fn(*args, zeroing_output_tensor=zeroing, out=out)
+        torch.cuda.synchronize()
+        P.check_guards(whole)
+        return P.bits_of(out)
+
+    print(f"case padded blockscale xcd pre={pre} zeroing={zeroing}", flush=True)
+    env("FP8GG_XCD", None)
+    got = run()
+    P.assert_rows_match(got.reshape(-1, d.N), ref, label=f"padded blockscale xcd order pre={pre}")
+    env("FP8GG_XCD", 0)
+    assert np.array_equal(run(), got)
 
 
 # (pre-shuffled W, forced configuration, persistent grid): the default plan is the
