@@ -339,12 +339,18 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
   a.zeroing = layout == FP8GG_LAYOUT_PADDED && zeroing ? 1 : 0;
   {
     // Tile order across the XCDs (performance only; results do not depend on it):
-    // the padded layout's data-parallel grid gives each XCD a contiguous eighth of
+    // the padded layout's data-parallel grid gives each XCD a contiguous share of
     // its tiles, so that the XCD holds whole groups (measured 2% faster on the
-    // padded tails workload; no gain on the stacked workloads).  FP8GG_XCD
-    // overrides for measurements (0 = plain order).
+    // padded tails workload; no gain on the stacked workloads), and so does the
+    // n_offsets grid, whose column tiles of one slab then share its X on one XCD
+    // (88.0-88.3 against 90.7-90.9 us on the n_offsets workload).  Not k_offsets:
+    // its groups, whose K slices differ in length, would each land on one XCD
+    // (285 against 137 us).  FP8GG_XCD overrides for measurements (0 = plain order).
     const fp8gg::KernelConfig& c0 = fp8gg::kConfigs[p.config_id];
-    const int xg = layout == FP8GG_LAYOUT_PADDED && c0.kind == fp8gg::kKindLds && c0.BM >= 128 ? 1 : 0;
+    const int xg = (layout == FP8GG_LAYOUT_PADDED && c0.kind == fp8gg::kKindLds && c0.BM >= 128) ||
+                           layout == FP8GG_LAYOUT_N_OFFSETS
+                       ? 1
+                       : 0;
     a.xcd_group = env_int("FP8GG_XCD", xg) ? 1 : 0;
   }
   a.skip_dead = env_int("FP8GG_SKIP_DEAD", 1) ? 1 : 0;

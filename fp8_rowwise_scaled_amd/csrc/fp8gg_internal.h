@@ -28,7 +28,7 @@ struct GemmArgs {
   int64_t m_tiles;       // packed: upper bound of M tiles over all groups; padded: per slab
   int64_t n_tiles;
   int32_t zeroing;       // padded: write zeros into padding rows
-  int32_t xcd_group;     // data-parallel grid: 1 = each XCD takes a contiguous eighth of the tiles (xcd_slot)
+  int32_t xcd_group;     // one-tile-per-workgroup grids: 1 = each XCD takes a contiguous share of the tiles (xcd_slot)
   int32_t skip_dead;     // 1: waves whose rows all lie past the tile's group issue no MFMAs
 };
 

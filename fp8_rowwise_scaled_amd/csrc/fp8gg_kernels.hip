@@ -412,13 +412,14 @@ __device__ __forceinline__ bool resolve_k_offsets(const GemmArgs& a, int64_t b, 
 // Tile order across the XCDs.  MI355X dispatches consecutive workgroups of a grid
 // to its eight XCDs in turn, and each XCD has its own L2, so workgroup w runs on
 // XCD w % 8.  xcd_slot only reorders work (every tile is still computed by one
-// workgroup in the same K order, so results do not depend on it): within P
-// consecutive workgroups (P a multiple of 8) it gives workgroup w position
-// (w % 8) * (P / 8) + w / 8, so that XCD x takes the contiguous positions
-// [x * P / 8, (x + 1) * P / 8) and the workgroups running together on one XCD
-// share operands.
+// workgroup in the same K order, so results do not depend on it): of a grid of P
+// workgroups, XCD x runs workgroups x, x + 8, ..., ceil((P - x) / 8) of them, and
+// xcd_slot gives them the contiguous positions that follow those of XCDs
+// 0 .. x-1 (a permutation of [0, P) for any P), so that the workgroups running
+// together on one XCD share operands.
 __device__ __forceinline__ int64_t xcd_slot(int64_t w, int64_t P) {
-  return (P % 8 == 0) ? (w % 8) * (P / 8) + w / 8 : w;
+  const int64_t x = w % 8, q = P / 8, r = P % 8;
+  return x * q + (x < r ? x : r) + w / 8;
 }
 
 // ---------------------------------------------------------------------------
@@ -829,7 +830,7 @@ gg_lds_kernel(GemmArgs a) {
   typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL, PRE> E;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
 
-  // xcd_group: each XCD takes a contiguous eighth of the tile order
+  // xcd_group: each XCD takes a contiguous share of the tile order
   const int64_t bid = a.xcd_group ? xcd_slot(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
   const int64_t n_tile = bid % a.n_tiles;
   const int64_t rest = bid / a.n_tiles;
@@ -871,10 +872,12 @@ gg_ragged_kernel(GemmArgs a) {
   typedef LdsTile<BM, BN, BK, WM, WN, STAGES, KTAIL, false> E;
   __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
   RaggedTile t;
+  // xcd_group: each XCD takes a contiguous share of the tile order
+  const int64_t bid = a.xcd_group ? xcd_slot(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
   if constexpr (LAYOUT == kNOffsets) {
-    if (!resolve_n_offsets<BM, BN>(a, blockIdx.x, t)) return;
+    if (!resolve_n_offsets<BM, BN>(a, bid, t)) return;
   } else {
-    if (!resolve_k_offsets<BM, BN>(a, blockIdx.x, t)) return;
+    if (!resolve_k_offsets<BM, BN>(a, bid, t)) return;
   }
   E e;
   e.init(smem);
@@ -1121,7 +1124,7 @@ gg_blockscale_kernel(GemmArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[E::SMEM_BYTES];
   __shared__ __attribute__((aligned(16))) float sc[STAGES * BlockscaleSlots<BM>::SC];
   __shared__ __attribute__((aligned(16))) float sc_dummy[64];
-  // xcd_group: each XCD takes a contiguous eighth of the tile order
+  // xcd_group: each XCD takes a contiguous share of the tile order
   const int64_t bid = a.xcd_group ? xcd_slot(blockIdx.x, gridDim.x) : (int64_t)blockIdx.x;
   const int64_t n0 = (bid % a.n_tiles) * BN;
   const int64_t rest = bid / a.n_tiles;

@@ -1,8 +1,9 @@
 """GPU tests of the two scheduling switches that only reorder or skip work.
 
-* FP8GG_XCD: the padded layout's data-parallel grid (rowwise and block-scaled)
-  hands each XCD a contiguous eighth of its tiles (the default) instead of every
-  eighth tile.  Every tile is still computed by one workgroup in the same K order.
+* FP8GG_XCD: the padded layout's data-parallel grid (rowwise and block-scaled) and
+  the n_offsets grid hand each XCD a contiguous share of their tiles (the default)
+  instead of every eighth tile.  Every tile is still computed by one workgroup in
+  the same K order.
 * FP8GG_SKIP_DEAD: a wave whose rows all lie past its tile's group reads no
   fragments and issues no MFMAs (the default); those outputs are never stored.
 
@@ -86,6 +87,36 @@ def test_padded_xcd_order_is_bitwise_neutral(F, env, zeroing, K):
     P.assert_rows_match(got.reshape(-1, w.N), ref, label=f"padded xcd order K={K}")
     env("FP8GG_XCD", 0)
     assert np.array_equal(run_padded(F, w, zeroing), got)
+
+
+@pytest.mark.parametrize("G,M,cfg", [(8, 512, None), (5, 300, 9), (12, 40, 18), (3, 64, 2)])
+def test_n_offsets_xcd_order_is_bitwise_neutral(F, env, G, M, cfg):
+    """The n_offsets grid in XCD order (its default), on grids that are and are not
+    multiples of 8: ragged column groups (one empty, one of 8 columns), an N tail."""
+    from tests.test_gpu_ragged import assert_cols_match
+    rng = np.random.default_rng(7900 + G)
+    widths = 8 * rng.integers(1, 60, G)
+    widths[0] = 0
+    widths[-1] = 8
+    w = wl.make_n_offsets(widths, M, 384, seed=7900 + G, total_N=int(widths.sum()) + 16)
+    offs = np.cumsum(widths).astype(np.int32)
+    ref = oracle.grouped_n_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, offs)
+    args = [P.dev(a) for a in (w.XQ, w.WQ, w.x_scale, w.w_scale)] + [P.dev(offs)]
+
+    def run():
+        whole, y = P.guarded_output((M, w.WQ.shape[0]))
+        F.f8f8bf16_rowwise_grouped_n_offsets(*args, out=y)
+        torch.cuda.synchronize()
+        P.check_guards(whole)
+        return P.bits_of(y)
+
+    print(f"case n_offsets xcd G={G} M={M} cfg={cfg}", flush=True)
+    env("FP8GG_CONFIG", cfg)
+    env("FP8GG_XCD", None)
+    got = run()
+    assert_cols_match(got, ref, f"n_offsets xcd order G={G}")
+    env("FP8GG_XCD", 0)
+    assert np.array_equal(run(), got)
 
 
 @pytest.mark.parametrize("zeroing", [True, False])
