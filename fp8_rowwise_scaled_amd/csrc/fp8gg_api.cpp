@@ -342,8 +342,9 @@ fp8gg_status run(int layout, int preshuffled, const uint8_t* XQ, const uint8_t* 
     // the padded layout's data-parallel grid gives each XCD a contiguous share of
     // its tiles, so that the XCD holds whole groups (measured 2% faster on the
     // padded tails workload; no gain on the stacked workloads), and so does the
-    // n_offsets grid, whose column tiles of one slab then share its X on one XCD
-    // (88.0-88.3 against 90.7-90.9 us on the n_offsets workload).  Not k_offsets:
+    // n_offsets grid, with its row tiles fastest, so that the row tiles reading one
+    // column tile of W run on one XCD (85.4-85.8 against 91.1-91.3 us on the
+    // n_offsets workload; XCD order with column tiles fastest: 88.1-88.3).  Not k_offsets:
     // its groups, whose K slices differ in length, would each land on one XCD
     // (285 against 137 us).  FP8GG_XCD overrides for measurements (0 = plain order).
     const fp8gg::KernelConfig& c0 = fp8gg::kConfigs[p.config_id];

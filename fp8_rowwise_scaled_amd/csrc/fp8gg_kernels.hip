@@ -328,11 +328,13 @@ __device__ __forceinline__ void prefix_ends8(const int32_t* offs, int64_t G, int
 
 // n_offsets: workgroup b takes column tile b % n_tiles (counted over the groups'
 // column ranges, BN per tile, an upper bound of them launched) and row tile
-// b / n_tiles of the group's slab.
+// b / n_tiles of the group's slab; with the XCD order (xcd_group) the row tile
+// runs fastest instead, so that the row tiles sharing a column tile's W are
+// consecutive and, within an XCD's contiguous share, share its L2.
 template <int BM, int BN>
 __device__ __forceinline__ bool resolve_n_offsets(const GemmArgs& a, int64_t b, RaggedTile& t) {
-  const int64_t n_tile = b % a.n_tiles;
-  const int64_t m_tile = b / a.n_tiles;
+  const int64_t n_tile = a.xcd_group ? b / a.m_tiles : b % a.n_tiles;
+  const int64_t m_tile = a.xcd_group ? b % a.m_tiles : b / a.n_tiles;
   int64_t start = 0, tiles_before = 0;
   for (int64_t g0 = 0; g0 < a.G; g0 += 8) {
     int64_t end[8], tiles[8];
