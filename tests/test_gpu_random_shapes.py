@@ -5,8 +5,11 @@ layout (stacked, offsets, batched, padded with either zeroing flag, each with pl
 or pre-shuffled W where the layout takes it, n_offsets, k_offsets, block-scaled
 stacked; and, in a second set, block scales on the stacked, offsets, batched and
 padded layouts with plain or pre-shuffled W), a group count, group sizes with empty
-groups, N and K off every tile multiple (whole 128-wide blocks under block scales), and either the default configuration or a forced one drawn from those the
-planner accepts.  Every case is compared with the oracle element by element, with
+groups, N and K off every tile multiple (whole 128-wide blocks under block scales),
+and either the default configuration or a forced one drawn from those the planner
+accepts.  A third set draws larger shapes (up to 16 groups of up to 1500 rows, N and
+K up to 2048) under the default selector, so that the persistent grid runs several
+rounds with its quarter tiles and remainder modes.  Every case is compared with the oracle element by element, with
 the sentinel and guard-band checks of the other parity tests.  The draws are fixed
 by the case number, so a failure names a reproducible shape.
 """
@@ -277,3 +280,55 @@ def test_random_blockscale_matches_oracle(F, case):
             got = run_blockscale(F, kind, d.XQ, d.WQ, d.x_scale, d.w_scale, d.zero_start_index_M, (G, em, N),
                                  zeroing)
         P.assert_rows_match(got.reshape(G * em, N), ref, label=f"case bs{case}")
+
+
+LARGE_KINDS = ["stacked", "stacked_pre", "offsets", "offsets_pre", "batched", "batched_pre", "padded", "padded_pre"]
+N_LARGE_CASES = 24
+
+
+@pytest.mark.parametrize("case", range(N_LARGE_CASES))
+def test_random_large_shape_matches_oracle(F, case):
+    """Larger shapes under the default selector: up to 16 groups of up to 1500 rows
+    (slabs of up to 1200), N and K up to 2048, so the persistent grid runs several
+    rounds and its quarter tiles (with the remainder mode sometimes forced)."""
+    rng = np.random.default_rng(50000 + case)
+    kind = LARGE_KINDS[case % len(LARGE_KINDS)]
+    pre = kind.endswith("_pre")
+    base = kind[:-4] if pre else kind
+    G = int(rng.integers(1, 17))
+    N = (32 if pre else 8) * int(rng.integers(1, (2048 // (32 if pre else 8)) + 1))
+    K = (64 if pre else 16) * int(rng.integers(1, (2048 // (64 if pre else 16)) + 1))
+    tail = None if rng.random() < 0.6 else int(rng.integers(0, 3))
+    seed = 60000 + case
+    with env("FP8GG_TAIL", tail):
+        if base in ("stacked", "offsets"):
+            sizes = rng.integers(0, 1500, G).astype(np.int64)
+            sizes[rng.random(G) < 0.15] = 0
+            w = wl.make_stacked(sizes, N, K, seed=seed)
+            print(f"case large{case}: {kind} G={G} sizes={sizes.tolist()} N={N} K={K} tail={tail}", flush=True)
+            offsets = np.cumsum(sizes).astype(np.int32)
+            ref = (oracle.grouped_stacked(w.XQ, w.WQ, w.x_scale, w.w_scale, w.M_sizes) if base == "stacked"
+                   else oracle.grouped_offsets(w.XQ, w.WQ, w.x_scale, w.w_scale, offsets))
+            got = run_packed(F, w, kind, offsets)
+            P.assert_rows_match(got, ref, label=f"large case {case}")
+            return
+        em = int(rng.integers(1, 1200))
+        z = np.full(G, em, np.int64) if base == "batched" else rng.integers(0, em + 1, G).astype(np.int64)
+        zeroing = bool(rng.random() < 0.5)
+        d = wl.make_dynamic(z, em, N, K, seed=seed)
+        print(f"case large{case}: {kind} G={G} em={em} valid={z.tolist()} zeroing={zeroing} N={N} K={K} "
+              f"tail={tail}", flush=True)
+        whole, out = P.guarded_output((G, em, N))
+        W = F.f8f8bf16_shuffle_b(P.dev(d.WQ)) if pre else P.dev(d.WQ)
+        if base == "batched":
+            fn = F.f8f8bf16_rowwise_grouped_batched_preshuffle if pre else F.f8f8bf16_rowwise_grouped_batched
+            fn(P.dev(d.XQ), W, P.dev(d.x_scale), P.dev(d.w_scale), out=out)
+            ref = oracle.grouped_batched(d.XQ, d.WQ, d.x_scale, d.w_scale)
+        else:
+            fn = F.f8f8bf16_rowwise_grouped_dynamic_preshuffle if pre else F.f8f8bf16_rowwise_grouped_dynamic
+            fn(P.dev(d.XQ), W, P.dev(d.x_scale), P.dev(d.w_scale), P.dev(d.zero_start_index_M),
+               zeroing_output_tensor=zeroing, out=out)
+            ref = oracle.grouped_dynamic(d.XQ, d.WQ, d.x_scale, d.w_scale, d.zero_start_index_M, zeroing)
+        torch.cuda.synchronize()
+        P.check_guards(whole)
+        P.assert_rows_match(P.bits_of(out).reshape(G * em, N), ref, label=f"large case {case}")
