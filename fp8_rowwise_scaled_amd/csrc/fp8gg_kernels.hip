@@ -1359,12 +1359,16 @@ gg_skinny_kernel(GemmArgs a) {
     }
   }
 
-  // Partial sums of waves 1..3 -> LDS; wave 0 adds them in wave order.
+  // Partial sums of waves 1..3 -> LDS as 16-byte quarters (one ds_write_b128 /
+  // ds_read_b128 per four accumulators); wave 0 adds them in wave order.
+  v4f* red4 = reinterpret_cast<v4f*>(red);
   if (wave > 0) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) red[(((wave - 1) * FM + fm) * 16 + i) * 64 + lane] = acc[fm][i];
+      for (int q = 0; q < 4; ++q)
+        red4[(((wave - 1) * FM + fm) * 4 + q) * 64 + lane] =
+            v4f{acc[fm][4 * q], acc[fm][4 * q + 1], acc[fm][4 * q + 2], acc[fm][4 * q + 3]};
   }
   __syncthreads();
   if (wave != 0) return;
@@ -1373,7 +1377,13 @@ gg_skinny_kernel(GemmArgs a) {
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) acc[fm][i] += red[(((w - 1) * FM + fm) * 16 + i) * 64 + lane];
+      for (int q = 0; q < 4; ++q) {
+        const v4f r = red4[(((w - 1) * FM + fm) * 4 + q) * 64 + lane];
+        acc[fm][4 * q] += r.x;
+        acc[fm][4 * q + 1] += r.y;
+        acc[fm][4 * q + 2] += r.z;
+        acc[fm][4 * q + 3] += r.w;
+      }
 
   // Epilogue: MFMA row rho = 8*j + 4*h + tt of the block is column n0 + rho.
 #pragma unroll
