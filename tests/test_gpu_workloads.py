@@ -134,6 +134,44 @@ def test_padded_tails_full_size(F):
     P.assert_rows_match(got, oracle.OracleResult(None, ref_bits, cls), label=w.name)
 
 
+def test_padded_tails_full_size_poisoned(F):
+    """The padded-tails workload with everything the call must not read poisoned:
+    padding rows of X hold NaN codes (0x7F) and NaN x_scale, and the empty group's
+    weights and w_scale are NaN.  With zeroing on and off, the valid rows equal the
+    clean call's bit for bit (same launch), padding rows are zero with zeroing on
+    and keep the sentinel with zeroing off."""
+    w = wl.padded_tails()
+    z = np.clip(w.zero_start_index_M, 0, w.expected_m)
+    assert (z == 0).any(), "the workload has an empty group"
+
+    def call(XQ, WQ, xs, ws, zeroing):
+        whole, out = P.guarded_output((w.G, w.expected_m, w.N))
+        F.f8f8bf16_rowwise_grouped_dynamic(P.dev(XQ), P.dev(WQ), P.dev(xs), P.dev(ws),
+                                           P.dev(w.zero_start_index_M), zeroing_output_tensor=zeroing, out=out)
+        torch.cuda.synchronize()
+        P.check_guards(whole)
+        return out.view(torch.int16)
+
+    XQ, xs, WQ, ws = w.XQ.copy(), w.x_scale.copy(), w.WQ.copy(), w.w_scale.copy()
+    for g in range(w.G):
+        XQ[g, z[g]:] = 0x7F
+        xs[g, z[g]:] = np.nan
+        if z[g] == 0:
+            WQ[g] = 0x7F
+            ws[g] = np.nan
+    for zeroing in (True, False):
+        print(f"case {w.name} poisoned zeroing={zeroing}", flush=True)
+        clean = call(w.XQ, w.WQ, w.x_scale, w.w_scale, zeroing)
+        bad = call(XQ, WQ, xs, ws, zeroing)
+        for g in range(w.G):
+            assert torch.equal(bad[g, :z[g]], clean[g, :z[g]]), f"group {g}: valid rows changed by the poison"
+            pad = bad[g, z[g]:]
+            if zeroing:
+                assert bool((pad == 0).all()), f"group {g}: padding rows not zero"
+            else:
+                assert bool((pad == P.SENTINEL).all()), f"group {g}: padding rows written"
+
+
 def test_tiny_full(F):
     w = wl.tiny_stacked()
     out = stacked_call(F, w)
