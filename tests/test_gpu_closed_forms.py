@@ -21,7 +21,10 @@ import torch
 
 import workloads as wl
 from tests import parity as P
+from tests.test_gpu_blockscale import forced as forced_bs
 from tests.test_gpu_parity import PLAIN_CONFIGS, PRE_CONFIGS, config_env  # noqa: F401 (fixture)
+from tests.test_gpu_ragged import RAGGED_CONFIGS, run_k, run_n
+from tests.test_gpu_ragged import forced as forced_cfg
 
 pytestmark = pytest.mark.gpu
 
@@ -181,3 +184,90 @@ def test_power_of_two_scale_changes_are_exact(F, config_env, cfg):
     mask[np.ix_(grows, cols)] = True
     assert np.array_equal(got[~mask], base[~mask]), "entries whose scale did not change moved"
     assert np.array_equal(as_f32(got[mask]), 0.5 * as_f32(base[mask])), "halved entries are not exactly halved"
+
+
+FINITE = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+
+
+@pytest.mark.parametrize("cfg", [None] + RAGGED_CONFIGS)
+def test_one_hot_rows_exact_n_offsets(F, cfg):
+    """n_offsets: column n of group g takes slab g of X, so Y[m, n] is the single
+    product at slab g's one-hot column; columns of no group keep the sentinel."""
+    rng = np.random.default_rng(7400 + (cfg or 0))
+    G, M, K = 4, 70, 208
+    widths = [0, 37, 200, 64]
+    total_N = 304                                   # three trailing columns of no group
+    offs = np.cumsum(widths).astype(np.int32)
+    owner = np.full(total_N, -1)
+    start = 0
+    for g, wd in enumerate(widths):
+        owner[start:start + wd] = g
+        start += wd
+    XQ = np.zeros((G, M, K), np.uint8)
+    ks = rng.integers(0, K, (G, M))
+    codes = rng.choice(FINITE_NONZERO, (G, M))
+    gi, mi = np.meshgrid(np.arange(G), np.arange(M), indexing="ij")
+    XQ[gi, mi, ks] = codes
+    WQ = rng.choice(FINITE, (total_N, K))
+    xs, ws = pow2(rng, (G, M)), pow2(rng, total_N)
+    cols = np.nonzero(owner >= 0)[0]
+    gc = owner[cols]
+    y = (decode(codes[gc].T) * decode(WQ[cols[None, :], ks[gc].T]) * xs[gc].T.astype(np.float64)
+         * ws[cols][None, :].astype(np.float64))
+    want = bf16_bits_exact(y)
+    print(f"case one-hot n_offsets cfg={cfg}", flush=True)
+    with forced_cfg(cfg):
+        got = run_n(F, XQ, WQ, xs, ws, offs)
+    assert np.array_equal(unsigned_zero(got[:, cols]), want), "written columns differ"
+    assert np.all(got[:, owner < 0] == np.uint16(P.SENTINEL)), "columns of no group were written"
+
+
+@pytest.mark.parametrize("cfg", [None] + RAGGED_CONFIGS)
+def test_one_hot_rows_exact_k_offsets(F, cfg):
+    """k_offsets: the one-hot column of row m lies in exactly one group's K slice;
+    that group's Y[g, m, :] is the single product, every other group's row is zero
+    (an empty slice included)."""
+    rng = np.random.default_rng(7500 + (cfg or 0))
+    M, N = 70, 136
+    widths = [0, 48, 400, 160]
+    G, total_K = len(widths), sum(widths)
+    offs = np.cumsum(widths).astype(np.int32)
+    kowner = np.repeat(np.arange(G), widths)
+    XQ, ks, codes = one_hot(rng, M, total_K)
+    WQ = rng.choice(FINITE, (N, total_K))
+    xs, ws = pow2(rng, (G, M)), pow2(rng, (G, N))
+    y = np.zeros((G, M, N))
+    gm = kowner[ks]
+    y[gm, np.arange(M)] = (decode(codes)[:, None] * decode(WQ[:, ks].T) * xs[gm, np.arange(M)][:, None].astype(np.float64)
+                           * ws[gm].astype(np.float64))
+    want = bf16_bits_exact(y)
+    print(f"case one-hot k_offsets cfg={cfg}", flush=True)
+    with forced_cfg(cfg):
+        got = run_k(F, XQ, WQ, xs, ws, offs)
+    assert np.array_equal(unsigned_zero(got), want)
+
+
+@pytest.mark.parametrize("cfg", [None, 0, 1, 2])
+def test_one_hot_rows_exact_blockscale(F, cfg):
+    """Block scales: the single product of row m lies in K block k_m // 128, so only
+    x_scale[m, kb] and w_scale[g, n // 128, kb] of that block may reach Y[m, n]; with
+    power-of-two block scales the result is exact."""
+    rng = np.random.default_rng(7600 + (cfg or 0))
+    sizes, N, K = [37, 0, 130, 3], 384, 640
+    G, M = len(sizes), sum(sizes)
+    XQ, ks, codes = one_hot(rng, M, K)
+    WQ = rng.choice(FINITE, (G, N, K))
+    xs, ws = pow2(rng, (M, K // 128)), pow2(rng, (G, N // 128, K // 128))
+    owner = np.repeat(np.arange(G), sizes)
+    kb = ks // 128
+    y = (decode(codes)[:, None] * decode(WQ[owner, :, ks]) * xs[np.arange(M), kb][:, None].astype(np.float64)
+         * ws[owner[:, None], (np.arange(N) // 128)[None, :], kb[:, None]].astype(np.float64))
+    want = bf16_bits_exact(y)
+    print(f"case one-hot block-scaled cfg={cfg}", flush=True)
+    with forced_bs(cfg):
+        whole, out = P.guarded_output((M, N))
+        F.f8f8bf16_groupwise_grouped_stacked(P.dev(XQ), P.dev(WQ), P.dev(xs), P.dev(ws),
+                                             P.dev(np.array(sizes, np.int64)), out=out)
+        torch.cuda.synchronize()
+    P.check_guards(whole)
+    assert np.array_equal(unsigned_zero(P.bits_of(out)), want)
