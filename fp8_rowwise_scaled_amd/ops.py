@@ -14,25 +14,39 @@ _FP8 = getattr(torch, "float8_e4m3fn", None)
 
 
 def _bytes(t: torch.Tensor, name: str) -> torch.Tensor:
-    if _FP8 is not None and t.dtype == _FP8:
-        t = t.view(torch.uint8)
-    if t.dtype != torch.uint8:
-        raise ValueError(f"{name} must be float8_e4m3fn or uint8 (raw e4m3fn bytes), got {t.dtype}")
-    return t
+    dt = t.dtype
+    if dt == torch.uint8:
+        return t
+    if _FP8 is not None and dt == _FP8:
+        return t.view(torch.uint8)
+    raise ValueError(f"{name} must be float8_e4m3fn or uint8 (raw e4m3fn bytes), got {dt}")
 
 
-def _check(t: torch.Tensor, name: str, dtype, shape) -> None:
+def _check(t: torch.Tensor, name: str, dtype, shape: tuple) -> None:
+    # One combined test on the common path (a decode call is short enough that the
+    # binding's own time shows); the separate tests below only name what failed.
+    if t.dtype != dtype or t.shape != shape or not t.is_cuda or not t.is_contiguous():
+        _refuse(t, name, dtype, shape)
+
+
+def _refuse(t: torch.Tensor, name: str, dtype, shape: tuple) -> None:
     if t.dtype != dtype:
         raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
+    raise ValueError(f"{name} must be contiguous")
+
+
+# The current stream's raw handle without building a torch.cuda.Stream object per
+# call (the same handle torch launches its own work on).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
 
 
 def _stream(dev: torch.device) -> int:
+    if _raw_stream is not None:
+        return _raw_stream(dev.index)
     return torch.cuda.current_stream(dev).cuda_stream
 
 

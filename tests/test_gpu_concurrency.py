@@ -131,3 +131,16 @@ def test_calls_from_several_host_threads(F, calls):
         for i, whole, y in outs[t]:
             P.check_guards(whole)
             assert np.array_equal(P.bits_of(y), expect[i]), f"thread {t}: {calls[i][0]}"
+
+
+def test_binding_launches_on_the_current_stream(F):
+    """The binding hands the library the handle of torch's current stream, on the
+    default stream and inside a side stream's context."""
+    from fp8_rowwise_scaled_amd import ops
+    dev = torch.device("cuda", 0)
+    assert ops._stream(dev) == torch.cuda.current_stream(dev).cuda_stream
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        assert ops._stream(dev) == s.cuda_stream
+        assert ops._stream(dev) != torch.cuda.default_stream(dev).cuda_stream
+    assert ops._stream(dev) == torch.cuda.current_stream(dev).cuda_stream
