@@ -39,6 +39,13 @@ def _refuse(t: torch.Tensor, name: str, dtype, shape: tuple) -> None:
     raise ValueError(f"{name} must be contiguous")
 
 
+def _on_gpu(t: torch.Tensor, name: str) -> None:
+    """For XQ and WQ after _bytes (dtype settled) whose shape the caller has just
+    read off the tensor itself: only placement and layout are left to check."""
+    if not t.is_cuda or not t.is_contiguous():
+        _refuse(t, name, t.dtype, tuple(t.shape))
+
+
 # The current stream's raw handle without building a torch.cuda.Stream object per
 # call (the same handle torch launches its own work on).
 _raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
@@ -59,8 +66,8 @@ def _stacked(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out, meta_name="M_sizes
     G, N, K2 = WQ.shape
     if K2 != K:
         raise ValueError(f"K mismatch: XQ has {K}, WQ has {K2}")
-    _check(XQ, "XQ", torch.uint8, (total_M, K))
-    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _on_gpu(XQ, "XQ")
+    _on_gpu(WQ, "WQ")
     _check(x_scale, "x_scale", torch.float32, (total_M,))
     _check(w_scale, "w_scale", torch.float32, (G, N))
     _check(M_sizes, meta_name, meta_dtype, (G,))
@@ -83,8 +90,8 @@ def _dynamic(fn_name, XQ, WQ, x_scale, w_scale, zero_start_index_M, zeroing_outp
     G2, N, K2 = WQ.shape
     if G2 != G or K2 != K:
         raise ValueError(f"shape mismatch: XQ {tuple(XQ.shape)} vs WQ {tuple(WQ.shape)}")
-    _check(XQ, "XQ", torch.uint8, (G, em, K))
-    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _on_gpu(XQ, "XQ")
+    _on_gpu(WQ, "WQ")
     _check(x_scale, "x_scale", torch.float32, (G, em))
     _check(w_scale, "w_scale", torch.float32, (G, N))
     _check(zero_start_index_M, "zero_start_index_M", torch.int64, (G,))
@@ -132,8 +139,8 @@ def _batched(fn_name, XQ, WQ, x_scale, w_scale, out):
     G2, N, K2 = WQ.shape
     if G2 != G or K2 != K:
         raise ValueError(f"shape mismatch: XQ {tuple(XQ.shape)} vs WQ {tuple(WQ.shape)}")
-    _check(XQ, "XQ", torch.uint8, (G, M, K))
-    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _on_gpu(XQ, "XQ")
+    _on_gpu(WQ, "WQ")
     _check(x_scale, "x_scale", torch.float32, (G, M))
     _check(w_scale, "w_scale", torch.float32, (G, N))
     if out is None:
@@ -182,8 +189,8 @@ def f8f8bf16_rowwise_grouped_n_offsets(XQ, WQ, x_scale, w_scale, n_offsets, out=
     N, K2 = WQ.shape
     if K2 != K:
         raise ValueError(f"K mismatch: XQ has {K}, WQ has {K2}")
-    _check(XQ, "XQ", torch.uint8, (G, M, K))
-    _check(WQ, "WQ", torch.uint8, (N, K))
+    _on_gpu(XQ, "XQ")
+    _on_gpu(WQ, "WQ")
     _check(x_scale, "x_scale", torch.float32, (G, M))
     _check(w_scale, "w_scale", torch.float32, (N,))
     _check(n_offsets, "n_offsets", torch.int32, (G,))
@@ -212,8 +219,8 @@ def f8f8bf16_rowwise_grouped_k_offsets(XQ, WQ, x_scale, w_scale, k_offsets, out=
     if k_offsets.dim() != 1:
         raise ValueError("k_offsets must be [G]")
     G = k_offsets.shape[0]
-    _check(XQ, "XQ", torch.uint8, (M, K))
-    _check(WQ, "WQ", torch.uint8, (N, K))
+    _on_gpu(XQ, "XQ")
+    _on_gpu(WQ, "WQ")
     _check(x_scale, "x_scale", torch.float32, (G, M))
     _check(w_scale, "w_scale", torch.float32, (G, N))
     _check(k_offsets, "k_offsets", torch.int32, (G,))
@@ -298,8 +305,8 @@ def _groupwise_dynamic(fn_name, XQ, WQ, x_scale, w_scale, zero_start_index_M, ze
         raise ValueError(f"shape mismatch: XQ {tuple(XQ.shape)} vs WQ {tuple(WQ.shape)}")
     if K % 128 or N % 128:
         raise ValueError(f"block scaling needs K and N to be multiples of 128 (N={N}, K={K})")
-    _check(XQ, "XQ", torch.uint8, (G, em, K))
-    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _on_gpu(XQ, "XQ")
+    _on_gpu(WQ, "WQ")
     _check(x_scale, "x_scale", torch.float32, (G, em, K // 128))
     _check(w_scale, "w_scale", torch.float32, (G, N // 128, K // 128))
     _check(zero_start_index_M, "zero_start_index_M", torch.int64, (G,))
@@ -348,8 +355,8 @@ def _groupwise_batched(fn_name, XQ, WQ, x_scale, w_scale, out):
         raise ValueError(f"shape mismatch: XQ {tuple(XQ.shape)} vs WQ {tuple(WQ.shape)}")
     if K % 128 or N % 128:
         raise ValueError(f"block scaling needs K and N to be multiples of 128 (N={N}, K={K})")
-    _check(XQ, "XQ", torch.uint8, (G, M, K))
-    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _on_gpu(XQ, "XQ")
+    _on_gpu(WQ, "WQ")
     _check(x_scale, "x_scale", torch.float32, (G, M, K // 128))
     _check(w_scale, "w_scale", torch.float32, (G, N // 128, K // 128))
     if out is None:
@@ -372,8 +379,8 @@ def _groupwise(fn_name, XQ, WQ, x_scale, w_scale, M_sizes, out, meta_name="M_siz
         raise ValueError(f"K mismatch: XQ has {K}, WQ has {K2}")
     if K % 128 or N % 128:
         raise ValueError(f"block scaling needs K and N to be multiples of 128 (N={N}, K={K})")
-    _check(XQ, "XQ", torch.uint8, (total_M, K))
-    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _on_gpu(XQ, "XQ")
+    _on_gpu(WQ, "WQ")
     _check(x_scale, "x_scale", torch.float32, (total_M, K // 128))
     _check(w_scale, "w_scale", torch.float32, (G, N // 128, K // 128))
     _check(M_sizes, meta_name, meta_dtype, (G,))
@@ -392,7 +399,7 @@ def f8f8bf16_shuffle_b(WQ, out=None):
     if WQ.dim() != 3:
         raise ValueError("WQ must be [G, N, K]")
     G, N, K = WQ.shape
-    _check(WQ, "WQ", torch.uint8, (G, N, K))
+    _on_gpu(WQ, "WQ")
     if out is None:
         out = torch.empty_like(WQ)
     _check(out, "out", torch.uint8, (G, N, K))
