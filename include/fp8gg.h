@@ -20,8 +20,9 @@
  *   - `stream` is a hipStream_t (NULL = the legacy default stream).  Work is only
  *     enqueued: no entry point copies between host and device or synchronises.
  *     Every call may be captured into a HIP graph.
- *   - No workspace: the library allocates no device memory.  Stacked calls with at
- *     least 256 rows per group (on average) run on a persistent grid, one
+ *   - No workspace: the library allocates no device memory.  Stacked, offsets and
+ *     batched calls with at least 256 rows per group (on average) run on a
+ *     persistent grid, one
  *     workgroup per compute unit; when the output tiles do not fill a whole number
  *     of rounds of that grid, the tiles of the last round may be computed as four
  *     quarter tiles each.  Every output element is still computed by one
