@@ -22,10 +22,9 @@
  *     Every call may be captured into a HIP graph.
  *   - No workspace: the library allocates no device memory.  Stacked, offsets and
  *     batched calls with at least 256 rows per group (on average) run on a
- *     persistent grid, one
- *     workgroup per compute unit; when the output tiles do not fill a whole number
- *     of rounds of that grid, the tiles of the last round may be computed as four
- *     quarter tiles each.  Every output element is still computed by one
+ *     persistent grid, one workgroup per compute unit; when the output tiles do
+ *     not fill a whole number of rounds of that grid, the tiles of the last round
+ *     may be computed as four quarter tiles each.  Every output element is still computed by one
  *     workgroup in one fixed K order, so results are deterministic and equal,
  *     bit for bit, to those of the one-tile-per-workgroup schedule.
  *   - Device-side metadata (M_sizes, zero_start_index_M) is never read by the host.
