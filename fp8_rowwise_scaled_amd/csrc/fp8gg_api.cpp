@@ -276,6 +276,9 @@ fp8gg_status make_plan(int layout, int preshuffled, int64_t G, int64_t M, int64_
     p->grid = p->m_tiles * p->n_tiles * G;
   }
   p->lds_bytes = fp8gg::lds_bytes(c);
+  // The ragged kernel runs two-stage tiles on an asymmetric ring: two X slots,
+  // three W slots (W copied two stages ahead).
+  if (ragged(layout) && c.kind == fp8gg::kKindLds && c.stages == 2) p->lds_bytes = (2 * c.BM + 3 * c.BN) * c.BK;
   if (p->grid > 0x7FFFFFFFLL)
     return fail(FP8GG_ERR_UNSUPPORTED_SHAPE, "grid of %lld workgroups exceeds the launch limit",
                 (long long)p->grid);

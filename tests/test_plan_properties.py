@@ -80,6 +80,8 @@ def test_plan_invariants(s):
     assert 0 < p["grid"] < 2 ** 31
     if layout in RAGGED:
         assert p["config_id"] in RAGGED_CONFIGS and p["persistent"] == 0
+        if p["stages"] == 2:   # two X slots and three W slots (W copied two stages ahead)
+            assert p["lds_bytes"] == (2 * BM + 3 * BN) * BK
     if layout == F.LAYOUT_PADDED:
         assert p["persistent"] == 0
 
